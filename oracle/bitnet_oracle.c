@@ -1,0 +1,260 @@
+/*
+ * Plain CPU oracle for the ternary-weight x int8-activation projection.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg do.  It shares no code with the HIP library: it has its own layout code,
+ * its own rounding and its own loops, written straight from the definitions.
+ *
+ * Build: gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC
+ * (no FMA contraction, IEEE float, default round-to-nearest-even mode).
+ *
+ * What is computed, and where the pages define it:
+ *
+ *  - Ternarization (BitNet b1.58, per tensor).  Every LM projection weight
+ *    becomes -1, 0 or +1 (blog "The Paper Says ARM Support. I Might Be the First
+ *    to Actually Compile It", section "What the model is trying to do"); the
+ *    scale is one number per tensor built from the mean absolute weight (ONNX
+ *    model card "multimodalart/VibeVoice-ASR-BitNet-ONNX", Quantization table,
+ *    row "LM projections"), applied to QAT master weights right before export
+ *    (same card, paragraph under the Quantization table).
+ *    Reading used here: m = mean|W| (fp64 sum, fixed order, rounded once to
+ *    fp32), code = clamp(rint(fl32(W / m)), -1, 1), stored scale = m.
+ *
+ *  - Packing.  Codes are stored at 2 bits in units of 128 consecutive inputs
+ *    (blog above, section "Postscript two": the format packs 128 elements per
+ *    unit and a 64-element reading scrambles the weights).  The bit placement
+ *    inside a unit is not on the pages; this oracle follows the layout that the
+ *    library header specifies (field value u = code + 1; unit-column-major).
+ *
+ *  - Activation quantization: per row, absmax int8: s = fl32(127 / max|x|),
+ *    xq = clamp(rint(fl32(x * s)), -127, 127); an all-zero row gives xq = 0 and
+ *    s = 1.  int8 activations appear on the pages for the audio encoder's I8_S
+ *    path (ONNX card, Quantization table, row "VAE encoders"); the LM formula
+ *    is this reading's.
+ *
+ *  - Contraction: with ternary codes the products become additions and
+ *    subtractions of activations (xujun.org article, section on heterogeneous
+ *    quantization; aitrends.kr summary, sections on technical features and
+ *    differentiators).  acc[m,n] = sum_{q=+1} xq - sum_{q=-1} xq in int32.
+ *
+ *  - Dequantization: y = acc * w_scale / x_scale, computed in fp64 and rounded
+ *    once to fp32 (the pages are silent on the epilogue; this is the plain
+ *    reading of "dequantize both factors").
+ *
+ * Parity pins for every function live in the CPU tests; none is "parity
+ * unpinned" except the correspondence of the packed bit layout to the original
+ * GGUF I2_S files, which are not available (the layout here is our own spec).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_UNIT 128
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* ---------------------------------------------------------------------- */
+/* Ternarization                                                           */
+/* ---------------------------------------------------------------------- */
+
+/* mean|W| over all N*K entries.  Each row is summed in fp64 with k ascending,
+ * then the row sums are added in fp64 with n ascending; the quotient by N*K is
+ * taken in fp64 and rounded once to fp32.  The order is fixed because one ulp
+ * of m can move a code that sits on the rounding threshold. */
+float oracle_absmean(const float *W, int64_t N, int64_t K) {
+    double total = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        double row = 0.0;
+        for (int64_t k = 0; k < K; ++k) row += fabs((double)W[n * K + k]);
+        total += row;
+    }
+    return (float)(total / (double)(N * K));
+}
+
+/* One code from one weight, given the tensor's m (m > 0). */
+static int8_t ternary_code(float w, float m) {
+    float r = w / m;          /* IEEE fp32 division, correctly rounded */
+    float t = rintf(r);       /* round half to even (default mode) */
+    if (t > 1.0f) return 1;
+    if (t < -1.0f) return -1;
+    return (int8_t)t;
+}
+
+/* codes q[N,K] in {-1,0,+1} and the stored scale m.  m == 0 (all-zero W)
+ * gives all-zero codes and scale 0. */
+void oracle_ternarize(const float *W, int64_t N, int64_t K, int8_t *q, float *w_scale) {
+    float m = oracle_absmean(W, N, K);
+    *w_scale = m;
+    int64_t total = N * K;
+    if (m == 0.0f) {
+        memset(q, 0, (size_t)total);
+        return;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < total; ++i) q[i] = ternary_code(W[i], m);
+}
+
+/* ---------------------------------------------------------------------- */
+/* 2-bit packing in 128-code units                                          */
+/* ---------------------------------------------------------------------- */
+
+/* Position of code (n,k) in the packed buffer: unit t = k/128 of row n is the
+ * 32-byte block number t*N + n; inside it, offset r = k%128 sits in byte r%32
+ * at bit 2*(r/32). */
+static int64_t packed_byte(int64_t N, int64_t n, int64_t k) {
+    int64_t t = k / ORACLE_UNIT, r = k % ORACLE_UNIT;
+    return (t * N + n) * 32 + (r % 32);
+}
+static int packed_shift(int64_t k) { return 2 * (int)((k % ORACLE_UNIT) / 32); }
+
+void oracle_pack(const int8_t *q, int64_t N, int64_t K, uint8_t *packed) {
+    memset(packed, 0, (size_t)(N * K / 4));
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            unsigned u = (unsigned)(q[n * K + k] + 1);   /* 0,1,2 */
+            packed[packed_byte(N, n, k)] |= (uint8_t)(u << packed_shift(k));
+        }
+}
+
+/* Inverse of oracle_pack.  Returns the number of fields holding the value 3,
+ * which no valid buffer contains (those codes are written as 0). */
+int64_t oracle_unpack(const uint8_t *packed, int64_t N, int64_t K, int8_t *q) {
+    int64_t bad = 0;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            unsigned u = (packed[packed_byte(N, n, k)] >> packed_shift(k)) & 3u;
+            if (u == 3u) { ++bad; u = 1u; }
+            q[n * K + k] = (int8_t)((int)u - 1);
+        }
+    return bad;
+}
+
+/* One code read straight from the packed buffer. */
+int oracle_code_at(const uint8_t *packed, int64_t N, int64_t n, int64_t k) {
+    unsigned u = (packed[packed_byte(N, n, k)] >> packed_shift(k)) & 3u;
+    return (int)u - 1;
+}
+
+void oracle_ternarize_pack(const float *W, int64_t N, int64_t K, uint8_t *packed,
+                           float *w_scale) {
+    int8_t *q = (int8_t *)malloc((size_t)(N * K));
+    oracle_ternarize(W, N, K, q, w_scale);
+    oracle_pack(q, N, K, packed);
+    free(q);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Activation quantization, one scale per row                               */
+/* ---------------------------------------------------------------------- */
+
+void oracle_quant_act(const float *x, int64_t M, int64_t K, int8_t *xq, float *x_scale) {
+    for (int64_t m = 0; m < M; ++m) {
+        const float *row = x + m * K;
+        float a = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = fabsf(row[k]);
+            if (v > a) a = v;
+        }
+        if (a == 0.0f) {
+            memset(xq + m * K, 0, (size_t)K);
+            x_scale[m] = 1.0f;
+            continue;
+        }
+        float s = 127.0f / a;            /* fp32, correctly rounded */
+        x_scale[m] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            float p = row[k] * s;        /* fp32 product */
+            float t = rintf(p);          /* half to even */
+            if (t > 127.0f) t = 127.0f;
+            if (t < -127.0f) t = -127.0f;
+            xq[m * K + k] = (int8_t)t;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Ternary contraction and dequantization                                   */
+/* ---------------------------------------------------------------------- */
+
+/* acc[m,n] = (sum of xq[m,k] over k with q[n,k] = +1)
+ *          - (sum of xq[m,k] over k with q[n,k] = -1). */
+void oracle_matmul_i32(const int8_t *xq, const int8_t *q, int64_t M, int64_t N, int64_t K,
+                       int32_t *acc) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int32_t plus = 0, minus = 0;
+            for (int64_t k = 0; k < K; ++k) {
+                int8_t c = q[n * K + k];
+                if (c == 1) plus += xq[m * K + k];
+                else if (c == -1) minus += xq[m * K + k];
+            }
+            acc[m * N + n] = plus - minus;
+        }
+}
+
+void oracle_dequant(const int32_t *acc, float w_scale, const float *x_scale, int64_t M,
+                    int64_t N, float *y) {
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            y[m * N + n] = (float)((double)acc[m * N + n] * (double)w_scale /
+                                   (double)x_scale[m]);
+}
+
+/* The whole projection: quantize x, decode the packed codes, contract, dequantize.
+ * xq_out / x_scale_out / acc_out may be NULL. */
+void oracle_ternary_matmul(int64_t M, int64_t N, int64_t K, const float *x,
+                           const uint8_t *packed, float w_scale, float *y,
+                           int8_t *xq_out, float *x_scale_out, int32_t *acc_out) {
+    int8_t *xq = (int8_t *)malloc((size_t)(M * K));
+    float *xs = (float *)malloc(sizeof(float) * (size_t)M);
+    int8_t *q = (int8_t *)malloc((size_t)(N * K));
+    int32_t *acc = (int32_t *)malloc(sizeof(int32_t) * (size_t)(M * N));
+    oracle_quant_act(x, M, K, xq, xs);
+    oracle_unpack(packed, N, K, q);
+    oracle_matmul_i32(xq, q, M, N, K, acc);
+    oracle_dequant(acc, w_scale, xs, M, N, y);
+    if (xq_out) memcpy(xq_out, xq, (size_t)(M * K));
+    if (x_scale_out) memcpy(x_scale_out, xs, sizeof(float) * (size_t)M);
+    if (acc_out) memcpy(acc_out, acc, sizeof(int32_t) * (size_t)(M * N));
+    free(xq); free(xs); free(q); free(acc);
+}
+
+/* Selected outputs only: for each pair (ms[i], ns[i]) the accumulator and the
+ * dequantized output, reading codes one by one from the packed buffer.  xq and
+ * x_scale are the oracle's own quantized activations for all M rows. */
+void oracle_matmul_sampled(int64_t N, int64_t K, const int8_t *xq, const float *x_scale,
+                           const uint8_t *packed, float w_scale, const int64_t *ms,
+                           const int64_t *ns, int64_t count, int32_t *acc, float *y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t m = ms[i], n = ns[i];
+        int32_t plus = 0, minus = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            int c = oracle_code_at(packed, N, n, k);
+            if (c == 1) plus += xq[m * K + k];
+            else if (c == -1) minus += xq[m * K + k];
+        }
+        acc[i] = plus - minus;
+        y[i] = (float)((double)acc[i] * (double)w_scale / (double)x_scale[m]);
+    }
+}
