@@ -1,0 +1,185 @@
+/*
+ * bitnet_tm.h -- C ABI of the MI355X (gfx950) ternary-weight x int8-activation
+ * projection library.
+ *
+ * The operation is the linear projection of a BitNet b1.58 ("I2_S") decoder:
+ *   - every projection weight is one of -1, 0, +1, with one floating scale per
+ *     tensor taken from the mean absolute weight (ONNX model card
+ *     "multimodalart/VibeVoice-ASR-BitNet-ONNX", Quantization table, row "LM
+ *     projections"; blog "The Paper Says ARM Support. I Might Be the First to
+ *     Actually Compile It", section "What the model is trying to do");
+ *   - codes are stored at 2 bits in units of 128 inputs (same blog, section
+ *     "Postscript two");
+ *   - with ternary weights the products reduce to adding and subtracting
+ *     activations (xujun.org AIGCPanel article, section on heterogeneous
+ *     quantization; aitrends.kr model summary, sections on technical features and
+ *     differentiators).
+ *
+ * Numeric definitions (the pages leave these open; this library fixes them):
+ *   m        = mean|W| over all N*K weights: each row summed in fp64 with k
+ *              ascending, rows added in fp64 with n ascending, divided by N*K in
+ *              fp64, rounded once to fp32.  w_scale = m.
+ *   code     = clamp(rint(fl32(W / m)), -1, 1), rint = round half to even,
+ *              fl32(W/m) = IEEE fp32 division.  m == 0 gives all codes 0.
+ *   x_scale  = fl32(127 / max_k |x[m,k]|) per row; xq = clamp(rint(fl32(x*s)), -127, 127).
+ *              An all-zero row gives xq = 0 and x_scale = 1.
+ *   acc      = sum_k xq[m,k] * code[n,k]   (exact, int32; |acc| <= 127*K)
+ *   y[m,n]   = acc * w_scale / x_scale[m]  (fp32; within 1e-6 relative of the
+ *              exactly rounded value; acc == 0 gives exactly 0)
+ *   NaN/Inf inputs and rows whose 127/absmax overflows are outside the contract.
+ *
+ * Packed layout (2 bits per code, N*K/4 bytes, K a multiple of 128):
+ *   field value u = code + 1 in {0,1,2}; the value 3 never occurs.
+ *   For code (n,k): t = k/128, r = k%128,
+ *     byte  = (t*N + n)*32 + (r % 32)
+ *     bits  = [2*(r/32)+1 : 2*(r/32)]
+ *   i.e. unit t of row n is a 32-byte block; all N blocks of unit t are
+ *   contiguous ("unit-column-major").  This bit placement is this library's
+ *   own; the pages fix only the unit size and the 2-bit width.
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE pointers on the current HIP device, which
+ *     must be a gfx950 (MI355X).  `stream` is a hipStream_t passed as void*
+ *     (NULL = the default stream).  Every call is asynchronous on `stream`.
+ *   - The library never allocates device memory and keeps no mutable global
+ *     state; callers own every buffer.  Calls on different streams are
+ *     independent as long as their buffers do not overlap.
+ *   - Arguments are checked on the host before anything is launched.  On any
+ *     error nothing is launched and nothing is written.  Faults inside kernels
+ *     surface at the caller's next synchronization.
+ *   - Pointers that are read or written with vector loads must be 16-byte
+ *     aligned (x, W, packed, xq, xq_out, workspace); others need their natural
+ *     alignment.
+ *   - Size limits: M, N, K >= 1, K % 128 == 0, and M*K, N*K, M*N each below 2^31.
+ */
+#ifndef BITNET_TM_H
+#define BITNET_TM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t bitnet_status;
+
+#define BITNET_OK            0
+#define BITNET_ERR_NULL      1  /* a required pointer is NULL                      */
+#define BITNET_ERR_SHAPE     2  /* M,N,K out of range or K % 128 != 0              */
+#define BITNET_ERR_ALIGN     3  /* a pointer is not aligned as required            */
+#define BITNET_ERR_WORKSPACE 4  /* workspace missing or smaller than required      */
+#define BITNET_ERR_HIP       5  /* a HIP call or kernel launch reported an error   */
+#define BITNET_ERR_DEVICE    6  /* the current device is not a gfx950             */
+
+/* Maximum number of problems in one grouped call. */
+#define BITNET_MAX_GROUP     256
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *bitnet_status_string(bitnet_status s);
+
+/* Bytes of the packed code buffer for an N x K weight: N*K/4. */
+size_t bitnet_packed_bytes(int64_t N, int64_t K);
+
+/* ------------------------------------------------------------------------
+ * Ternarization and packing (offline, once per weight tensor).
+ *
+ * W        [N,K] fp32 row-major master weights (out x in), 16-byte aligned.
+ * packed   [N*K/4] bytes, 16-byte aligned, fully overwritten.
+ * w_scale  one fp32 written on the device: mean|W| (see definitions above).
+ * workspace: at least bitnet_ternarize_workspace_bytes(N) bytes, 16-byte
+ *          aligned; holds the fp64 row sums.  Contents on return are unspecified.
+ * Passage: ONNX model card, Quantization table, row "LM projections" (per-tensor
+ * absmean scale, ternary values); same card, note under that table (ternarize
+ * the master weights right before export); blog, "Postscript two" (128-code
+ * units).
+ * ------------------------------------------------------------------------ */
+size_t bitnet_ternarize_workspace_bytes(int64_t N);
+
+bitnet_status bitnet_ternarize_pack(const float *W, int64_t N, int64_t K, uint8_t *packed,
+                                    float *w_scale, void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+/* ------------------------------------------------------------------------
+ * Per-row int8 absmax activation quantization.
+ *
+ * x        [M,K] fp32 row-major, 16-byte aligned.
+ * xq       [M,K] int8 row-major (natural k order), 16-byte aligned.
+ * x_scale  [M] fp32: 127/absmax of each row (1.0 for an all-zero row).
+ * Passage: int8 activations with absmax scaling appear on the pages for the
+ * audio encoder's I8_S path (ONNX model card, Quantization table, row "VAE
+ * encoders"); the formula above is this library's definition for the LM.
+ * ------------------------------------------------------------------------ */
+bitnet_status bitnet_quant_act(const float *x, int64_t M, int64_t K, int8_t *xq,
+                               float *x_scale, void *stream);
+
+/* ------------------------------------------------------------------------
+ * The projection: y[M,N] = dequant( quant(x) . codes^T ).
+ *
+ * x        [M,K] fp32 row-major, 16-byte aligned.
+ * packed   codes of W [N,K] in the packed layout, 16-byte aligned.
+ * w_scale  device pointer to the fp32 tensor scale written by
+ *          bitnet_ternarize_pack.
+ * y        [M,N] fp32 row-major output, 4-byte aligned.
+ * workspace: at least bitnet_matmul_workspace_bytes(M, K) bytes, 256-byte
+ *          aligned (quantized activations, scales and row sums).
+ * xq_out, x_scale_out, acc_out: optional (may be NULL) copies of the int8
+ *          activations [M,K], their scales [M] and the int32 accumulators [M,N],
+ *          for parity checks.
+ * M <= 16 runs the decode GEMV (HBM-bound weight stream), M > 16 the prefill
+ * GEMM (int8 MFMA); results are identical either way.
+ * Passage: the add/subtract contraction (xujun.org article, heterogeneous
+ * quantization section; aitrends.kr summary, technical-features section); the
+ * decoder reads all of its weights for every token (blog, "What the model is
+ * trying to do").
+ * ------------------------------------------------------------------------ */
+size_t bitnet_matmul_workspace_bytes(int64_t M, int64_t K);
+
+bitnet_status bitnet_ternary_matmul(int64_t M, int64_t N, int64_t K, const float *x,
+                                    const uint8_t *packed, const float *w_scale, float *y,
+                                    void *workspace, size_t workspace_bytes, int8_t *xq_out,
+                                    float *x_scale_out, int32_t *acc_out, void *stream);
+
+/* Same projection from already-quantized activations (xq natural order, as
+ * written by bitnet_quant_act).  workspace: bitnet_matmul_workspace_bytes(M, K). */
+bitnet_status bitnet_ternary_matmul_q8(int64_t M, int64_t N, int64_t K, const int8_t *xq,
+                                       const float *x_scale, const uint8_t *packed,
+                                       const float *w_scale, float *y, void *workspace,
+                                       size_t workspace_bytes, int32_t *acc_out,
+                                       void *stream);
+
+/* ------------------------------------------------------------------------
+ * Grouped projections: `count` independent problems with the same M, one
+ * quantization launch and one matmul launch for all of them.  A decoder layer
+ * (7 projections) or a whole decoder (196) fits in one call.
+ *
+ * problems_dev  device copy of the problem array (read by the kernels).
+ * problems_host host copy of the same array (read by the host to check shapes
+ *               and size the launch); both must hold identical values.
+ * workspace     at least bitnet_grouped_workspace_bytes(M, problems_host, count)
+ *               bytes, 256-byte aligned.
+ * count         1..BITNET_MAX_GROUP.
+ * Every problem obeys the single-problem rules above.
+ * ------------------------------------------------------------------------ */
+typedef struct bitnet_problem {
+    const float *x;          /* [M,K] fp32 activations                     */
+    const uint8_t *packed;   /* packed codes of W [N,K]                    */
+    const float *w_scale;    /* device fp32 tensor scale                   */
+    float *y;                /* [M,N] fp32 output                          */
+    int64_t N;
+    int64_t K;
+} bitnet_problem;
+
+size_t bitnet_grouped_workspace_bytes(int64_t M, const bitnet_problem *problems_host,
+                                      int32_t count);
+
+bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *problems_dev,
+                                            int32_t count, const bitnet_problem *problems_host,
+                                            void *workspace, size_t workspace_bytes,
+                                            void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITNET_TM_H */

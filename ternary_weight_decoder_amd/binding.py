@@ -1,0 +1,259 @@
+"""Thin Python binding over the C ABI in include/bitnet_tm.h.
+
+Argument marshalling only: every step of the projection runs in the gfx950 HIP
+kernels of ``libbitnet_tm.so``.  torch supplies device memory and the current
+stream; no torch type crosses the ABI.  If the library is missing or the device
+is not a gfx950, calls raise -- there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import _build
+
+LIB_PATH = _build.LIB_PATH
+
+BITNET_OK = 0
+BITNET_MAX_GROUP = 256
+UNIT = 128
+
+_c = ctypes
+_p = _c.c_void_p
+_i64 = _c.c_int64
+_i32 = _c.c_int32
+_sz = _c.c_size_t
+
+
+class BitnetError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__(f"{fn}: status {status} ({status_string(status)})")
+
+
+class bitnet_problem(ctypes.Structure):
+    _fields_ = [("x", _p), ("packed", _p), ("w_scale", _p), ("y", _p),
+                ("N", _i64), ("K", _i64)]
+
+
+EXPORTS = (
+    "bitnet_status_string", "bitnet_packed_bytes", "bitnet_ternarize_workspace_bytes",
+    "bitnet_ternarize_pack", "bitnet_quant_act", "bitnet_matmul_workspace_bytes",
+    "bitnet_ternary_matmul", "bitnet_ternary_matmul_q8", "bitnet_grouped_workspace_bytes",
+    "bitnet_ternary_matmul_grouped",
+)
+
+_lib = None
+
+
+def lib():
+    """Load libbitnet_tm.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"HIP library {LIB_PATH} is not built; run __graft_entry__.build() "
+                "(python -m ternary_weight_decoder_amd._build)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.bitnet_status_string.argtypes = [_i32]
+        L.bitnet_status_string.restype = _c.c_char_p
+        L.bitnet_packed_bytes.argtypes = [_i64, _i64]
+        L.bitnet_packed_bytes.restype = _sz
+        L.bitnet_ternarize_workspace_bytes.argtypes = [_i64]
+        L.bitnet_ternarize_workspace_bytes.restype = _sz
+        L.bitnet_ternarize_pack.argtypes = [_p, _i64, _i64, _p, _p, _p, _sz, _p]
+        L.bitnet_ternarize_pack.restype = _i32
+        L.bitnet_quant_act.argtypes = [_p, _i64, _i64, _p, _p, _p]
+        L.bitnet_quant_act.restype = _i32
+        L.bitnet_matmul_workspace_bytes.argtypes = [_i64, _i64]
+        L.bitnet_matmul_workspace_bytes.restype = _sz
+        L.bitnet_ternary_matmul.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _sz, _p, _p,
+                                            _p, _p]
+        L.bitnet_ternary_matmul.restype = _i32
+        L.bitnet_ternary_matmul_q8.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _sz,
+                                               _p, _p]
+        L.bitnet_ternary_matmul_q8.restype = _i32
+        L.bitnet_grouped_workspace_bytes.argtypes = [_i64, _p, _i32]
+        L.bitnet_grouped_workspace_bytes.restype = _sz
+        L.bitnet_ternary_matmul_grouped.argtypes = [_i64, _p, _i32, _p, _p, _sz, _p]
+        L.bitnet_ternary_matmul_grouped.restype = _i32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().bitnet_status_string(int(status)).decode()
+
+
+def _check(status: int, fn: str) -> None:
+    if status != BITNET_OK:
+        raise BitnetError(status, fn)
+
+
+def _ptr(t):
+    return None if t is None else _p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return _p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+# Raw entry points: same names and arguments as the C ABI (tensors stand in for
+# device pointers).  They allocate nothing.
+# ---------------------------------------------------------------------------
+
+def bitnet_packed_bytes(N: int, K: int) -> int:
+    return int(lib().bitnet_packed_bytes(N, K))
+
+
+def bitnet_ternarize_workspace_bytes(N: int) -> int:
+    return int(lib().bitnet_ternarize_workspace_bytes(N))
+
+
+def bitnet_matmul_workspace_bytes(M: int, K: int) -> int:
+    return int(lib().bitnet_matmul_workspace_bytes(M, K))
+
+
+def bitnet_ternarize_pack_into(W, N, K, packed, w_scale, workspace, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().bitnet_ternarize_pack(_ptr(W), N, K, _ptr(packed), _ptr(w_scale),
+                                       _ptr(workspace), ws_bytes, _stream(stream)),
+           "bitnet_ternarize_pack")
+
+
+def bitnet_quant_act_into(x, M, K, xq, x_scale, stream=None) -> None:
+    _check(lib().bitnet_quant_act(_ptr(x), M, K, _ptr(xq), _ptr(x_scale), _stream(stream)),
+           "bitnet_quant_act")
+
+
+def bitnet_ternary_matmul_into(M, N, K, x, packed, w_scale, y, workspace, xq_out=None,
+                               x_scale_out=None, acc_out=None, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().bitnet_ternary_matmul(M, N, K, _ptr(x), _ptr(packed), _ptr(w_scale), _ptr(y),
+                                       _ptr(workspace), ws_bytes, _ptr(xq_out),
+                                       _ptr(x_scale_out), _ptr(acc_out), _stream(stream)),
+           "bitnet_ternary_matmul")
+
+
+def bitnet_ternary_matmul_q8_into(M, N, K, xq, x_scale, packed, w_scale, y, workspace,
+                                  acc_out=None, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().bitnet_ternary_matmul_q8(M, N, K, _ptr(xq), _ptr(x_scale), _ptr(packed),
+                                          _ptr(w_scale), _ptr(y), _ptr(workspace), ws_bytes,
+                                          _ptr(acc_out), _stream(stream)),
+           "bitnet_ternary_matmul_q8")
+
+
+# ---------------------------------------------------------------------------
+# Convenience forms that allocate their outputs with torch (plumbing only).
+# ---------------------------------------------------------------------------
+
+def bitnet_ternarize_pack(W: torch.Tensor, stream=None):
+    """fp32 W [N,K] -> (packed uint8 [N*K/4], w_scale fp32 [1]) on W's device."""
+    _dev(W, torch.float32, "W")
+    N, K = W.shape
+    packed = torch.empty(max(N * K // 4, 1), dtype=torch.uint8, device=W.device)
+    w_scale = torch.empty(1, dtype=torch.float32, device=W.device)
+    ws = torch.empty(max(bitnet_ternarize_workspace_bytes(N), 16), dtype=torch.uint8,
+                     device=W.device)
+    bitnet_ternarize_pack_into(W, N, K, packed, w_scale, ws, stream)
+    return packed, w_scale
+
+
+def bitnet_quant_act(x: torch.Tensor, stream=None):
+    """fp32 x [M,K] -> (xq int8 [M,K], x_scale fp32 [M])."""
+    _dev(x, torch.float32, "x")
+    M, K = x.shape
+    xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    xs = torch.empty(M, dtype=torch.float32, device=x.device)
+    bitnet_quant_act_into(x, M, K, xq, xs, stream)
+    return xq, xs
+
+
+def bitnet_ternary_matmul(x: torch.Tensor, packed: torch.Tensor, w_scale: torch.Tensor,
+                          N: int, *, return_parts: bool = False, stream=None):
+    """y [M,N] fp32; with return_parts also xq, x_scale and the int32 accumulators."""
+    _dev(x, torch.float32, "x")
+    _dev(packed, torch.uint8, "packed")
+    _dev(w_scale, torch.float32, "w_scale")
+    M, K = x.shape
+    y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    ws = torch.empty(bitnet_matmul_workspace_bytes(M, K), dtype=torch.uint8, device=x.device)
+    if return_parts:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        xs = torch.empty(M, dtype=torch.float32, device=x.device)
+        acc = torch.empty((M, N), dtype=torch.int32, device=x.device)
+        bitnet_ternary_matmul_into(M, N, K, x, packed, w_scale, y, ws, xq, xs, acc, stream)
+        return {"y": y, "xq": xq, "x_scale": xs, "acc": acc}
+    bitnet_ternary_matmul_into(M, N, K, x, packed, w_scale, y, ws, stream=stream)
+    return y
+
+
+def bitnet_ternary_matmul_q8(xq: torch.Tensor, x_scale: torch.Tensor, packed: torch.Tensor,
+                             w_scale: torch.Tensor, N: int, *, return_acc: bool = False,
+                             stream=None):
+    _dev(xq, torch.int8, "xq")
+    M, K = xq.shape
+    y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    ws = torch.empty(bitnet_matmul_workspace_bytes(M, K), dtype=torch.uint8, device=xq.device)
+    acc = torch.empty((M, N), dtype=torch.int32, device=xq.device) if return_acc else None
+    bitnet_ternary_matmul_q8_into(M, N, K, xq, x_scale, packed, w_scale, y, ws, acc, stream)
+    return (y, acc) if return_acc else y
+
+
+class GroupedPlan:
+    """A fixed set of independent projections with the same M, launched together.
+
+    Holds the host and device copies of the problem array and the workspace, so
+    that run() is a single C call with no allocation.
+    """
+
+    def __init__(self, M: int, xs, packeds, w_scales, ys, Ns, Ks, device=None):
+        count = len(xs)
+        if not 1 <= count <= BITNET_MAX_GROUP:
+            raise ValueError(f"group size must be 1..{BITNET_MAX_GROUP}")
+        self.M = int(M)
+        self.count = count
+        arr = (bitnet_problem * count)()
+        for i in range(count):
+            arr[i] = bitnet_problem(xs[i].data_ptr(), packeds[i].data_ptr(),
+                                    w_scales[i].data_ptr(), ys[i].data_ptr(), int(Ns[i]),
+                                    int(Ks[i]))
+        self._keep = (list(xs), list(packeds), list(w_scales), list(ys))
+        self.host = arr
+        dev = device if device is not None else xs[0].device
+        raw = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8)
+        self.dev = raw.to(dev)
+        nbytes = int(lib().bitnet_grouped_workspace_bytes(self.M, _c.byref(arr), count))
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.ws_bytes = nbytes
+
+    def run(self, stream=None) -> None:
+        bitnet_ternary_matmul_grouped(self.M, self.dev, self.count, self.host, self.workspace,
+                                      stream)
+
+
+def bitnet_grouped_workspace_bytes(M: int, problems_host, count: int) -> int:
+    return int(lib().bitnet_grouped_workspace_bytes(M, _c.byref(problems_host), count))
+
+
+def bitnet_ternary_matmul_grouped(M, problems_dev, count, problems_host, workspace,
+                                  stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().bitnet_ternary_matmul_grouped(M, _ptr(problems_dev), count,
+                                               _c.byref(problems_host), _ptr(workspace),
+                                               ws_bytes, _stream(stream)),
+           "bitnet_ternary_matmul_grouped")

@@ -1,0 +1,255 @@
+// C ABI of the ternary projection library: argument checks, workspace layout
+// and dispatch to the gfx950 kernels.  Nothing is launched unless every check
+// passes; no device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstring>
+
+#include "bitnet_internal.hpp"
+#include "bitnet_tm.h"
+
+using namespace bitnet;
+
+namespace {
+
+constexpr int64_t kLimit = (int64_t)1 << 31;  // M*K, N*K, M*N must stay below this
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool shape_ok(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1) return false;
+  if (K % 128 != 0) return false;  // 128 codes per packing unit
+  if (M >= kLimit || N >= kLimit || K >= kLimit) return false;
+  if (M * K >= kLimit || N * K >= kLimit || M * N >= kLimit) return false;
+  return true;
+}
+
+// Per-device record of the architecture check: 0 unknown, 1 gfx950, 2 other.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+bitnet_status device_check() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BITNET_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return BITNET_ERR_DEVICE;
+  int v = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BITNET_ERR_HIP;
+    v = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_ok[dev].store(v, std::memory_order_relaxed);
+  }
+  return v == 1 ? BITNET_OK : BITNET_ERR_DEVICE;
+}
+
+bitnet_status from_hip(hipError_t e) { return e == hipSuccess ? BITNET_OK : BITNET_ERR_HIP; }
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+bitnet_status check_problem(int64_t M, const bitnet_problem &p) {
+  if (!p.x || !p.packed || !p.w_scale || !p.y) return BITNET_ERR_NULL;
+  if (!shape_ok(M, p.N, p.K)) return BITNET_ERR_SHAPE;
+  if (!aligned(p.x, 16) || !aligned(p.packed, 16) || !aligned(p.w_scale, 4) ||
+      !aligned(p.y, 4))
+    return BITNET_ERR_ALIGN;
+  return BITNET_OK;
+}
+
+// Workspace offsets (256-byte units) of each problem of a group.
+size_t group_ws(int64_t M, const bitnet_problem *ph, int32_t count, uint32_t *off) {
+  size_t total = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    if (off) off[i] = (uint32_t)(total / 256);
+    total += align256(ws_layout(M, ph[i].K).total);
+  }
+  return total;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *bitnet_status_string(bitnet_status s) {
+  switch (s) {
+    case BITNET_OK: return "ok";
+    case BITNET_ERR_NULL: return "required pointer is NULL";
+    case BITNET_ERR_SHAPE: return "shape out of range (M,N,K >= 1, K % 128 == 0, products < 2^31)";
+    case BITNET_ERR_ALIGN: return "pointer not aligned as required";
+    case BITNET_ERR_WORKSPACE: return "workspace missing or too small";
+    case BITNET_ERR_HIP: return "HIP runtime or launch error";
+    case BITNET_ERR_DEVICE: return "current device is not a gfx950";
+    default: return "unknown status";
+  }
+}
+
+size_t bitnet_packed_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 1) return 0;
+  return (size_t)(N * K / 4);
+}
+
+size_t bitnet_ternarize_workspace_bytes(int64_t N) {
+  if (N < 1) return 0;
+  return (size_t)N * sizeof(double);
+}
+
+bitnet_status bitnet_ternarize_pack(const float *W, int64_t N, int64_t K, uint8_t *packed,
+                                    float *w_scale, void *workspace, size_t workspace_bytes,
+                                    void *stream) {
+  if (!W || !packed || !w_scale) return BITNET_ERR_NULL;
+  if (!shape_ok(1, N, K)) return BITNET_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(w_scale, 4)) return BITNET_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bitnet_ternarize_workspace_bytes(N))
+    return BITNET_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return BITNET_ERR_ALIGN;
+  bitnet_status st = device_check();
+  if (st != BITNET_OK) return st;
+  return from_hip(launch_ternarize_pack(W, (int)N, (int)K, packed, w_scale,
+                                        reinterpret_cast<double *>(workspace),
+                                        as_stream(stream)));
+}
+
+bitnet_status bitnet_quant_act(const float *x, int64_t M, int64_t K, int8_t *xq,
+                               float *x_scale, void *stream) {
+  if (!x || !xq || !x_scale) return BITNET_ERR_NULL;
+  if (!shape_ok(M, 1, K)) return BITNET_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(x_scale, 4)) return BITNET_ERR_ALIGN;
+  bitnet_status st = device_check();
+  if (st != BITNET_OK) return st;
+  return from_hip(launch_quant_rows(x, (int)M, (int)K, xq, nullptr, x_scale, nullptr, nullptr,
+                                    as_stream(stream)));
+}
+
+size_t bitnet_matmul_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 1 || K < 1) return 0;
+  return ws_layout(M, K).total;
+}
+
+static bitnet_status matmul_from_ws(int64_t M, int64_t N, int64_t K, const uint8_t *packed,
+                                    const float *w_scale, float *y, uint8_t *ws,
+                                    int32_t *acc_out, hipStream_t s) {
+  const WsLayout L = ws_layout(M, K);
+  const int8_t *xqp = reinterpret_cast<const int8_t *>(ws + L.xq);
+  const float *xs = reinterpret_cast<const float *>(ws + L.scale);
+  const int32_t *rs = reinterpret_cast<const int32_t *>(ws + L.rowsum);
+  if (M <= kGemvMaxM)
+    return from_hip(launch_gemv((int)M, (int)N, (int)K, xqp, xs, rs, packed, w_scale, y,
+                                acc_out, s));
+  return from_hip(
+      launch_gemm((int)M, (int)N, (int)K, xqp, xs, rs, packed, w_scale, y, acc_out, s));
+}
+
+bitnet_status bitnet_ternary_matmul(int64_t M, int64_t N, int64_t K, const float *x,
+                                    const uint8_t *packed, const float *w_scale, float *y,
+                                    void *workspace, size_t workspace_bytes, int8_t *xq_out,
+                                    float *x_scale_out, int32_t *acc_out, void *stream) {
+  if (!x || !packed || !w_scale || !y) return BITNET_ERR_NULL;
+  if (!shape_ok(M, N, K)) return BITNET_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(w_scale, 4) || !aligned(y, 4) ||
+      (xq_out && !aligned(xq_out, 16)) || (x_scale_out && !aligned(x_scale_out, 4)) ||
+      (acc_out && !aligned(acc_out, 4)))
+    return BITNET_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bitnet_matmul_workspace_bytes(M, K))
+    return BITNET_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BITNET_ERR_ALIGN;
+  bitnet_status st = device_check();
+  if (st != BITNET_OK) return st;
+  hipStream_t s = as_stream(stream);
+  if (M <= kGemvMaxM && gemv_fusable(M, K))
+    return from_hip(launch_gemv_fused((int)M, (int)N, (int)K, x, packed, w_scale, y, xq_out,
+                                      x_scale_out, acc_out, s));
+  uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
+  const WsLayout L = ws_layout(M, K);
+  st = from_hip(launch_quant_rows(x, (int)M, (int)K, xq_out,
+                                  reinterpret_cast<int8_t *>(ws + L.xq),
+                                  reinterpret_cast<float *>(ws + L.scale), x_scale_out,
+                                  reinterpret_cast<int32_t *>(ws + L.rowsum), s));
+  if (st != BITNET_OK) return st;
+  return matmul_from_ws(M, N, K, packed, w_scale, y, ws, acc_out, s);
+}
+
+bitnet_status bitnet_ternary_matmul_q8(int64_t M, int64_t N, int64_t K, const int8_t *xq,
+                                       const float *x_scale, const uint8_t *packed,
+                                       const float *w_scale, float *y, void *workspace,
+                                       size_t workspace_bytes, int32_t *acc_out,
+                                       void *stream) {
+  if (!xq || !x_scale || !packed || !w_scale || !y) return BITNET_ERR_NULL;
+  if (!shape_ok(M, N, K)) return BITNET_ERR_SHAPE;
+  if (!aligned(xq, 16) || !aligned(x_scale, 4) || !aligned(packed, 16) ||
+      !aligned(w_scale, 4) || !aligned(y, 4) || (acc_out && !aligned(acc_out, 4)))
+    return BITNET_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bitnet_matmul_workspace_bytes(M, K))
+    return BITNET_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BITNET_ERR_ALIGN;
+  bitnet_status st = device_check();
+  if (st != BITNET_OK) return st;
+  hipStream_t s = as_stream(stream);
+  uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
+  const WsLayout L = ws_layout(M, K);
+  st = from_hip(launch_permute_q8(xq, x_scale, (int)M, (int)K,
+                                  reinterpret_cast<int8_t *>(ws + L.xq),
+                                  reinterpret_cast<float *>(ws + L.scale),
+                                  reinterpret_cast<int32_t *>(ws + L.rowsum), s));
+  if (st != BITNET_OK) return st;
+  return matmul_from_ws(M, N, K, packed, w_scale, y, ws, acc_out, s);
+}
+
+size_t bitnet_grouped_workspace_bytes(int64_t M, const bitnet_problem *problems_host,
+                                      int32_t count) {
+  if (M < 1 || !problems_host || count < 1) return 0;
+  return group_ws(M, problems_host, count, nullptr);
+}
+
+bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *problems_dev,
+                                            int32_t count, const bitnet_problem *problems_host,
+                                            void *workspace, size_t workspace_bytes,
+                                            void *stream) {
+  if (!problems_dev || !problems_host) return BITNET_ERR_NULL;
+  if (count < 1 || count > kMaxGroup) return BITNET_ERR_SHAPE;
+  if (!aligned(problems_dev, 8)) return BITNET_ERR_ALIGN;
+  for (int32_t i = 0; i < count; ++i) {
+    bitnet_status st = check_problem(M, problems_host[i]);
+    if (st != BITNET_OK) return st;
+  }
+  GroupTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  tab.count = count;
+  tab.M = (int32_t)M;
+  const size_t need = group_ws(M, problems_host, count, tab.ws_off);
+  if (!workspace || workspace_bytes < need) return BITNET_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BITNET_ERR_ALIGN;
+  bitnet_status st = device_check();
+  if (st != BITNET_OK) return st;
+
+  // Dispatch order: longest K first, so the longest-running workgroups start
+  // early and the tail of the launch is made of short ones.
+  int32_t idx[kMaxGroup];
+  for (int32_t i = 0; i < count; ++i) idx[i] = i;
+  std::stable_sort(idx, idx + count, [&](int32_t a, int32_t b) {
+    return problems_host[a].K > problems_host[b].K;
+  });
+  const bool gemv = M <= kGemvMaxM;
+  uint64_t total = 0;
+  for (int32_t s = 0; s < count; ++s) {
+    const bitnet_problem &p = problems_host[idx[s]];
+    total += gemv ? (uint64_t)gemv_blocks(p.N) : (uint64_t)gemm_blocks(M, p.N);
+    if (total >= ((uint64_t)1 << 31)) return BITNET_ERR_SHAPE;
+    tab.blk_end[s] = (uint32_t)total;
+    tab.order[s] = (uint16_t)idx[s];
+  }
+  hipStream_t hs = as_stream(stream);
+  uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
+  if (gemv) {
+    int64_t kmax = 0;
+    for (int32_t i = 0; i < count; ++i) kmax = std::max(kmax, problems_host[i].K);
+    if (gemv_fusable(M, kmax))
+      return from_hip(launch_gemv_grouped(problems_dev, tab, ws, true, (size_t)(M * kmax), hs));
+  }
+  st = from_hip(launch_quant_grouped(problems_dev, tab, ws, hs));
+  if (st != BITNET_OK) return st;
+  if (gemv) return from_hip(launch_gemv_grouped(problems_dev, tab, ws, false, 0, hs));
+  return from_hip(launch_gemm_grouped(problems_dev, tab, ws, hs));
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Device-side helpers shared by the gfx950 kernels of the ternary projection
+// library.  One code path: gfx950 only, wave64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bitnet {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int kUnit = 128;             // codes per packing unit
+constexpr int kUnitBytes = 32;         // bytes per packing unit (2 bits per code)
+constexpr uint32_t kFieldMask = 0x03030303u;
+
+// The four 2-bit fields of one packed dword, each spread into the bytes of one
+// output dword.  For dword d of unit t (bytes 4d..4d+3), output dword g holds in
+// byte c the field value u = code + 1 of input k = 128t + 32g + 4d + c.
+__device__ __forceinline__ v4i unpack_fields(uint32_t d) {
+  v4i b;
+  b.x = (int)(d & kFieldMask);
+  b.y = (int)((d >> 2) & kFieldMask);
+  b.z = (int)((d >> 4) & kFieldMask);
+  b.w = (int)((d >> 6) & kFieldMask);
+  return b;
+}
+
+// Offset of input k inside a row of permuted int8 activations.  Inside each
+// 128-input unit, natural k = 128t + 32g + 4d + c is stored at 128t + 16d + 4g + c,
+// so the 16 activations that meet packed dword d of a unit are 16 contiguous
+// bytes (in the byte order unpack_fields produces).
+__device__ __forceinline__ int perm_offset(int k) {
+  const int t = k >> 7, r = k & 127;
+  const int g = r >> 5, d = (r & 31) >> 2, c = r & 3;
+  return (t << 7) + (d << 4) + (g << 2) + c;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Round half to even, then clamp to [-127, 127] (v_rndne_f32 + v_med3).
+__device__ __forceinline__ int quant_one(float x, float s) {
+  float p = x * s;
+  float r = __builtin_rintf(p);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int)r;
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+         ((uint32_t)(d & 0xff) << 24);
+}
+
+// Dequantization epilogue: acc * w_scale / x_scale, two correctly rounded fp32
+// operations (|acc| < 2^24 converts exactly).
+__device__ __forceinline__ float dequant(int acc, float w_scale, float x_scale) {
+  return ((float)acc * w_scale) / x_scale;
+}
+
+}  // namespace bitnet

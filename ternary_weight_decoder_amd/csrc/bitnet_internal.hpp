@@ -1,0 +1,78 @@
+// Host-side launchers shared between the kernel files and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "bitnet_tm.h"
+
+namespace bitnet {
+
+constexpr int kMaxGroup = BITNET_MAX_GROUP;
+
+// Workspace of one problem: permuted int8 activations [M][K], fp32 scales [M],
+// int32 row sums [M]; each region 256-byte aligned.
+struct WsLayout {
+  size_t xq, scale, rowsum, total;
+};
+
+__host__ __device__ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+__host__ __device__ inline WsLayout ws_layout(int64_t M, int64_t K) {
+  WsLayout w;
+  w.xq = 0;
+  w.scale = align256((size_t)(M * K));
+  w.rowsum = w.scale + align256((size_t)M * 4);
+  w.total = w.rowsum + align256((size_t)M * 4);
+  return w;
+}
+
+// Per-launch table of a grouped call, passed by value as a kernel argument.
+struct GroupTable {
+  int32_t count;
+  int32_t M;
+  uint32_t blk_end[kMaxGroup];   // inclusive prefix sum of workgroups, in dispatch order
+  uint16_t order[kMaxGroup];     // problem index of each dispatch slot
+  uint32_t ws_off[kMaxGroup];    // workspace offset of each problem, in 256-byte units
+};
+
+// ternarize.hip
+hipError_t launch_ternarize_pack(const float *W, int N, int K, uint8_t *packed, float *w_scale,
+                                 double *rowsums, hipStream_t stream);
+
+// quant.hip
+hipError_t launch_quant_rows(const float *x, int M, int K, int8_t *xq_nat, int8_t *xq_perm,
+                             float *x_scale, float *x_scale2, int32_t *rowsum,
+                             hipStream_t stream);
+hipError_t launch_permute_q8(const int8_t *xq, const float *x_scale_in, int M, int K,
+                             int8_t *xq_perm, float *x_scale, int32_t *rowsum,
+                             hipStream_t stream);
+hipError_t launch_quant_grouped(const bitnet_problem *problems, const GroupTable &tab,
+                                uint8_t *workspace, hipStream_t stream);
+
+// gemv.hip  (M <= 16)
+constexpr int kGemvMaxM = 16;
+// Largest M*K whose int8 rows the decode kernel quantizes into LDS itself.
+constexpr int64_t kGemvFusedLdsBytes = 36 * 1024;
+hipError_t launch_gemv(int M, int N, int K, const int8_t *xq_perm, const float *x_scale,
+                       const int32_t *rowsum, const uint8_t *packed, const float *w_scale,
+                       float *y, int32_t *acc_out, hipStream_t stream);
+hipError_t launch_gemv_fused(int M, int N, int K, const float *x, const uint8_t *packed,
+                             const float *w_scale, float *y, int8_t *xq_out,
+                             float *x_scale_out, int32_t *acc_out, hipStream_t stream);
+int gemv_blocks(int64_t N);
+bool gemv_fusable(int64_t M, int64_t K);
+hipError_t launch_gemv_grouped(const bitnet_problem *problems, const GroupTable &tab,
+                               const uint8_t *workspace, bool fused, size_t lds_bytes,
+                               hipStream_t stream);
+
+// gemm.hip  (M > 16)
+hipError_t launch_gemm(int M, int N, int K, const int8_t *xq_perm, const float *x_scale,
+                       const int32_t *rowsum, const uint8_t *packed, const float *w_scale,
+                       float *y, int32_t *acc_out, hipStream_t stream);
+int gemm_blocks(int64_t M, int64_t N);
+hipError_t launch_gemm_grouped(const bitnet_problem *problems, const GroupTable &tab,
+                               const uint8_t *workspace, hipStream_t stream);
+
+}  // namespace bitnet

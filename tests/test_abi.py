@@ -1,0 +1,133 @@
+"""The C-ABI library loads, exports what include/bitnet_tm.h declares, and rejects
+bad arguments on the host.  No compute call is made, so this runs without a GPU:
+every case below fails validation before the library touches the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from ternary_weight_decoder_amd import _build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitnet_tm.h")
+
+ERR = {"NULL": 1, "SHAPE": 2, "ALIGN": 3, "WORKSPACE": 4}
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|size_t|bitnet_status)\s*\*?\s*"
+                                 r"(bitnet_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_build.LIB_PATH):
+        _build.build()
+    lib = ctypes.CDLL(_build.LIB_PATH)
+    p, i64, sz, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int32
+    lib.bitnet_status_string.restype = ctypes.c_char_p
+    lib.bitnet_status_string.argtypes = [i32]
+    lib.bitnet_packed_bytes.restype = sz
+    lib.bitnet_packed_bytes.argtypes = [i64, i64]
+    lib.bitnet_matmul_workspace_bytes.restype = sz
+    lib.bitnet_matmul_workspace_bytes.argtypes = [i64, i64]
+    lib.bitnet_ternarize_workspace_bytes.restype = sz
+    lib.bitnet_ternarize_workspace_bytes.argtypes = [i64]
+    lib.bitnet_ternary_matmul.argtypes = [i64, i64, i64, p, p, p, p, p, sz, p, p, p, p]
+    lib.bitnet_ternary_matmul.restype = i32
+    lib.bitnet_ternarize_pack.argtypes = [p, i64, i64, p, p, p, sz, p]
+    lib.bitnet_ternarize_pack.restype = i32
+    lib.bitnet_quant_act.argtypes = [p, i64, i64, p, p, p]
+    lib.bitnet_quant_act.restype = i32
+    lib.bitnet_ternary_matmul_q8.argtypes = [i64, i64, i64, p, p, p, p, p, p, sz, p, p]
+    lib.bitnet_ternary_matmul_q8.restype = i32
+    lib.bitnet_ternary_matmul_grouped.argtypes = [i64, p, i32, p, p, sz, p]
+    lib.bitnet_ternary_matmul_grouped.restype = i32
+    return lib
+
+
+def test_header_declares_the_three_named_entry_points():
+    fns = declared_functions()
+    for name in ("bitnet_ternarize_pack", "bitnet_quant_act", "bitnet_ternary_matmul"):
+        assert name in fns
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_library_has_gfx950_code_object():
+    data = open(_build.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+def test_size_helpers(L):
+    assert L.bitnet_packed_bytes(1536, 1536) == 589824
+    assert L.bitnet_packed_bytes(8960, 1536) == 3440640
+    assert L.bitnet_ternarize_workspace_bytes(8960) == 8960 * 8
+    ws = L.bitnet_matmul_workspace_bytes(1800, 1536)
+    assert ws >= 1800 * 1536 + 2 * 4 * 1800 and ws % 256 == 0
+    for s in range(0, 7):
+        assert L.bitnet_status_string(s)
+
+
+# Fake, never-dereferenced device addresses: validation rejects before any use.
+A = 0x7f0000000000   # 256-byte aligned
+NULL = None
+
+
+def test_matmul_validation(L):
+    ws_ok = L.bitnet_matmul_workspace_bytes(1, 1536)
+    f = L.bitnet_ternary_matmul
+    assert f(1, 1536, 1536, NULL, A, A, A, A, ws_ok, NULL, NULL, NULL, NULL) == ERR["NULL"]
+    assert f(1, 1536, 1536, A, NULL, A, A, A, ws_ok, NULL, NULL, NULL, NULL) == ERR["NULL"]
+    assert f(1, 1536, 1000, A, A, A, A, A, ws_ok, NULL, NULL, NULL, NULL) == ERR["SHAPE"]
+    assert f(0, 1536, 1536, A, A, A, A, A, ws_ok, NULL, NULL, NULL, NULL) == ERR["SHAPE"]
+    assert f(1, 0, 1536, A, A, A, A, A, ws_ok, NULL, NULL, NULL, NULL) == ERR["SHAPE"]
+    assert f(1, 1 << 31, 128, A, A, A, A, A, ws_ok, NULL, NULL, NULL, NULL) == ERR["SHAPE"]
+    assert f(1 << 20, 1 << 12, 128, A, A, A, A, A, ws_ok, NULL, NULL, NULL, NULL) == ERR["SHAPE"]
+    assert f(1, 1536, 1536, A + 4, A, A, A, A, ws_ok, NULL, NULL, NULL, NULL) == ERR["ALIGN"]
+    assert f(1, 1536, 1536, A, A + 8, A, A, A, ws_ok, NULL, NULL, NULL, NULL) == ERR["ALIGN"]
+    assert f(1, 1536, 1536, A, A, A, A + 2, A, ws_ok, NULL, NULL, NULL, NULL) == ERR["ALIGN"]
+    assert f(1, 1536, 1536, A, A, A, A, A, ws_ok, A + 4, NULL, NULL, NULL) == ERR["ALIGN"]
+    assert f(1, 1536, 1536, A, A, A, A, A, ws_ok - 1, NULL, NULL, NULL, NULL) == ERR["WORKSPACE"]
+    assert f(1, 1536, 1536, A, A, A, A, NULL, ws_ok, NULL, NULL, NULL, NULL) == ERR["WORKSPACE"]
+    assert f(1, 1536, 1536, A, A, A, A, A + 16, ws_ok, NULL, NULL, NULL, NULL) == ERR["ALIGN"]
+
+
+def test_ternarize_and_quant_validation(L):
+    ws = L.bitnet_ternarize_workspace_bytes(64)
+    t = L.bitnet_ternarize_pack
+    assert t(NULL, 64, 128, A, A, A, ws, NULL) == ERR["NULL"]
+    assert t(A, 64, 100, A, A, A, ws, NULL) == ERR["SHAPE"]
+    assert t(A + 4, 64, 128, A, A, A, ws, NULL) == ERR["ALIGN"]
+    assert t(A, 64, 128, A, A, A, ws - 8, NULL) == ERR["WORKSPACE"]
+    assert t(A, 64, 128, A, A, NULL, ws, NULL) == ERR["WORKSPACE"]
+    q = L.bitnet_quant_act
+    assert q(NULL, 4, 128, A, A, NULL) == ERR["NULL"]
+    assert q(A, 4, 130, A, A, NULL) == ERR["SHAPE"]
+    assert q(A, 4, 128, A + 1, A, NULL) == ERR["ALIGN"]
+    q8 = L.bitnet_ternary_matmul_q8
+    wsm = L.bitnet_matmul_workspace_bytes(4, 128)
+    assert q8(4, 8, 128, NULL, A, A, A, A, A, wsm, NULL, NULL) == ERR["NULL"]
+    assert q8(4, 8, 128, A, A, A, A, A, A, wsm - 1, NULL, NULL) == ERR["WORKSPACE"]
+
+
+def test_grouped_validation(L):
+    from ternary_weight_decoder_amd.binding import bitnet_problem
+    arr = (bitnet_problem * 2)()
+    arr[0] = bitnet_problem(A, A, A, A, 1536, 1536)
+    arr[1] = bitnet_problem(A, A, A, A, 256, 1000)
+    g = L.bitnet_ternary_matmul_grouped
+    ref = ctypes.cast(ctypes.byref(arr), ctypes.c_void_p)
+    assert g(1, NULL, 2, ref, A, 1 << 30, NULL) == ERR["NULL"]
+    assert g(1, A, 0, ref, A, 1 << 30, NULL) == ERR["SHAPE"]
+    assert g(1, A, 257, ref, A, 1 << 30, NULL) == ERR["SHAPE"]
+    assert g(1, A, 2, ref, A, 1 << 30, NULL) == ERR["SHAPE"]   # K = 1000
+    arr[1] = bitnet_problem(A, A, NULL, A, 256, 1536)
+    assert g(1, A, 2, ref, A, 1 << 30, NULL) == ERR["NULL"]
+    arr[1] = bitnet_problem(A, A, A, A, 256, 1536)
+    assert g(1, A, 2, ref, A, 16, NULL) == ERR["WORKSPACE"]

@@ -1,0 +1,364 @@
+"""GPU parity: the HIP path against the CPU oracle, element by element.
+
+Inputs come from the seeded generators; the oracle and the HIP library each
+compute from them independently.  Packed bytes, scales, int8 activations and
+int32 accumulators must be bit-exact; fp32 outputs must be within 1e-6
+relative (exactly 0 where the accumulator is 0).  Outputs are pre-filled with a
+NaN sentinel and guarded by a canary tail so that unwritten or overrun elements
+show up.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from ternary_weight_decoder_amd import synth
+from conftest import read_golden
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 1e-6
+CANARY = 4096
+
+
+@pytest.fixture(scope="module")
+def tb():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ternary_weight_decoder_amd import binding
+    binding.lib()
+    return binding
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev_tensor(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def guarded(n, dtype, fill):
+    """A device buffer of n elements + a canary tail, all set to `fill`."""
+    import torch
+    t = torch.full((n + CANARY,), fill, dtype=dtype, device="cuda:0")
+    return t, t[:n]
+
+
+def check_canary(buf, n, fill):
+    tail = buf[n:].cpu().numpy()
+    if np.isnan(fill):
+        assert np.isnan(tail).all(), "canary overwritten"
+    else:
+        assert (tail == fill).all(), "canary overwritten"
+
+
+def assert_y_close(y, ref):
+    assert not np.isnan(y).any(), "unwritten output (NaN sentinel survived)"
+    zero = ref == 0
+    assert (y[zero] == 0).all()
+    rel = np.abs(y.astype(np.float64) - ref.astype(np.float64)) / np.maximum(
+        np.abs(ref.astype(np.float64)), 1e-300)
+    worst = float(rel[~zero].max()) if (~zero).any() else 0.0
+    assert worst <= REL_TOL, f"max relative error {worst:.3e}"
+
+
+def gpu_ternarize_pack(tb, W):
+    import torch
+    N, K = W.shape
+    packed_buf, packed = guarded(N * K // 4, torch.uint8, 0xAB)
+    ws = torch.empty(tb.bitnet_ternarize_workspace_bytes(N), dtype=torch.uint8, device="cuda:0")
+    w_scale = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda:0")
+    tb.bitnet_ternarize_pack_into(dev_tensor(W), N, K, packed, w_scale, ws)
+    torch.cuda.synchronize()
+    check_canary(packed_buf, N * K // 4, 0xAB)
+    return packed.cpu().numpy(), np.float32(w_scale.cpu().numpy()[0])
+
+
+def gpu_matmul(tb, x, packed, w_scale, N, K):
+    import torch
+    M = x.shape[0]
+    ybuf, y = guarded(M * N, torch.float32, float("nan"))
+    accbuf, acc = guarded(M * N, torch.int32, -12345)
+    xqbuf, xq = guarded(M * K, torch.int8, 99)
+    xsbuf, xs = guarded(M, torch.float32, float("nan"))
+    ws = torch.empty(tb.bitnet_matmul_workspace_bytes(M, K), dtype=torch.uint8, device="cuda:0")
+    ws_scale = torch.full((1,), float(w_scale), dtype=torch.float32, device="cuda:0")
+    tb.bitnet_ternary_matmul_into(M, N, K, dev_tensor(x), dev_tensor(packed), ws_scale, y, ws,
+                                  xq, xs, acc)
+    torch.cuda.synchronize()
+    check_canary(ybuf, M * N, float("nan"))
+    check_canary(accbuf, M * N, -12345)
+    check_canary(xqbuf, M * K, 99)
+    check_canary(xsbuf, M, float("nan"))
+    return {"y": y.cpu().numpy().reshape(M, N), "acc": acc.cpu().numpy().reshape(M, N),
+            "xq": xq.cpu().numpy().reshape(M, K), "x_scale": xs.cpu().numpy()}
+
+
+# ---------------------------------------------------------------------------
+# Ternarization + packing
+# ---------------------------------------------------------------------------
+
+TERN_CASES = {
+    "q_1536x1536": lambda: synth.normal_weights(1536, 1536, 0),
+    "kv_256x1536": lambda: synth.normal_weights(256, 1536, 1002),
+    "gate_8960x1536": lambda: synth.normal_weights(8960, 1536, 1004),
+    "down_1536x8960": lambda: synth.normal_weights(1536, 8960, 1006),
+    "t3_8960x1536": lambda: synth.student_t_weights(8960, 1536, 50004),
+    "ragged_37x384": lambda: synth.normal_weights(37, 384, 5),
+    "tiny_1x128": lambda: synth.normal_weights(1, 128, 6),
+    "zero_16x256": lambda: np.zeros((16, 256), np.float32),
+}
+
+
+@pytest.mark.parametrize("case", sorted(TERN_CASES))
+def test_ternarize_pack_parity(tb, case):
+    say(f"[ternarize_pack] {case}")
+    W = TERN_CASES[case]()
+    N, K = W.shape
+    packed_ref, s_ref = oracle.ternarize_pack(W)
+    packed, s = gpu_ternarize_pack(tb, W)
+    assert s.tobytes() == s_ref.tobytes()
+    np.testing.assert_array_equal(packed, packed_ref)
+    _, bad = oracle.unpack(packed, N, K)
+    assert bad == 0
+
+
+def test_ternarize_golden_ties(tb):
+    say("[ternarize_pack] golden ties")
+    rows = read_golden("ternarize_ties.txt")
+    # Example A: row 0 |W| = 1.0, rows 1-2 |W| = 0.25 -> m = 0.5, codes sign / 0 / 0.
+    N, K = 3, 128
+    A = np.array([[1.0] * K, [0.25] * K, [0.25] * K], np.float32)
+    sign = np.where((np.add.outer(np.arange(N), np.arange(K)) % 3) == 0, -1, 1)
+    W = (A * sign).astype(np.float32)
+    packed, s = gpu_ternarize_pack(tb, W)
+    assert s == np.float32(0.5)
+    q, _ = oracle.unpack(packed, N, K)
+    np.testing.assert_array_equal(q, np.stack([sign[0], 0 * sign[1], 0 * sign[2]]).astype(np.int8))
+    assert any(r[0] == "example" for r in rows)
+
+
+# ---------------------------------------------------------------------------
+# Activation quantization
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K", [(1, 1536), (4, 1536), (16, 8960), (17, 128), (256, 1536),
+                                 (1800, 1536), (3, 8960)])
+def test_quant_act_parity(tb, M, K):
+    import torch
+    say(f"[quant_act] M={M} K={K}")
+    x = synth.activations(M, K, seed=M * 7 + K)
+    if M == 3:
+        x[1] = 0.0
+    xq_ref, xs_ref = oracle.quant_act(x)
+    xqbuf, xq = guarded(M * K, torch.int8, 99)
+    xsbuf, xs = guarded(M, torch.float32, float("nan"))
+    tb.bitnet_quant_act_into(dev_tensor(x), M, K, xq, xs)
+    torch.cuda.synchronize()
+    check_canary(xqbuf, M * K, 99)
+    check_canary(xsbuf, M, float("nan"))
+    np.testing.assert_array_equal(xq.cpu().numpy().reshape(M, K), xq_ref)
+    assert xs.cpu().numpy().tobytes() == xs_ref.tobytes()
+
+
+def test_quant_act_golden(tb):
+    import torch
+    say("[quant_act] golden rows")
+    rows = read_golden("quant_act_worked.txt")
+    cur = {}
+    cases = []
+    for r in rows:
+        if r[0] == "row":
+            cur = {}
+            cases.append(cur)
+        elif r[0] == "scale":
+            cur["scale"] = float(r[1])
+        elif r[0] == "x":
+            cur["x"] = [float(v) for v in r[1:]]
+        elif r[0] == "xq":
+            cur["xq"] = [int(v) for v in r[1:]]
+    for c in cases:
+        x = np.zeros((1, 128), np.float32)
+        x[0, :len(c["x"])] = c["x"]
+        xq, xs = tb.bitnet_quant_act(dev_tensor(x))
+        torch.cuda.synchronize()
+        assert xs.cpu().numpy()[0] == np.float32(c["scale"])
+        np.testing.assert_array_equal(xq.cpu().numpy()[0, :len(c["xq"])], c["xq"])
+
+
+# ---------------------------------------------------------------------------
+# Projection: decode GEMV (M <= 16) and prefill GEMM (M > 16)
+# ---------------------------------------------------------------------------
+
+MATMUL_CASES = [(m, 200, 384) for m in range(1, 21)] + [
+    (1, 1536, 1536), (1, 256, 1536), (1, 8960, 1536), (1, 1536, 8960), (4, 1536, 8960),
+    (16, 1536, 8960), (16, 65, 128), (32, 300, 512), (64, 8960, 1536), (256, 1536, 1536),
+    (257, 520, 256), (1800, 300, 1536), (129, 257, 1280),
+]
+
+
+@pytest.mark.parametrize("M,N,K", MATMUL_CASES)
+def test_matmul_parity(tb, M, N, K):
+    say(f"[matmul] M={M} N={N} K={K}")
+    W = synth.normal_weights(N, K, seed=N + K)
+    x = synth.activations(M, K, seed=1000 + M)
+    packed, s = oracle.ternarize_pack(W)
+    ref = oracle.ternary_matmul(x, packed, s, N)
+    got = gpu_matmul(tb, x, packed, s, N, K)
+    np.testing.assert_array_equal(got["xq"], ref["xq"])
+    assert got["x_scale"].tobytes() == ref["x_scale"].tobytes()
+    np.testing.assert_array_equal(got["acc"], ref["acc"])
+    assert_y_close(got["y"], ref["y"])
+
+
+@pytest.mark.parametrize("M", [1, 17])
+def test_matmul_worst_case_magnitude(tb, M):
+    say(f"[matmul] worst-case magnitude M={M}")
+    K, N = 8960, 64
+    x = np.ones((M, K), np.float32)            # absmax 1 -> xq = 127 everywhere
+    W = np.full((N, K), 0.5, np.float32)
+    W[1::2] = -0.5                              # codes +1 on even rows, -1 on odd rows
+    packed, s = oracle.ternarize_pack(W)
+    got = gpu_matmul(tb, x, packed, s, N, K)
+    want = np.where(np.arange(N) % 2 == 0, 127 * K, -127 * K)
+    np.testing.assert_array_equal(got["acc"], np.tile(want, (M, 1)))
+    assert_y_close(got["y"], oracle.ternary_matmul(x, packed, s, N)["y"])
+
+
+@pytest.mark.parametrize("M", [5, 64])
+def test_matmul_q8_parity(tb, M):
+    import torch
+    say(f"[matmul_q8] M={M}")
+    N, K = 300, 1536
+    W = synth.normal_weights(N, K, seed=77)
+    x = synth.activations(M, K, seed=78)
+    packed, s = oracle.ternarize_pack(W)
+    ref = oracle.ternary_matmul(x, packed, s, N)
+    y, acc = tb.bitnet_ternary_matmul_q8(dev_tensor(ref["xq"]), dev_tensor(ref["x_scale"]),
+                                         dev_tensor(packed), dev_tensor(np.array([s])), N,
+                                         return_acc=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
+    assert_y_close(y.cpu().numpy(), ref["y"])
+
+
+def test_zero_activation_row_and_zero_weights(tb):
+    say("[matmul] zero row / zero tensor")
+    M, N, K = 3, 64, 256
+    x = synth.activations(M, K, seed=3)
+    x[1] = 0.0
+    W = synth.normal_weights(N, K, seed=4)
+    packed, s = oracle.ternarize_pack(W)
+    got = gpu_matmul(tb, x, packed, s, N, K)
+    assert got["x_scale"][1] == 1.0 and not got["acc"][1].any() and not got["y"][1].any()
+    Wz = np.zeros((N, K), np.float32)
+    pz, sz = oracle.ternarize_pack(Wz)
+    got = gpu_matmul(tb, x, pz, sz, N, K)
+    assert not got["acc"].any() and not got["y"].any()
+
+
+def test_deterministic_and_input_sensitive(tb):
+    say("[matmul] determinism / smell test")
+    M, N, K = 4, 1536, 1536
+    x = synth.activations(M, K, seed=9)
+    p1, s1 = oracle.ternarize_pack(synth.normal_weights(N, K, 10))
+    p2, s2 = oracle.ternarize_pack(synth.normal_weights(N, K, 11))
+    a = gpu_matmul(tb, x, p1, s1, N, K)
+    b = gpu_matmul(tb, x, p1, s1, N, K)
+    c = gpu_matmul(tb, x, p2, s2, N, K)
+    assert a["y"].tobytes() == b["y"].tobytes()
+    assert (a["y"] != c["y"]).mean() > 0.99
+
+
+def test_misaligned_input_is_rejected_and_nothing_written(tb):
+    import torch
+    say("[matmul] misaligned pointer")
+    M, N, K = 1, 64, 128
+    flat = torch.zeros(M * K + 4, dtype=torch.float32, device="cuda:0")
+    x = flat[1:1 + M * K].view(M, K)
+    packed = torch.zeros(N * K // 4, dtype=torch.uint8, device="cuda:0")
+    w = torch.ones(1, dtype=torch.float32, device="cuda:0")
+    y = torch.full((M, N), float("nan"), device="cuda:0")
+    ws = torch.empty(tb.bitnet_matmul_workspace_bytes(M, K), dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(tb.BitnetError) as ei:
+        tb.bitnet_ternary_matmul_into(M, N, K, x, packed, w, y, ws)
+    assert ei.value.status == 3
+    torch.cuda.synchronize()
+    assert torch.isnan(y).all()
+
+
+# ---------------------------------------------------------------------------
+# Grouped launches: one decoder layer, and the 196-matrix sweep
+# ---------------------------------------------------------------------------
+
+def _layer_inputs(M, problems):
+    Ws = [synth.problem_weights(p) for p in problems]
+    xs = [synth.problem_activations(p, M) for p in problems]
+    return Ws, xs
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 256])
+def test_grouped_layer_parity(tb, M):
+    import torch
+    say(f"[grouped] one layer M={M}")
+    problems = synth.layer_problems()
+    Ws, xs = _layer_inputs(M, problems)
+    packs = [oracle.ternarize_pack(W) for W in Ws]
+    dx = [dev_tensor(x) for x in xs]
+    dp = [dev_tensor(p) for p, _ in packs]
+    ds = [dev_tensor(np.array([s], np.float32)) for _, s in packs]
+    ys = [torch.full((M, p.N), float("nan"), device="cuda:0") for p in problems]
+    plan = tb.GroupedPlan(M, dx, dp, ds, ys, [p.N for p in problems], [p.K for p in problems])
+    plan.run()
+    torch.cuda.synchronize()
+    for i, p in enumerate(problems):
+        ref = oracle.ternary_matmul(xs[i], packs[i][0], packs[i][1], p.N)
+        assert_y_close(ys[i].cpu().numpy(), ref["y"])
+
+
+def test_grouped_sweep_sampled(tb):
+    """All 196 projections at M=1 in one grouped call; GPU-ternarized weights
+    (packed bytes checked in full on a few matrices), outputs checked on a sample
+    of every matrix."""
+    import torch
+    say("[grouped] 196-matrix sweep M=1 (sampled)")
+    M = 1
+    problems = synth.sweep_problems()
+    rng = np.random.default_rng(123)
+    dx, dp, ds, ys, xs, packs_host, scales = [], [], [], [], [], [], []
+    ws_t = torch.empty(max(tb.bitnet_ternarize_workspace_bytes(8960), 16), dtype=torch.uint8,
+                       device="cuda:0")
+    for i, p in enumerate(problems):
+        W = synth.problem_weights(p)
+        Wd = dev_tensor(W)
+        packed = torch.empty(p.N * p.K // 4, dtype=torch.uint8, device="cuda:0")
+        w_scale = torch.empty(1, dtype=torch.float32, device="cuda:0")
+        tb.bitnet_ternarize_pack_into(Wd, p.N, p.K, packed, w_scale, ws_t)
+        if i in (0, 4, 6):
+            torch.cuda.synchronize()
+            pr, sr = oracle.ternarize_pack(W)
+            np.testing.assert_array_equal(packed.cpu().numpy(), pr)
+            assert w_scale.cpu().numpy()[0] == sr
+        x = synth.problem_activations(p, M)
+        xs.append(x)
+        dx.append(dev_tensor(x))
+        dp.append(packed)
+        ds.append(w_scale)
+        ys.append(torch.full((M, p.N), float("nan"), device="cuda:0"))
+    plan = tb.GroupedPlan(M, dx, dp, ds, ys, [p.N for p in problems], [p.K for p in problems])
+    plan.run()
+    torch.cuda.synchronize()
+    for i, p in enumerate(problems):
+        y = ys[i].cpu().numpy()
+        assert not np.isnan(y).any()
+        xq, xsc = oracle.quant_act(xs[i])
+        ns = rng.choice(p.N, size=32, replace=False).astype(np.int64)
+        ms = np.zeros_like(ns)
+        acc, yref = oracle.matmul_sampled(xq, xsc, dp[i].cpu().numpy(), ds[i].cpu().numpy()[0],
+                                          p.N, ms, ns)
+        assert_y_close(y[0, ns], yref)
