@@ -240,15 +240,13 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
   }
   hipStream_t hs = as_stream(stream);
   uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
-  if (gemv) {
-    int64_t kmax = 0;
-    for (int32_t i = 0; i < count; ++i) kmax = std::max(kmax, problems_host[i].K);
-    if (gemv_fusable(M, kmax))
-      return from_hip(launch_gemv_grouped(problems_dev, tab, ws, true, (size_t)(M * kmax), hs));
-  }
+  int64_t kmax = 0;
+  for (int32_t i = 0; i < count; ++i) kmax = std::max(kmax, problems_host[i].K);
+  if (gemv && gemv_fusable(M, kmax))
+    return from_hip(launch_gemv_grouped(problems_dev, tab, ws, true, kmax, hs));
   st = from_hip(launch_quant_grouped(problems_dev, tab, ws, hs));
   if (st != BITNET_OK) return st;
-  if (gemv) return from_hip(launch_gemv_grouped(problems_dev, tab, ws, false, 0, hs));
+  if (gemv) return from_hip(launch_gemv_grouped(problems_dev, tab, ws, false, kmax, hs));
   return from_hip(launch_gemm_grouped(problems_dev, tab, ws, hs));
 }
 

@@ -14,6 +14,34 @@ constexpr int kUnit = 128;             // codes per packing unit
 constexpr int kUnitBytes = 32;         // bytes per packing unit (2 bits per code)
 constexpr uint32_t kFieldMask = 0x03030303u;
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define BITNET_GLOBAL __attribute__((address_space(1)))
+
+// Loads and stores through global-address-space pointers.  Pointers that arrive
+// in structs are generic to the compiler, which would emit flat accesses; those
+// count on both vmcnt and lgkmcnt, so every LDS wait would also drain the memory
+// pipeline.  T must be a scalar or a native (ext_vector_type) vector: HIP's
+// class-based vector types lose the address space on the way.
+template <typename T>
+__device__ __forceinline__ T ld_global(const void *p) {
+  return *(const BITNET_GLOBAL T *)p;
+}
+template <typename T>
+__device__ __forceinline__ void st_global(void *p, T v) {
+  *(BITNET_GLOBAL T *)p = v;
+}
+
+// Raw buffer resource over `bytes` bytes at `base` (stride 0; the 32-bit data
+// format that untyped buffer loads need on gfx9-family parts).  A load whose
+// offset is at or beyond `bytes` returns zeros and makes no memory access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 // The four 2-bit fields of one packed dword, each spread into the bytes of one
 // output dword.  For dword d of unit t (bytes 4d..4d+3), output dword g holds in
 // byte c the field value u = code + 1 of input k = 128t + 32g + 4d + c.

@@ -54,7 +54,10 @@ hipError_t launch_quant_grouped(const bitnet_problem *problems, const GroupTable
 // gemv.hip  (M <= 16)
 constexpr int kGemvMaxM = 16;
 // Largest M*K whose int8 rows the decode kernel quantizes into LDS itself.
-constexpr int64_t kGemvFusedLdsBytes = 36 * 1024;
+#ifndef BITNET_GEMV_FUSED_MAX
+#define BITNET_GEMV_FUSED_MAX (36 * 1024)
+#endif
+constexpr int64_t kGemvFusedLdsBytes = BITNET_GEMV_FUSED_MAX;
 hipError_t launch_gemv(int M, int N, int K, const int8_t *xq_perm, const float *x_scale,
                        const int32_t *rowsum, const uint8_t *packed, const float *w_scale,
                        float *y, int32_t *acc_out, hipStream_t stream);
@@ -64,7 +67,7 @@ hipError_t launch_gemv_fused(int M, int N, int K, const float *x, const uint8_t 
 int gemv_blocks(int64_t N);
 bool gemv_fusable(int64_t M, int64_t K);
 hipError_t launch_gemv_grouped(const bitnet_problem *problems, const GroupTable &tab,
-                               const uint8_t *workspace, bool fused, size_t lds_bytes,
+                               const uint8_t *workspace, bool fused, int64_t kmax,
                                hipStream_t stream);
 
 // gemm.hip  (M > 16)

@@ -71,20 +71,20 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0)
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0;
 
   v4i st_reg[4];
-  uint4 w_cur[CB], w_nxt[CB];
+  u32x4 w_cur[CB], w_nxt[CB];
   const v4i zero4 = v4i{0, 0, 0, 0};
 
   // Prologue: unit 0.
   {
     const v4i *src = reinterpret_cast<const v4i *>(st_src);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st_reg[i] = st_live ? src[i] : zero4;
+    for (int i = 0; i < 4; ++i) st_reg[i] = st_live ? ld_global<v4i>(src + i) : zero4;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<v4i *>(&a_lds[0][st_dst + 16 * i]) = st_reg[i];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
-      w_cur[cb] = n_live[cb] ? *reinterpret_cast<const uint4 *>(w_ptr[cb]) : make_uint4(0, 0, 0, 0);
+      w_cur[cb] = n_live[cb] ? ld_global<u32x4>(w_ptr[cb]) : u32x4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
 
@@ -94,12 +94,12 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0)
     if (more) {
       const v4i *src = reinterpret_cast<const v4i *>(st_src + (size_t)(u + 1) * kUnit);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st_reg[i] = st_live ? src[i] : zero4;
+      for (int i = 0; i < 4; ++i) st_reg[i] = st_live ? ld_global<v4i>(src + i) : zero4;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
         w_nxt[cb] = n_live[cb]
-                        ? *reinterpret_cast<const uint4 *>(w_ptr[cb] + (size_t)(u + 1) * ustride)
-                        : make_uint4(0, 0, 0, 0);
+                        ? ld_global<u32x4>(w_ptr[cb] + (size_t)(u + 1) * ustride)
+                        : u32x4{0u, 0u, 0u, 0u};
     }
     const int8_t *a_base = &a_lds[buf][(wm * WM + li) * LDS_STRIDE + 64 * lh];
 #pragma unroll
@@ -129,22 +129,22 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0)
 
   // Epilogue: element r of a 32x32 block sits at row 8*(r/4) + 4*(lane/32) + r%4,
   // column lane%32.
-  const float ws = *p.w_scale;
+  const float ws = ld_global<float>(p.w_scale);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = m0 + wm * WM + rb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
       if (row >= p.M) continue;
-      const int rs = p.rowsum[row];
-      const float xs = p.x_scale[row];
+      const int rs = ld_global<int>(p.rowsum + row);
+      const float xs = ld_global<float>(p.x_scale + row);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const int n = n0 + wn * WN + cb * 32 + li;
         if (n < p.N) {
           const int a = acc[rb][cb][r] - rs;
-          if (p.acc_out) p.acc_out[(size_t)row * p.N + n] = a;
-          p.y[(size_t)row * p.N + n] = dequant(a, ws, xs);
+          if (p.acc_out) st_global<int>(p.acc_out + (size_t)row * p.N + n, a);
+          st_global<float>(p.y + (size_t)row * p.N + n, dequant(a, ws, xs));
         }
       }
     }

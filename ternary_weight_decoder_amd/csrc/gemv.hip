@@ -8,12 +8,19 @@
 // That keeps the VALU work at the 2-bit unpack alone (7 ops per 16 codes per
 // lane), independent of M, where a dot4 formulation would add 4*M more.
 //
-// Work split: a workgroup (4 waves) owns 16*C output columns; its 4 waves split
-// the K units evenly and add their int32 partials through LDS (exact in any
-// order).  Lane (col = lane%16, h = lane/16) loads 8 bytes = packed dwords
-// 2h, 2h+1 of unit u for column col, so a wave reads 512 contiguous bytes per
-// unit and column tile.  Field values u = code+1 enter the MFMA; the epilogue
+// Work split: each wave owns T column tiles of 16*C columns and walks the full
+// K of each, so no cross-wave reduction is needed; the 4 waves of a workgroup
+// take interleaved tiles, which keeps their reads of one unit adjacent in
+// memory.  Lane (col = lane%16, h = lane/16) loads 8 bytes = packed dwords 2h,
+// 2h+1 of unit u for column col: a wave reads 512 contiguous bytes per unit and
+// 16-column block.  Field values u = code+1 enter the MFMA; the epilogue
 // subtracts the activation row sum.
+//
+// Weights are read with buffer loads kept D (tile, unit) items ahead in a
+// register ring that runs across tile boundaries.  Loads for columns past N or
+// items past the wave's range are aimed past the buffer's end: the hardware
+// returns zeros without touching memory, so every ring slot issues the same
+// instructions and the wait counts stay static.
 //
 // Activation quantization is fused when the M x K int8 rows fit in LDS: every
 // workgroup quantizes the rows itself (absmax, scale, round, row sum) into LDS
@@ -25,9 +32,23 @@
 namespace bitnet {
 namespace {
 
-constexpr int kGemvC = 4;                       // 16-column tiles per workgroup
-constexpr int kGemvCols = 16 * kGemvC;
+#ifndef BITNET_GEMV_C
+#define BITNET_GEMV_C 4
+#endif
+#ifndef BITNET_GEMV_DEPTH
+#define BITNET_GEMV_DEPTH 3
+#endif
+// Weights are read once per call: non-temporal loads keep them from evicting
+// the activations and small tables that every workgroup reuses.
+#ifndef BITNET_GEMV_AUX
+#define BITNET_GEMV_AUX 2
+#endif
+constexpr int kGemvC = BITNET_GEMV_C;           // 16-column blocks per wave tile
+constexpr int kGemvDepth = BITNET_GEMV_DEPTH;   // items in flight per wave
+constexpr int kWeightAux = BITNET_GEMV_AUX;     // cache-policy bits of weight loads
+constexpr int kWaveCols = 16 * kGemvC;          // columns of one wave tile
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 
 struct GemvProblem {
   const uint8_t *packed;
@@ -44,9 +65,8 @@ struct GemvProblem {
 };
 
 struct GemvShared {
-  v4i part[4][kGemvC][64];
-  float red[kGemvMaxM][4];
-  int ired[kGemvMaxM][4];
+  float red[kGemvMaxM][kWaves];
+  int ired[kGemvMaxM][kWaves];
   float scale[kGemvMaxM];
   int rowsum[kGemvMaxM];
 };
@@ -57,10 +77,10 @@ __device__ __forceinline__ void quant_rows_to_lds(const GemvProblem &p, GemvShar
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n4 = p.K >> 2;
   for (int m = 0; m < p.M; ++m) {
-    const float4 *x4 = reinterpret_cast<const float4 *>(p.x + (size_t)m * p.K);
+    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(p.x + (size_t)m * p.K);
     float a = 0.0f;
     for (int i = tid; i < n4; i += kThreads) {
-      const float4 v = x4[i];
+      const f32x4 v = ld_global<f32x4>(x4 + i);
       a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     }
     a = wave_max(a);
@@ -70,23 +90,23 @@ __device__ __forceinline__ void quant_rows_to_lds(const GemvProblem &p, GemvShar
   for (int m = 0; m < p.M; ++m) {
     const float a = fmaxf(fmaxf(sh.red[m][0], sh.red[m][1]), fmaxf(sh.red[m][2], sh.red[m][3]));
     const float s = (a == 0.0f) ? 1.0f : 127.0f / a;
-    const float4 *x4 = reinterpret_cast<const float4 *>(p.x + (size_t)m * p.K);
+    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(p.x + (size_t)m * p.K);
     int8_t *dst = xq_lds + (size_t)m * p.K;
     int sum = 0;
     for (int i = tid; i < n4; i += kThreads) {
-      const float4 v = x4[i];
+      const f32x4 v = ld_global<f32x4>(x4 + i);
       const int q0 = quant_one(v.x, s), q1 = quant_one(v.y, s);
       const int q2 = quant_one(v.z, s), q3 = quant_one(v.w, s);
       sum += q0 + q1 + q2 + q3;
       const uint32_t w = pack4_i8(q0, q1, q2, q3);
       *reinterpret_cast<uint32_t *>(dst + perm_offset(4 * i)) = w;
-      if (write_out) reinterpret_cast<uint32_t *>(p.xq_out + (size_t)m * p.K)[i] = w;
+      if (write_out) st_global<uint32_t>(p.xq_out + (size_t)m * p.K + 4 * i, w);
     }
     sum = wave_sum(sum);
     if (lane == 0) sh.ired[m][wave] = sum;
     if (tid == 0) {
       sh.scale[m] = s;
-      if (write_out) p.x_scale_out[m] = s;
+      if (write_out) st_global<float>(p.x_scale_out + m, s);
     }
   }
   __syncthreads();
@@ -95,105 +115,136 @@ __device__ __forceinline__ void quant_rows_to_lds(const GemvProblem &p, GemvShar
   __syncthreads();
 }
 
+// One workgroup: columns [n_base, n_base + kWaves * T * kWaveCols); wave w owns
+// tiles t = 0..T-1 starting at column n_base + (t * kWaves + w) * kWaveCols.
 template <bool FUSED>
-__device__ __forceinline__ void gemv_block(const GemvProblem &p, int n_base, GemvShared &sh,
-                                           int8_t *xq_lds) {
+__device__ __forceinline__ void gemv_block(const GemvProblem &p, int n_base, int T,
+                                           GemvShared &sh, int8_t *xq_lds) {
   constexpr int C = kGemvC;
+  constexpr int D = kGemvDepth;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
   const int h = lane >> 4;
   const int units = p.K >> 7;
-  const int u0 = (wave * units) >> 2;
-  const int u1 = ((wave + 1) * units) >> 2;
+  const int items = T * units;
+
+  const uint32_t w_bytes = (uint32_t)((size_t)p.N * p.K / 4);
+  const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(p.packed, w_bytes);
+  const uint32_t ustride = (uint32_t)p.N * kUnitBytes;
+  const bool a_live = col < p.M;
+  const uint32_t a_row = (uint32_t)(a_live ? col : 0) * p.K + 32 * h;
+  const uint32_t a_bytes = (uint32_t)((size_t)p.M * p.K);
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(FUSED ? nullptr : p.xqp, FUSED ? 0 : a_bytes);
+  const int lane_col0 = n_base + wave * kWaveCols + col;   // column of block 0, tile 0
+  constexpr int kTileStride = kWaves * kWaveCols;          // column step between tiles
+
+  // Load cursor (tile, unit) of the next item to fetch.
+  int lt = 0, lu = 0;
+  u32x2 wr[D][C];
+  v4i ar0[D], ar1[D];
+  auto load_item = [&](u32x2 *w, v4i &a0, v4i &a1) {
+    const bool live = lt < T;
+    const int ncol = lane_col0 + lt * kTileStride;
+    const uint32_t ub = (uint32_t)lu * ustride + 8 * h;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int n = ncol + 16 * c;
+      const uint32_t off = (live && n < p.N) ? (uint32_t)n * kUnitBytes + ub : w_bytes;
+      w[c] = __builtin_amdgcn_raw_buffer_load_b64(w_rsrc, off, 0, kWeightAux);
+    }
+    if (!FUSED) {
+      const uint32_t ao = (live && a_live) ? a_row + (uint32_t)lu * kUnit : a_bytes;
+      a0 = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, ao, 0, 0);
+      a1 = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, ao + 16, 0, 0);
+    }
+    if (++lu == units) {
+      lu = 0;
+      ++lt;
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < D; ++j) load_item(wr[j], ar0[j], ar1[j]);
 
   if (FUSED) quant_rows_to_lds(p, sh, xq_lds, p.xq_out != nullptr && n_base == 0);
+
+  const float ws = ld_global<float>(p.w_scale);
+  // Row of accumulator element r of this lane, and its dequantization inputs.
+  int row_rs[4];
+  float row_xs[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = min(4 * h + r, p.M - 1);
+    row_rs[r] = FUSED ? sh.rowsum[row] : ld_global<int>(p.rowsum + row);
+    row_xs[r] = FUSED ? sh.scale[row] : ld_global<float>(p.x_scale + row);
+  }
 
   v4i acc[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) acc[c] = v4i{0, 0, 0, 0};
+  const v4i zero4 = v4i{0, 0, 0, 0};
+  int ct = 0, cu = 0;   // compute cursor
 
-  const bool a_live = col < p.M;
-  const int8_t *a_ptr = (FUSED ? xq_lds : p.xqp) + (size_t)col * p.K + 32 * h;
-  const size_t ustride = (size_t)p.N * kUnitBytes;
-  const uint8_t *w_ptr[C];
-  bool n_live[C];
+  for (int base = 0; base < items; base += D) {
 #pragma unroll
-  for (int c = 0; c < C; ++c) {
-    const int n = n_base + 16 * c + col;
-    n_live[c] = n < p.N;
-    w_ptr[c] = p.packed + (size_t)n * kUnitBytes + 8 * h;
-  }
-
-  uint2 w_cur[C], w_nxt[C];
-  v4i a0 = v4i{0, 0, 0, 0}, a1 = v4i{0, 0, 0, 0};
-  if (u0 < u1) {
+    for (int j = 0; j < D; ++j) {
+      const int i = base + j;
+      v4i a0 = zero4, a1 = zero4;
+      if (FUSED) {
+        if (a_live && i < items) {
+          const v4i *ap = reinterpret_cast<const v4i *>(xq_lds + a_row + (uint32_t)cu * kUnit);
+          a0 = ap[0];
+          a1 = ap[1];
+        }
+      } else {
+        a0 = ar0[j];
+        a1 = ar1[j];
+      }
+      // Items past the range carry zero operands: their MFMAs add nothing.
 #pragma unroll
-    for (int c = 0; c < C; ++c)
-      w_cur[c] = n_live[c] ? *reinterpret_cast<const uint2 *>(w_ptr[c] + (size_t)u0 * ustride)
-                           : make_uint2(0u, 0u);
-  }
-  for (int u = u0; u < u1; ++u) {
-    if (u + 1 < u1) {
+      for (int c = 0; c < C; ++c) {
+        acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, unpack_fields(wr[j][c].x), acc[c],
+                                                       0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, unpack_fields(wr[j][c].y), acc[c],
+                                                       0, 0, 0);
+      }
+      load_item(wr[j], ar0[j], ar1[j]);
+      if (i < items && ++cu == units) {
+        // Tile ct complete: element (row = 4h + r, column col) of each block.
+        const int ncol = lane_col0 + ct * kTileStride;
 #pragma unroll
-      for (int c = 0; c < C; ++c)
-        w_nxt[c] = n_live[c]
-                       ? *reinterpret_cast<const uint2 *>(w_ptr[c] + (size_t)(u + 1) * ustride)
-                       : make_uint2(0u, 0u);
-    }
-    if (a_live) {
-      const v4i *ap = reinterpret_cast<const v4i *>(a_ptr + (size_t)u * kUnit);
-      a0 = ap[0];
-      a1 = ap[1];
-    }
+        for (int c = 0; c < C; ++c) {
+          const int n = ncol + 16 * c;
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, unpack_fields(w_cur[c].x), acc[c],
-                                                     0, 0, 0);
-      acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, unpack_fields(w_cur[c].y), acc[c],
-                                                     0, 0, 0);
-    }
-#pragma unroll
-    for (int c = 0; c < C; ++c) w_cur[c] = w_nxt[c];
-  }
-
-#pragma unroll
-  for (int c = 0; c < C; ++c) sh.part[wave][c][lane] = acc[c];
-  __syncthreads();
-
-  const float ws = *p.w_scale;
-  // Output element (row = 4*(l/16) + r, column = l%16) of each 16x16 tile.
-  for (int i = threadIdx.x; i < C * 64; i += kThreads) {
-    const int c = i >> 6, l = i & 63;
-    const int n = n_base + 16 * c + (l & 15);
-    if (n >= p.N) continue;
-    const v4i s = sh.part[0][c][l] + sh.part[1][c][l] + sh.part[2][c][l] + sh.part[3][c][l];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * (l >> 4) + r;
-      if (row < p.M) {
-        const int rs = FUSED ? sh.rowsum[row] : p.rowsum[row];
-        const float xs = FUSED ? sh.scale[row] : p.x_scale[row];
-        const int a = s[r] - rs;
-        if (p.acc_out) p.acc_out[(size_t)row * p.N + n] = a;
-        p.y[(size_t)row * p.N + n] = dequant(a, ws, xs);
+          for (int r = 0; r < 4; ++r) {
+            const int row = 4 * h + r;
+            if (row < p.M && n < p.N) {
+              const int a = acc[c][r] - row_rs[r];
+              if (p.acc_out) st_global<int>(p.acc_out + (size_t)row * p.N + n, a);
+              st_global<float>(p.y + (size_t)row * p.N + n, dequant(a, ws, row_xs[r]));
+            }
+          }
+          acc[c] = zero4;
+        }
+        cu = 0;
+        ++ct;
       }
     }
   }
 }
 
 template <bool FUSED>
-__global__ void __launch_bounds__(kThreads) gemv_kernel(GemvProblem p) {
+__global__ void __launch_bounds__(kThreads) gemv_kernel(GemvProblem p, int T) {
   __shared__ GemvShared sh;
   extern __shared__ __attribute__((aligned(16))) int8_t xq_lds[];
-  gemv_block<FUSED>(p, blockIdx.x * kGemvCols, sh, xq_lds);
+  gemv_block<FUSED>(p, blockIdx.x * kWaves * T * kWaveCols, T, sh, xq_lds);
 }
 
 // Grouped: dispatch slot s of the table owns workgroups [blk_end[s-1], blk_end[s]).
 template <bool FUSED>
 __global__ void __launch_bounds__(kThreads)
     gemv_grouped_kernel(const bitnet_problem *__restrict__ problems, GroupTable tab,
-                        const uint8_t *__restrict__ workspace) {
+                        const uint8_t *__restrict__ workspace, int T) {
   __shared__ GemvShared sh;
   extern __shared__ __attribute__((aligned(16))) int8_t xq_lds[];
   const uint32_t b = blockIdx.x;
@@ -229,12 +280,21 @@ __global__ void __launch_bounds__(kThreads)
   p.N = (int)pr.N;
   p.K = (int)pr.K;
   p.M = M;
-  gemv_block<FUSED>(p, (int)(b - first) * kGemvCols, sh, xq_lds);
+  gemv_block<FUSED>(p, (int)(b - first) * kWaves * T * kWaveCols, T, sh, xq_lds);
 }
 
 }  // namespace
 
-int gemv_blocks(int64_t N) { return (int)((N + kGemvCols - 1) / kGemvCols); }
+#ifndef BITNET_GEMV_T
+#define BITNET_GEMV_T 1
+#endif
+// Tiles per wave (a workgroup covers 4 * T * 16 * C columns).
+int gemv_tiles_per_wave() { return BITNET_GEMV_T; }
+
+int gemv_blocks(int64_t N) {
+  const int64_t cols = (int64_t)kWaves * gemv_tiles_per_wave() * kWaveCols;
+  return (int)((N + cols - 1) / cols);
+}
 
 bool gemv_fusable(int64_t M, int64_t K) { return M * K <= kGemvFusedLdsBytes; }
 
@@ -243,7 +303,7 @@ hipError_t launch_gemv(int M, int N, int K, const int8_t *xq_perm, const float *
                        float *y, int32_t *acc_out, hipStream_t stream) {
   GemvProblem p{packed, nullptr, xq_perm, x_scale, rowsum, w_scale, y, acc_out,
                 nullptr, nullptr, N, K, M};
-  gemv_kernel<false><<<gemv_blocks(N), kThreads, 0, stream>>>(p);
+  gemv_kernel<false><<<gemv_blocks(N), kThreads, 0, stream>>>(p, gemv_tiles_per_wave());
   return hipGetLastError();
 }
 
@@ -252,18 +312,21 @@ hipError_t launch_gemv_fused(int M, int N, int K, const float *x, const uint8_t 
                              float *x_scale_out, int32_t *acc_out, hipStream_t stream) {
   GemvProblem p{packed, x, nullptr, nullptr, nullptr, w_scale, y, acc_out,
                 xq_out, x_scale_out, N, K, M};
-  gemv_kernel<true><<<gemv_blocks(N), kThreads, (size_t)M * K, stream>>>(p);
+  gemv_kernel<true><<<gemv_blocks(N), kThreads, (size_t)M * K, stream>>>(
+      p, gemv_tiles_per_wave());
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_grouped(const bitnet_problem *problems, const GroupTable &tab,
-                               const uint8_t *workspace, bool fused, size_t lds_bytes,
+                               const uint8_t *workspace, bool fused, int64_t kmax,
                                hipStream_t stream) {
   const unsigned blocks = tab.blk_end[tab.count - 1];
+  const int T = gemv_tiles_per_wave();
   if (fused)
-    gemv_grouped_kernel<true><<<blocks, kThreads, lds_bytes, stream>>>(problems, tab, workspace);
+    gemv_grouped_kernel<true><<<blocks, kThreads, (size_t)(tab.M * kmax), stream>>>(
+        problems, tab, workspace, T);
   else
-    gemv_grouped_kernel<false><<<blocks, kThreads, 0, stream>>>(problems, tab, workspace);
+    gemv_grouped_kernel<false><<<blocks, kThreads, 0, stream>>>(problems, tab, workspace, T);
   return hipGetLastError();
 }
 

@@ -38,30 +38,30 @@ __device__ __forceinline__ void quant_row(const float *__restrict__ xr, int K,
                                           int32_t *__restrict__ rowsum_out) {
   __shared__ float fred[4];
   __shared__ int ired[4];
-  const float4 *x4 = reinterpret_cast<const float4 *>(xr);
+  const f32x4 *x4 = reinterpret_cast<const f32x4 *>(xr);
   const int n4 = K >> 2;
   float a = 0.0f;
   for (int i = threadIdx.x; i < n4; i += kQuantThreads) {
-    const float4 v = x4[i];
+    const f32x4 v = ld_global<f32x4>(x4 + i);
     a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
   }
   a = block_max(a, fred);
   const float s = (a == 0.0f) ? 1.0f : 127.0f / a;
   int sum = 0;
   for (int i = threadIdx.x; i < n4; i += kQuantThreads) {
-    const float4 v = x4[i];
+    const f32x4 v = ld_global<f32x4>(x4 + i);
     const int q0 = quant_one(v.x, s), q1 = quant_one(v.y, s);
     const int q2 = quant_one(v.z, s), q3 = quant_one(v.w, s);
     sum += q0 + q1 + q2 + q3;
     const uint32_t w = pack4_i8(q0, q1, q2, q3);
-    if (nat) reinterpret_cast<uint32_t *>(nat)[i] = w;
-    if (perm) *reinterpret_cast<uint32_t *>(perm + perm_offset(4 * i)) = w;
+    if (nat) st_global<uint32_t>(nat + 4 * i, w);
+    if (perm) st_global<uint32_t>(perm + perm_offset(4 * i), w);
   }
   sum = block_sum(sum, ired);
   if (threadIdx.x == 0) {
-    if (scale_out) *scale_out = s;
-    if (scale_out2) *scale_out2 = s;
-    if (rowsum_out) *rowsum_out = sum;
+    if (scale_out) st_global<float>(scale_out, s);
+    if (scale_out2) st_global<float>(scale_out2, s);
+    if (rowsum_out) st_global<int>(rowsum_out, sum);
   }
 }
 
@@ -87,15 +87,15 @@ __global__ void __launch_bounds__(kQuantThreads)
   const uint32_t *src = reinterpret_cast<const uint32_t *>(xq + off);
   int sum = 0;
   for (int i = threadIdx.x; i < (K >> 2); i += kQuantThreads) {
-    const uint32_t w = src[i];
+    const uint32_t w = ld_global<uint32_t>(src + i);
     sum += (int)(int8_t)(w & 0xff) + (int)(int8_t)((w >> 8) & 0xff) +
            (int)(int8_t)((w >> 16) & 0xff) + (int)(int8_t)(w >> 24);
-    *reinterpret_cast<uint32_t *>(xq_perm + off + perm_offset(4 * i)) = w;
+    st_global<uint32_t>(xq_perm + off + perm_offset(4 * i), w);
   }
   sum = block_sum(sum, ired);
   if (threadIdx.x == 0) {
-    x_scale[row] = x_scale_in[row];
-    rowsum[row] = sum;
+    st_global<float>(x_scale + row, ld_global<float>(x_scale_in + row));
+    st_global<int>(rowsum + row, sum);
   }
 }
 

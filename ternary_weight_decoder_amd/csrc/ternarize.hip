@@ -19,16 +19,16 @@ __global__ void __launch_bounds__(256) absrow_kernel(const float *__restrict__ W
                                                      double *__restrict__ rowsums) {
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
   if (n >= N) return;
-  const float4 *r = reinterpret_cast<const float4 *>(W + (size_t)n * K);
+  const f32x4 *r = reinterpret_cast<const f32x4 *>(W + (size_t)n * K);
   double s = 0.0;
   for (int i = 0; i < (K >> 2); ++i) {
-    const float4 v = r[i];
+    const f32x4 v = ld_global<f32x4>(r + i);
     s += fabs((double)v.x);
     s += fabs((double)v.y);
     s += fabs((double)v.z);
     s += fabs((double)v.w);
   }
-  rowsums[n] = s;
+  st_global<double>(rowsums + n, s);
 }
 
 // One thread: rows added with n ascending, then the mean rounded to fp32.
@@ -36,8 +36,8 @@ __global__ void absmean_final_kernel(const double *__restrict__ rowsums, int N, 
                                      float *__restrict__ w_scale) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   double t = 0.0;
-  for (int n = 0; n < N; ++n) t += rowsums[n];
-  *w_scale = (float)(t / count);
+  for (int n = 0; n < N; ++n) t += ld_global<double>(rowsums + n);
+  st_global<float>(w_scale, (float)(t / count));
 }
 
 __device__ __forceinline__ uint32_t field_of(float w, float m) {
@@ -59,18 +59,18 @@ __global__ void __launch_bounds__(256) pack_kernel(const float *__restrict__ W, 
   const int64_t rest = idx >> 3;
   const int n = (int)(rest % N);
   const int t = (int)(rest / N);
-  const float m = *w_scale;
+  const float m = ld_global<float>(w_scale);
   const float *row = W + (size_t)n * K + (size_t)t * kUnit + 4 * d;
   uint32_t out = 0;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const float4 v = *reinterpret_cast<const float4 *>(row + 32 * g);
+    const f32x4 v = ld_global<f32x4>(row + 32 * g);
     out |= field_of(v.x, m) << (0 + 2 * g);
     out |= field_of(v.y, m) << (8 + 2 * g);
     out |= field_of(v.z, m) << (16 + 2 * g);
     out |= field_of(v.w, m) << (24 + 2 * g);
   }
-  packed[idx] = out;
+  st_global<uint32_t>(packed + idx, out);
 }
 
 }  // namespace
