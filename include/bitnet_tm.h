@@ -50,7 +50,9 @@
  *   - Pointers that are read or written with vector loads must be 16-byte
  *     aligned (x, W, packed, xq, xq_out, workspace); others need their natural
  *     alignment.
- *   - Size limits: M, N, K >= 1, K % 128 == 0, and M*K, N*K, M*N each below 2^31.
+ *   - Size limits: M, N, K >= 1, K % 128 == 0, M*K and N*K below 2^31, and
+ *     (M + 128) * N * 4 below 2^31 (the fp32 output is addressed with 32-bit
+ *     byte offsets).
  */
 #ifndef BITNET_TM_H
 #define BITNET_TM_H

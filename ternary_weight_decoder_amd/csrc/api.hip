@@ -23,6 +23,8 @@ bool shape_ok(int64_t M, int64_t N, int64_t K) {
   if (K % 128 != 0) return false;  // 128 codes per packing unit
   if (M >= kLimit || N >= kLimit || K >= kLimit) return false;
   if (M * K >= kLimit || N * K >= kLimit || M * N >= kLimit) return false;
+  // Byte offsets of the fp32 output, including a 128-row tile past M, stay 32-bit.
+  if ((M + 128) * N * 4 >= kLimit) return false;
   return true;
 }
 

@@ -34,6 +34,13 @@ __device__ __forceinline__ void st_global(void *p, T v) {
   *(BITNET_GLOBAL T *)p = v;
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding and leaves the other counters alone (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int vmcnt_wait(int n) {
+  return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8);
+}
+
 // Raw buffer resource over `bytes` bytes at `base` (stride 0; the 32-bit data
 // format that untyped buffer loads need on gfx9-family parts).  A load whose
 // offset is at or beyond `bytes` returns zeros and makes no memory access.

@@ -37,6 +37,24 @@ struct GroupTable {
   uint32_t ws_off[kMaxGroup];    // workspace offset of each problem, in 256-byte units
 };
 
+// Dispatch slot of workgroup b in a grouped launch (binary search over the
+// block ranges; the index is uniform, so the table is read through the scalar
+// cache), the first workgroup of that slot and its problem index.
+struct SlotInfo {
+  int slot;
+  uint32_t first;
+  int problem;
+};
+
+__device__ __forceinline__ SlotInfo find_slot(const GroupTable &tab, uint32_t b) {
+  int lo = 0, hi = tab.count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (b < tab.blk_end[mid]) hi = mid; else lo = mid + 1;
+  }
+  return SlotInfo{lo, lo ? tab.blk_end[lo - 1] : 0u, (int)tab.order[lo]};
+}
+
 // ternarize.hip
 hipError_t launch_ternarize_pack(const float *W, int N, int K, uint8_t *packed, float *w_scale,
                                  double *rowsums, hipStream_t stream);

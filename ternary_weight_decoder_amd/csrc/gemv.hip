@@ -248,14 +248,9 @@ __global__ void __launch_bounds__(kThreads)
   __shared__ GemvShared sh;
   extern __shared__ __attribute__((aligned(16))) int8_t xq_lds[];
   const uint32_t b = blockIdx.x;
-  int lo = 0, hi = tab.count - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (b < tab.blk_end[mid]) hi = mid; else lo = mid + 1;
-  }
-  const int slot = lo;
-  const uint32_t first = slot ? tab.blk_end[slot - 1] : 0u;
-  const int pi = tab.order[slot];
+  const SlotInfo si = find_slot(tab, b);
+  const uint32_t first = si.first;
+  const int pi = si.problem;
   const bitnet_problem pr = problems[pi];
   const int M = tab.M;
   GemvProblem p;
