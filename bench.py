@@ -1,23 +1,30 @@
 #!/usr/bin/env python3
 """Benchmark of the ternary projection path on one MI355X.
 
-Workload (the JSON line's `value`): one decode token through every ternary
-projection of the 28-layer, 1536-hidden decoder -- 196 matrices (q, k, v, o,
-gate, up, down per layer), M = 1 -- as one grouped launch per step: per-row
-int8 quantization of each projection's activations, the ternary x int8
-contraction and the fp32 dequantization, all inside the decode kernel.  The
-weights (seeded synthetic fp32 masters, ~N(0, 0.02)) are ternarized and packed
-on the GPU once before timing, as the format ships pre-ternarized weights.
-Two copies of the 327.5 MB packed set alternate between steps so the reads come
-from HBM rather than the 256 MB last-level cache.
+Headline (`value`): one decode token through every ternary projection of the
+28-layer, 1536-hidden decoder -- 196 matrices (q, k, v, o, gate, up, down per
+layer) at M = 1 -- as one grouped launch per step: per-row int8 quantization of
+each projection's activations, the ternary x int8 contraction and the fp32
+dequantization, all inside one kernel.  `value` is packed-weight GB/s.  The
+weights (seeded fp32 masters ~N(0, 0.02)) are ternarized and packed on the GPU
+once before timing, as the format ships pre-ternarized weights.  Two copies of
+the 327.5 MB packed set alternate between steps so the reads come from HBM
+rather than the 256 MB last-level cache.
 
-Also reported in the same line: the prefill half of the metric (M = 256 tokens
-through the same 196 matrices, int8 TOPS), the offline ternarize+pack rate, and
-the CPU oracle timed on a bounded sample of the decode workload on this host.
+`roofline` describes that decode kernel: algorithmic bytes per launch (packed
+codes + fp32 activations + fp32 outputs + scales) over the launch duration
+timed with HIP events on the launch stream.  `traffic` comes from the counter
+summary in profiles/ when it was taken on the current kernel source.
+
+`configs` reports the other workloads (single 1536x1536 GEMV, one decoder
+layer, the sweep at M = 4 and 16, prefill at M = 256 and 1800, batched decode
+at M = 32 and 64); `cpu_baseline` times the CPU oracle on a bounded sample of
+the headline workload on this host.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -31,8 +38,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0       # MI355X dense int8 MFMA
-
 METRIC = "ternary matmul: decode weight GB/s (% HBM peak); prefill int8 TOPS (% MFMA peak)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_grouped_decode_sweep_m1_pmc.txt")
+DECODE_SOURCES = ("gemv.hip", "bitnet_device.hpp", "bitnet_internal.hpp")
 
 
 def log(msg):
@@ -45,30 +53,88 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=28)
-    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--only", choices=("all", "decode", "prefill", "copy"), default="all",
+                    help="decode: headline only; prefill: one prefill step size (--prefill-m) "
+                         "only; copy: 1 GiB copy probe used to calibrate the byte counters")
     ap.add_argument("--prefill-m", type=int, default=256)
-    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the timed CPU-oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
 
+def host_cpu() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip() + f" ({os.cpu_count()} logical CPUs)"
+    except OSError:
+        pass
+    return "unknown"
+
+
+def decode_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "ternary_weight_decoder_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Timer:
+    """HIP events on the launch stream around a block of launches."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def time(self, fn, steps, warmup=3):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for i in range(steps):
+            fn(i)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps   # ms per step
+
+
+def copy_probe(torch):
+    """A plain 1 GiB elementwise copy (negation), five times: the byte-counter
+    reference (1 GiB read and 1 GiB written per launch)."""
+    n = (1 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": 4 * n, "launches": 5}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path would shard by replicating weights per GPU, see the design notes)",
-              file=sys.stderr)
+        print(f"bench.py: this implementation runs on one GPU; --gpus {args.gpus} is not "
+              "supported (multi-GPU operation would replicate the packed weights per GPU; "
+              "see the design notes)", file=sys.stderr)
         sys.exit(2)
 
     import torch
     from ternary_weight_decoder_amd import binding as tb, synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.only == "copy":
+        copy_probe(torch)
+        return
     dev = torch.device("cuda:0")
     tb.lib()
     stream = torch.cuda.current_stream()
+    timer = Timer(torch, stream)
 
     problems = synth.sweep_problems(args.layers)
     n_mat = len(problems)
@@ -78,8 +144,7 @@ def main():
     packed, w_scales = [], []
     ws_t = torch.empty(tb.bitnet_ternarize_workspace_bytes(synth.INTERMEDIATE), dtype=torch.uint8,
                        device=dev)
-    tern_ms = 0.0
-    w_bytes = 0
+    tern_ms, w_bytes = 0.0, 0
     for p in problems:
         W = torch.from_numpy(synth.problem_weights(p)).to(dev)
         pk = torch.empty(p.N * p.K // 4, dtype=torch.uint8, device=dev)
@@ -95,89 +160,100 @@ def main():
         w_scales.append(sc)
         del W
     packed_bytes = sum(p.N * p.K // 4 for p in problems)
-
-    # ---- decode sweep, M = 1 --------------------------------------------------
-    M = 1
-    xs_host = [synth.problem_activations(p, M) for p in problems]
-    xs = [torch.from_numpy(x).to(dev) for x in xs_host]
-    ys = [torch.empty((M, p.N), dtype=torch.float32, device=dev) for p in problems]
+    copy_b = [t.clone() for t in packed]
     Ns = [p.N for p in problems]
     Ks = [p.K for p in problems]
-    copy_b = [t.clone() for t in packed]
-    plans = [tb.GroupedPlan(M, xs, packed, w_scales, ys, Ns, Ks),
-             tb.GroupedPlan(M, xs, copy_b, w_scales, ys, Ns, Ks)]
-    alg_bytes = (packed_bytes + sum(M * p.K * 4 for p in problems) +
-                 sum(M * p.N * 4 for p in problems) + 4 * n_mat)
 
-    log(f"[bench] decode: warmup {args.warmup}, timed {args.steps} steps")
-    for i in range(args.warmup):
-        plans[i % 2].run()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        plans[i % 2].run()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_total = start.elapsed_time(end)
-    ms_step = ms_total / args.steps
+    def alg_bytes(M, probs):
+        return (sum(p.N * p.K // 4 for p in probs) + sum(M * p.K * 4 for p in probs) +
+                sum(M * p.N * 4 for p in probs) + 4 * len(probs))
+
+    def decode_plans(M, probs=problems, xs_host=None, copies=(packed, copy_b)):
+        idx = [problems.index(p) for p in probs] if probs is not problems else range(n_mat)
+        if xs_host is None:
+            xs = [torch.from_numpy(synth.problem_activations(p, M)).to(dev) for p in probs]
+        else:
+            xs = [torch.from_numpy(x).to(dev) for x in xs_host]
+        ys = [torch.empty((M, p.N), dtype=torch.float32, device=dev) for p in probs]
+        plans = [tb.GroupedPlan(M, xs, [c[i] for i in idx], [w_scales[i] for i in idx], ys,
+                                [p.N for p in probs], [p.K for p in probs]) for c in copies]
+        return plans, xs, ys
+
+    if args.only == "prefill":
+        M = args.prefill_m
+        log(f"[bench] prefill M={M} only")
+        res = prefill_config(torch, tb, timer, problems, packed, w_scales, M, dev)
+        print(json.dumps({"workload": f"prefill M={M} over {n_mat} matrices", **res}), flush=True)
+        return
+
+    # ---- headline: decode sweep, M = 1 ------------------------------------------
+    M = 1
+    xs_host = [synth.problem_activations(p, M) for p in problems]
+    plans, xs, ys = decode_plans(M, xs_host=xs_host)
+    steps = args.steps
+    log(f"[bench] decode sweep M=1: warmup {args.warmup}, timed {steps} steps")
+    ms_step = timer.time(lambda i=0: plans[i % 2].run(), steps, warmup=args.warmup)
     weight_gbps = packed_bytes / (ms_step * 1e-3) / 1e9
-    achieved = alg_bytes / (ms_step * 1e-3) / 1e9
-    log(f"[bench] decode {ms_step * 1e3:.1f} us/step, weight {weight_gbps:.0f} GB/s")
+    bytes_launch = alg_bytes(M, problems)
+    achieved = bytes_launch / (ms_step * 1e-3) / 1e9
+    log(f"[bench] decode {ms_step * 1e3:.1f} us/step, weight {weight_gbps:.0f} GB/s, "
+        f"all bytes {achieved:.0f} GB/s")
 
-    # ---- prefill, M = 256 tokens through the same 196 matrices ---------------
-    prefill = None
-    if not args.no_prefill:
-        Mp = args.prefill_m
-        pproblems = synth.prefill_problems(args.layers)
-        pxs = [torch.from_numpy(synth.problem_activations(p, Mp)).to(dev) for p in pproblems]
-        pys = [torch.empty((Mp, p.N), dtype=torch.float32, device=dev) for p in pproblems]
-        pplan = tb.GroupedPlan(Mp, pxs, packed, w_scales, pys, Ns, Ks)
-        for _ in range(3):
-            pplan.run()
-        torch.cuda.synchronize()
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record(stream)
-        for _ in range(args.prefill_steps):
-            pplan.run()
-        s1.record(stream)
-        torch.cuda.synchronize()
-        pms = s0.elapsed_time(s1) / args.prefill_steps
-        ops = 2.0 * Mp * sum(p.N * p.K for p in pproblems)
-        tops = ops / (pms * 1e-3) / 1e12
-        prefill = {"workload": f"prefill M={Mp} over {len(pproblems)} matrices, one grouped call "
-                               "(quantization launch + int8 MFMA GEMM launch)",
-                   "ms_per_step": round(pms, 4), "int8_TOPS": round(tops, 2),
-                   "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
-                   "ops_per_step": ops}
-        log(f"[bench] prefill {pms:.3f} ms/step, {tops:.0f} TOPS")
-        del pxs, pys, pplan
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            recs = [json.loads(s) for s in f if s.startswith("{")]
+        if recs and recs[-1].get("source_hash") == decode_source_hash():
+            traffic = recs[-1].get("bytes_per_launch")
 
-    # ---- CPU oracle on a bounded sample of the decode workload ----------------
+    configs = {}
+    if args.only == "all" and not args.no_configs:
+        configs = other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales,
+                                alg_bytes, decode_plans, dev)
+
+    # ---- CPU oracle on a bounded sample of the headline workload -------------
     cpu = None
-    if not args.no_cpu_baseline:
+    if args.only == "all" and not args.no_cpu_baseline:
         import oracle
         cores = oracle.num_threads()
-        t_spent, bytes_done, mats = 0.0, 0, 0
-        max_rel = 0.0
+        t_spent, bytes_done, mats, max_rel, packed_equal = 0.0, 0, 0, 0.0, 0
+        plans[0].run()
+        torch.cuda.synchronize()
+        refs = []
         for i, p in enumerate(problems):
             W = synth.problem_weights(p)
             pk_ref, s_ref = oracle.ternarize_pack(W)      # offline step, not timed
+            refs.append((pk_ref, s_ref))
             t0 = time.perf_counter()
             ref = oracle.ternary_matmul(xs_host[i], pk_ref, s_ref, p.N)
             t_spent += time.perf_counter() - t0
             bytes_done += p.N * p.K // 4
             mats += 1
+            packed_equal += int(np.array_equal(packed[i].cpu().numpy(), pk_ref))
             y_gpu = ys[i].cpu().numpy()
             rel = np.abs(y_gpu - ref["y"]) / np.maximum(np.abs(ref["y"]), 1e-30)
             max_rel = max(max_rel, float(rel.max()))
             if t_spent >= args.cpu_seconds:
                 break
+        # The same oracle on one thread, over the first layer's 7 projections.
+        oracle.set_num_threads(1)
+        t1, b1 = 0.0, 0
+        for i, p in enumerate(problems[:min(7, mats)]):
+            t0 = time.perf_counter()
+            oracle.ternary_matmul(xs_host[i], refs[i][0], refs[i][1], p.N)
+            t1 += time.perf_counter() - t0
+            b1 += p.N * p.K // 4
+        oracle.set_num_threads(cores)
         cpu = {"value": round(bytes_done / t_spent / 1e9, 4), "unit": "GB/s", "cores": cores,
                "kind": "oracle",
                "sample": f"first {mats} of {n_mat} decode projections (layers in order, M=1): "
-                         f"quantize + unpack + int32 matmul + dequant, {t_spent:.1f} s; "
-                         f"GPU outputs agree with it to max rel err {max_rel:.2e}"}
+                         f"per-row quantize, unpack, int32 add/sub contraction, dequantize; "
+                         f"{t_spent:.1f} s of oracle time on {cores} threads; GPU-packed codes "
+                         f"equal to the oracle's in {packed_equal}/{mats} matrices; GPU outputs "
+                         f"agree to max relative error {max_rel:.2e}",
+               "single_thread": {"value": round(b1 / t1 / 1e9, 4), "unit": "GB/s",
+                                 "sample": "layer 0's 7 projections, M=1, 1 thread"},
+               "host_cpu": host_cpu()}
         log(f"[bench] cpu oracle {cpu['value']} GB/s on {cores} threads ({mats} matrices)")
 
     line = {
@@ -185,7 +261,7 @@ def main():
         "value": round(weight_gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 6),
         "higher_is_better": True,
@@ -193,20 +269,160 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": f"decode sweep: {n_mat} ternary projections ({args.layers} layers "
-                               "x q,k,v,o,gate,up,down; hidden 1536, intermediate 8960), M=1, "
-                               "one grouped launch per step",
-                   "M": M, "matrices": n_mat, "packed_weight_bytes": packed_bytes,
+        "config": {"workload": f"decode sweep: all {n_mat} ternary projections of a "
+                               f"{args.layers}-layer decoder (q,k,v,o 1536->1536/256; gate,up "
+                               "1536->8960; down 8960->1536), M=1, one grouped launch per step",
+                   "M": 1, "matrices": n_mat, "packed_weight_bytes": packed_bytes,
                    "weight_copies_rotated": 2},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "bytes_per_launch": alg_bytes},
+                     "traffic": traffic, "algorithmic_bytes_per_launch": bytes_launch,
+                     "kernel": "gemv_grouped_kernel<fused quantization>"},
         "cpu_baseline": cpu,
-        "prefill": prefill,
-        "ternarize_pack": {"ms_total": round(tern_ms, 3),
+        "ternarize_pack": {"workload": f"{n_mat} matrices, fp32 masters read once",
+                           "ms_total": round(tern_ms, 3),
                            "fp32_read_GBps": round(w_bytes / (tern_ms * 1e-3) / 1e9, 1)},
+        "configs": configs,
     }
     print(json.dumps(line), flush=True)
+
+
+def gpu_activations(torch, g, M, K, dev):
+    """~N(0,1) rows with 1% of the channels scaled by 20, drawn on the GPU."""
+    x = torch.randn((M, K), generator=g, device=dev)
+    cols = torch.randperm(K, generator=g, device=dev)[:max(1, K // 100)]
+    x[:, cols] *= 20.0
+    return x
+
+
+def prefill_config(torch, tb, timer, problems, packed, w_scales, M, dev):
+    g = torch.Generator(device=dev)
+    g.manual_seed(30000 + M)
+    xs = [gpu_activations(torch, g, M, p.K, dev) for p in problems]
+    ys = [torch.empty((M, p.N), device=dev) for p in problems]
+    plan = tb.GroupedPlan(M, xs, packed, w_scales, ys, [p.N for p in problems],
+                          [p.K for p in problems])
+    ms = timer.time(lambda i=0: plan.run(), 5 if M > 1000 else 10, warmup=2)
+    ops = 2.0 * M * sum(p.N * p.K for p in problems)
+    res = {"ms_per_step": round(ms, 4), "int8_TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
+           "frac_of_int8_peak": round(ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+           "step": "quantization launch + int8 MFMA GEMM launch over all matrices",
+           "activations": "seeded on the GPU: N(0,1), 1% of channels x20"}
+    del xs, ys, plan
+    torch.cuda.empty_cache()
+    return res
+
+
+def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, alg_bytes,
+                  decode_plans, dev):
+    out = {}
+    # Single 1536x1536 GEMV at M=1 (weights seed 0), 600 packed copies rotated
+    # (354 MB) so each launch reads from HBM; this size is launch-latency bound.
+    W, x = synth.single_gemv(seed=0)
+    pk, sc = tb.bitnet_ternarize_pack(torch.from_numpy(W).to(dev))
+    copies = [pk.clone() for _ in range(600)]
+    xd = torch.from_numpy(x).to(dev)
+    y = torch.empty((1, 1536), device=dev)
+    ws = torch.empty(tb.bitnet_matmul_workspace_bytes(1, 1536), dtype=torch.uint8, device=dev)
+    ms = timer.time(lambda i=0: tb.bitnet_ternary_matmul_into(1, 1536, 1536, xd, copies[i % 600],
+                                                              sc, y, ws), 600)
+    out["single_gemv_1536x1536_m1"] = {
+        "us_per_call": round(ms * 1e3, 2),
+        "weight_GBps": round(1536 * 1536 / 4 / (ms * 1e-3) / 1e9, 1),
+        "note": "one 590 KB matrix per launch: launch and latency bound"}
+    del copies
+
+    # One decoder layer (7 projections, M=1) per grouped launch; steps walk the 28
+    # layers so each launch reads fresh weights.
+    layers = len(problems) // 7
+    layer_plans = []
+    for l in range(layers):
+        probs = problems[7 * l:7 * l + 7]
+        plans, _, _ = decode_plans(1, probs, copies=(packed,))
+        layer_plans.append(plans[0])
+    ms = timer.time(lambda i=0: layer_plans[i % layers].run(), 4 * layers)
+    lb = sum(p.N * p.K // 4 for p in problems[:7])
+    out["one_layer_m1"] = {"us_per_layer": round(ms * 1e3, 2),
+                           "weight_GBps": round(lb / (ms * 1e-3) / 1e9, 1),
+                           "frac_of_hbm_peak": round(alg_bytes(1, problems[:7]) /
+                                                     (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    del layer_plans
+
+    # One token through the decoder with the data dependencies of a layer kept:
+    # per layer four grouped launches in order (q,k,v | o | gate,up | down), 112
+    # launches per token, captured once in a HIP graph and replayed.  Graph
+    # replays are checked bit-exact against the eager launches first.
+    chain, chain_ys = [], []
+    for l in range(layers):
+        for grp in ((0, 1, 2), (3,), (4, 5), (6,)):
+            probs = [problems[7 * l + j] for j in grp]
+            plans, _, ys_c = decode_plans(1, probs, copies=(packed,))
+            chain.append(plans[0])
+            chain_ys.extend(ys_c)
+
+    def run_chain(i=0):
+        for pl in chain:
+            pl.run()
+    run_chain()
+    torch.cuda.synchronize()
+    eager = [y.clone() for y in chain_ys]
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            run_chain()
+    torch.cuda.current_stream().wait_stream(cap)
+    replay_ok = True
+    for _ in range(3):
+        for y in chain_ys:
+            y.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        replay_ok &= all(torch.equal(a, b) for a, b in zip(chain_ys, eager))
+    ms = timer.time(lambda i=0: graph.replay(), 100)
+    ms_eager = timer.time(run_chain, 20)
+    out["decode_token_chain_m1"] = {
+        "us_per_token": round(ms * 1e3, 2), "launches": len(chain),
+        "weight_GBps": round(sum(p.N * p.K // 4 for p in problems) / (ms * 1e-3) / 1e9, 1),
+        "us_per_token_eager_launches": round(ms_eager * 1e3, 2),
+        "graph_replays_match_eager": bool(replay_ok),
+        "note": "28 layers x 4 dependent grouped launches (qkv, o, gate+up, down), HIP graph"}
+    del chain, chain_ys, eager, graph
+
+    pbytes = sum(p.N * p.K // 4 for p in problems)
+    for M in (4, 16):
+        plans, _, _ = decode_plans(M)
+        ms = timer.time(lambda i=0: plans[i % 2].run(), 100)
+        out[f"decode_sweep_m{M}"] = {
+            "us_per_step": round(ms * 1e3, 2), "weight_GBps": round(pbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(alg_bytes(M, problems) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        del plans
+
+    # Prefill: M=256 (30 s of audio + prompt) and M=1800 (4 min of audio) over
+    # the same 196 matrices.
+    for M in (synth.PREFILL_M_30S, synth.PREFILL_M_LONG):
+        out[f"prefill_m{M}"] = prefill_config(torch, tb, timer, problems, packed, w_scales, M, dev)
+
+    # Batched decode: M=32 and 64 on the 28 gate and 28 down matrices.
+    sub = [p for p in problems if p.proj in (4, 6)]
+    g = torch.Generator(device=dev)
+    for M in (32, 64):
+        g.manual_seed(40000 + M)
+        xs = [gpu_activations(torch, g, M, p.K, dev) for p in sub]
+        idx = [problems.index(p) for p in sub]
+        ys = [torch.empty((M, p.N), device=dev) for p in sub]
+        plans = [tb.GroupedPlan(M, xs, [c[i] for i in idx], [w_scales[i] for i in idx], ys,
+                                [p.N for p in sub], [p.K for p in sub]) for c in (packed, copy_b)]
+        ms = timer.time(lambda i=0: plans[i % 2].run(), 50)
+        sb = sum(p.N * p.K // 4 for p in sub)
+        ops = 2.0 * M * sum(p.N * p.K for p in sub)
+        out[f"batched_decode_m{M}"] = {
+            "us_per_step": round(ms * 1e3, 2), "weight_GBps": round(sb / (ms * 1e-3) / 1e9, 1),
+            "int8_TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
+            "frac_of_hbm_peak": round(alg_bytes(M, sub) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        del xs, ys, plans
+    return out
 
 
 if __name__ == "__main__":
