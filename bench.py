@@ -50,13 +50,17 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--layers", type=int, default=28)
     ap.add_argument("--only", choices=("all", "decode", "prefill", "copy"), default="all",
                     help="decode: headline only; prefill: one prefill step size (--prefill-m) "
                          "only; copy: 1 GiB copy probe used to calibrate the byte counters")
     ap.add_argument("--prefill-m", type=int, default=256)
+    ap.add_argument("--decode-m", type=int, default=1,
+                    help="rows of the headline decode sweep (1 unless profiling other sizes)")
+    ap.add_argument("--decode-subset", choices=("all", "gate_down"), default="all",
+                    help="matrices of the decode sweep (gate_down: the 28 gate + 28 down)")
     ap.add_argument("--no-configs", action="store_true", help="skip the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the timed CPU-oracle work")
@@ -187,14 +191,20 @@ def main():
         return
 
     # ---- headline: decode sweep, M = 1 ------------------------------------------
-    M = 1
-    xs_host = [synth.problem_activations(p, M) for p in problems]
-    plans, xs, ys = decode_plans(M, xs_host=xs_host)
+    M = args.decode_m
+    if args.decode_subset == "gate_down":
+        sweep = [p for p in problems if p.proj in (4, 6)]
+    else:
+        sweep = problems
+    xs_host = [synth.problem_activations(p, M) for p in sweep]
+    plans, xs, ys = decode_plans(M, probs=sweep, xs_host=xs_host)
+    packed_bytes = sum(p.N * p.K // 4 for p in sweep)
     steps = args.steps
-    log(f"[bench] decode sweep M=1: warmup {args.warmup}, timed {steps} steps")
+    log(f"[bench] decode sweep M={M} over {len(sweep)} matrices: warmup {args.warmup}, "
+        f"timed {steps} steps")
     ms_step = timer.time(lambda i=0: plans[i % 2].run(), steps, warmup=args.warmup)
     weight_gbps = packed_bytes / (ms_step * 1e-3) / 1e9
-    bytes_launch = alg_bytes(M, problems)
+    bytes_launch = alg_bytes(M, sweep)
     achieved = bytes_launch / (ms_step * 1e-3) / 1e9
     log(f"[bench] decode {ms_step * 1e3:.1f} us/step, weight {weight_gbps:.0f} GB/s, "
         f"all bytes {achieved:.0f} GB/s")
@@ -220,7 +230,7 @@ def main():
         plans[0].run()
         torch.cuda.synchronize()
         refs = []
-        for i, p in enumerate(problems):
+        for i, p in enumerate(sweep):
             W = synth.problem_weights(p)
             pk_ref, s_ref = oracle.ternarize_pack(W)      # offline step, not timed
             refs.append((pk_ref, s_ref))
@@ -229,7 +239,7 @@ def main():
             t_spent += time.perf_counter() - t0
             bytes_done += p.N * p.K // 4
             mats += 1
-            packed_equal += int(np.array_equal(packed[i].cpu().numpy(), pk_ref))
+            packed_equal += int(np.array_equal(packed[problems.index(p)].cpu().numpy(), pk_ref))
             y_gpu = ys[i].cpu().numpy()
             rel = np.abs(y_gpu - ref["y"]) / np.maximum(np.abs(ref["y"]), 1e-30)
             max_rel = max(max_rel, float(rel.max()))
@@ -238,7 +248,7 @@ def main():
         # The same oracle on one thread, over the first layer's 7 projections.
         oracle.set_num_threads(1)
         t1, b1 = 0.0, 0
-        for i, p in enumerate(problems[:min(7, mats)]):
+        for i, p in enumerate(sweep[:min(7, mats)]):
             t0 = time.perf_counter()
             oracle.ternary_matmul(xs_host[i], refs[i][0], refs[i][1], p.N)
             t1 += time.perf_counter() - t0
@@ -246,7 +256,8 @@ def main():
         oracle.set_num_threads(cores)
         cpu = {"value": round(bytes_done / t_spent / 1e9, 4), "unit": "GB/s", "cores": cores,
                "kind": "oracle",
-               "sample": f"first {mats} of {n_mat} decode projections (layers in order, M=1): "
+               "sample": f"first {mats} of {len(sweep)} decode projections (layers in order, "
+                         f"M={M}): "
                          f"per-row quantize, unpack, int32 add/sub contraction, dequantize; "
                          f"{t_spent:.1f} s of oracle time on {cores} threads; GPU-packed codes "
                          f"equal to the oracle's in {packed_equal}/{mats} matrices; GPU outputs "
@@ -269,10 +280,10 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": f"decode sweep: all {n_mat} ternary projections of a "
+        "config": {"workload": f"decode sweep: all {len(sweep)} ternary projections of a "
                                f"{args.layers}-layer decoder (q,k,v,o 1536->1536/256; gate,up "
-                               "1536->8960; down 8960->1536), M=1, one grouped launch per step",
-                   "M": 1, "matrices": n_mat, "packed_weight_bytes": packed_bytes,
+                               f"1536->8960; down 8960->1536), M={M}, one grouped launch per step",
+                   "M": M, "matrices": len(sweep), "packed_weight_bytes": packed_bytes,
                    "weight_copies_rotated": 2},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -246,7 +246,19 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
   for (int32_t i = 0; i < count; ++i) kmax = std::max(kmax, problems_host[i].K);
   if (gemv && gemv_fusable(M, kmax))
     return from_hip(launch_gemv_grouped(problems_dev, tab, ws, true, kmax, hs));
-  st = from_hip(launch_quant_grouped(problems_dev, tab, ws, hs));
+  QuantTable qt;
+  std::memset(&qt, 0, sizeof(qt));
+  qt.count = count;
+  qt.M = (int32_t)M;
+  uint64_t qtotal = 0;
+  for (int32_t s = 0; s < count; ++s) {
+    qtotal += (uint64_t)quant_grouped_blocks(M, problems_host[idx[s]].K);
+    if (qtotal >= ((uint64_t)1 << 31)) return BITNET_ERR_SHAPE;
+    qt.wg_end[s] = (uint32_t)qtotal;
+    qt.order[s] = tab.order[s];
+  }
+  std::memcpy(qt.ws_off, tab.ws_off, sizeof(qt.ws_off));
+  st = from_hip(launch_quant_grouped(problems_dev, qt, ws, hs));
   if (st != BITNET_OK) return st;
   if (gemv) return from_hip(launch_gemv_grouped(problems_dev, tab, ws, false, kmax, hs));
   return from_hip(launch_gemm_grouped(problems_dev, tab, ws, hs));

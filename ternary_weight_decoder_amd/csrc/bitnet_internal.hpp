@@ -37,6 +37,16 @@ struct GroupTable {
   uint32_t ws_off[kMaxGroup];    // workspace offset of each problem, in 256-byte units
 };
 
+// Per-launch table of a grouped quantization: workgroups [wg_end[s-1], wg_end[s])
+// quantize the rows of problem order[s].
+struct QuantTable {
+  int32_t count;
+  int32_t M;
+  uint32_t wg_end[kMaxGroup];
+  uint16_t order[kMaxGroup];
+  uint32_t ws_off[kMaxGroup];
+};
+
 // Dispatch slot of workgroup b in a grouped launch (binary search over the
 // block ranges; the index is uniform, so the table is read through the scalar
 // cache), the first workgroup of that slot and its problem index.
@@ -66,7 +76,8 @@ hipError_t launch_quant_rows(const float *x, int M, int K, int8_t *xq_nat, int8_
 hipError_t launch_permute_q8(const int8_t *xq, const float *x_scale_in, int M, int K,
                              int8_t *xq_perm, float *x_scale, int32_t *rowsum,
                              hipStream_t stream);
-hipError_t launch_quant_grouped(const bitnet_problem *problems, const GroupTable &tab,
+int64_t quant_grouped_blocks(int64_t M, int64_t K);
+hipError_t launch_quant_grouped(const bitnet_problem *problems, const QuantTable &tab,
                                 uint8_t *workspace, hipStream_t stream);
 
 // gemv.hip  (M <= 16)

@@ -8,13 +8,14 @@
 // That keeps the VALU work at the 2-bit unpack alone (7 ops per 16 codes per
 // lane), independent of M, where a dot4 formulation would add 4*M more.
 //
-// Work split: each wave owns T column tiles of 16*C columns and walks the full
-// K of each, so no cross-wave reduction is needed; the 4 waves of a workgroup
-// take interleaved tiles, which keeps their reads of one unit adjacent in
-// memory.  Lane (col = lane%16, h = lane/16) loads 8 bytes = packed dwords 2h,
-// 2h+1 of unit u for column col: a wave reads 512 contiguous bytes per unit and
-// 16-column block.  Field values u = code+1 enter the MFMA; the epilogue
-// subtracts the activation row sum.
+// Work split: each wave owns one tile of 64 columns and walks its full K, so no
+// cross-wave reduction is needed; the 4 waves of a workgroup take adjacent
+// tiles, which keeps their reads of one unit adjacent in memory.  Lane
+// (col = lane%16, h = lane/16) loads 8 bytes = packed dwords 2h, 2h+1 of unit
+// u for column col: a wave reads 512 contiguous bytes per unit and 16-column
+// block.  Field values u = code+1 enter the MFMA; the epilogue subtracts the
+// activation row sum.  (Splitting the long-K projections' units between waves
+// measured no faster: the launch is bound by the aggregate stream.)
 //
 // Weights are read with buffer loads kept D (tile, unit) items ahead in a
 // register ring that runs across tile boundaries.  Loads for columns past N or
@@ -115,11 +116,10 @@ __device__ __forceinline__ void quant_rows_to_lds(const GemvProblem &p, GemvShar
   __syncthreads();
 }
 
-// One workgroup: columns [n_base, n_base + kWaves * T * kWaveCols); wave w owns
-// tiles t = 0..T-1 starting at column n_base + (t * kWaves + w) * kWaveCols.
+// Workgroup blk of a problem: wave w owns columns [(4 blk + w) * 64, +64).
 template <bool FUSED>
-__device__ __forceinline__ void gemv_block(const GemvProblem &p, int n_base, int T,
-                                           GemvShared &sh, int8_t *xq_lds) {
+__device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, GemvShared &sh,
+                                           int8_t *lds) {
   constexpr int C = kGemvC;
   constexpr int D = kGemvDepth;
   const int lane = threadIdx.x & 63;
@@ -127,7 +127,6 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int n_base, int
   const int col = lane & 15;
   const int h = lane >> 4;
   const int units = p.K >> 7;
-  const int items = T * units;
 
   const uint32_t w_bytes = (uint32_t)((size_t)p.N * p.K / 4);
   const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(p.packed, w_bytes);
@@ -136,20 +135,17 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int n_base, int
   const uint32_t a_row = (uint32_t)(a_live ? col : 0) * p.K + 32 * h;
   const uint32_t a_bytes = (uint32_t)((size_t)p.M * p.K);
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(FUSED ? nullptr : p.xqp, FUSED ? 0 : a_bytes);
-  const int lane_col0 = n_base + wave * kWaveCols + col;   // column of block 0, tile 0
-  constexpr int kTileStride = kWaves * kWaveCols;          // column step between tiles
+  const int lane_col0 = (blk * kWaves + wave) * kWaveCols + col;   // column of block 0
 
-  // Load cursor (tile, unit) of the next item to fetch.
-  int lt = 0, lu = 0;
+  int lu = 0;   // next unit to fetch
   u32x2 wr[D][C];
   v4i ar0[D], ar1[D];
   auto load_item = [&](u32x2 *w, v4i &a0, v4i &a1) {
-    const bool live = lt < T;
-    const int ncol = lane_col0 + lt * kTileStride;
+    const bool live = lu < units;
     const uint32_t ub = (uint32_t)lu * ustride + 8 * h;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      const int n = ncol + 16 * c;
+      const int n = lane_col0 + 16 * c;
       const uint32_t off = (live && n < p.N) ? (uint32_t)n * kUnitBytes + ub : w_bytes;
       w[c] = __builtin_amdgcn_raw_buffer_load_b64(w_rsrc, off, 0, kWeightAux);
     }
@@ -158,18 +154,15 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int n_base, int
       a0 = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, ao, 0, 0);
       a1 = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, ao + 16, 0, 0);
     }
-    if (++lu == units) {
-      lu = 0;
-      ++lt;
-    }
+    ++lu;
   };
 #pragma unroll
   for (int j = 0; j < D; ++j) load_item(wr[j], ar0[j], ar1[j]);
 
-  if (FUSED) quant_rows_to_lds(p, sh, xq_lds, p.xq_out != nullptr && n_base == 0);
+  if (FUSED) quant_rows_to_lds(p, sh, lds, p.xq_out != nullptr && blk == 0);
 
+  // Dequantization inputs of accumulator element r of this lane (row 4h + r).
   const float ws = ld_global<float>(p.w_scale);
-  // Row of accumulator element r of this lane, and its dequantization inputs.
   int row_rs[4];
   float row_xs[4];
 #pragma unroll
@@ -183,16 +176,15 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int n_base, int
 #pragma unroll
   for (int c = 0; c < C; ++c) acc[c] = v4i{0, 0, 0, 0};
   const v4i zero4 = v4i{0, 0, 0, 0};
-  int ct = 0, cu = 0;   // compute cursor
 
-  for (int base = 0; base < items; base += D) {
+  for (int base = 0; base < units; base += D) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int i = base + j;
       v4i a0 = zero4, a1 = zero4;
       if (FUSED) {
-        if (a_live && i < items) {
-          const v4i *ap = reinterpret_cast<const v4i *>(xq_lds + a_row + (uint32_t)cu * kUnit);
+        if (a_live && i < units) {
+          const v4i *ap = reinterpret_cast<const v4i *>(lds + a_row + (uint32_t)i * kUnit);
           a0 = ap[0];
           a1 = ap[1];
         }
@@ -200,7 +192,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int n_base, int
         a0 = ar0[j];
         a1 = ar1[j];
       }
-      // Items past the range carry zero operands: their MFMAs add nothing.
+      // Items past the range carry zero codes: their MFMAs add nothing.
 #pragma unroll
       for (int c = 0; c < C; ++c) {
         acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, unpack_fields(wr[j][c].x), acc[c],
@@ -209,42 +201,37 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int n_base, int
                                                        0, 0, 0);
       }
       load_item(wr[j], ar0[j], ar1[j]);
-      if (i < items && ++cu == units) {
-        // Tile ct complete: element (row = 4h + r, column col) of each block.
-        const int ncol = lane_col0 + ct * kTileStride;
+    }
+  }
+
+  // Element (row = 4h + r, column col) of each 16-column block.
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-          const int n = ncol + 16 * c;
+  for (int c = 0; c < C; ++c) {
+    const int n = lane_col0 + 16 * c;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = 4 * h + r;
-            if (row < p.M && n < p.N) {
-              const int a = acc[c][r] - row_rs[r];
-              if (p.acc_out) st_global<int>(p.acc_out + (size_t)row * p.N + n, a);
-              st_global<float>(p.y + (size_t)row * p.N + n, dequant(a, ws, row_xs[r]));
-            }
-          }
-          acc[c] = zero4;
-        }
-        cu = 0;
-        ++ct;
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * h + r;
+      if (row < p.M && n < p.N) {
+        const int a = acc[c][r] - row_rs[r];
+        if (p.acc_out) st_global<int>(p.acc_out + (size_t)row * p.N + n, a);
+        st_global<float>(p.y + (size_t)row * p.N + n, dequant(a, ws, row_xs[r]));
       }
     }
   }
 }
 
 template <bool FUSED>
-__global__ void __launch_bounds__(kThreads) gemv_kernel(GemvProblem p, int T) {
+__global__ void __launch_bounds__(kThreads) gemv_kernel(GemvProblem p) {
   __shared__ GemvShared sh;
   extern __shared__ __attribute__((aligned(16))) int8_t xq_lds[];
-  gemv_block<FUSED>(p, blockIdx.x * kWaves * T * kWaveCols, T, sh, xq_lds);
+  gemv_block<FUSED>(p, blockIdx.x, sh, xq_lds);
 }
 
 // Grouped: dispatch slot s of the table owns workgroups [blk_end[s-1], blk_end[s]).
 template <bool FUSED>
 __global__ void __launch_bounds__(kThreads)
     gemv_grouped_kernel(const bitnet_problem *__restrict__ problems, GroupTable tab,
-                        const uint8_t *__restrict__ workspace, int T) {
+                        const uint8_t *__restrict__ workspace) {
   __shared__ GemvShared sh;
   extern __shared__ __attribute__((aligned(16))) int8_t xq_lds[];
   const uint32_t b = blockIdx.x;
@@ -275,19 +262,13 @@ __global__ void __launch_bounds__(kThreads)
   p.N = (int)pr.N;
   p.K = (int)pr.K;
   p.M = M;
-  gemv_block<FUSED>(p, (int)(b - first) * kWaves * T * kWaveCols, T, sh, xq_lds);
+  gemv_block<FUSED>(p, (int)(b - first), sh, xq_lds);
 }
 
 }  // namespace
 
-#ifndef BITNET_GEMV_T
-#define BITNET_GEMV_T 1
-#endif
-// Tiles per wave (a workgroup covers 4 * T * 16 * C columns).
-int gemv_tiles_per_wave() { return BITNET_GEMV_T; }
-
 int gemv_blocks(int64_t N) {
-  const int64_t cols = (int64_t)kWaves * gemv_tiles_per_wave() * kWaveCols;
+  const int64_t cols = (int64_t)kWaves * kWaveCols;
   return (int)((N + cols - 1) / cols);
 }
 
@@ -298,7 +279,7 @@ hipError_t launch_gemv(int M, int N, int K, const int8_t *xq_perm, const float *
                        float *y, int32_t *acc_out, hipStream_t stream) {
   GemvProblem p{packed, nullptr, xq_perm, x_scale, rowsum, w_scale, y, acc_out,
                 nullptr, nullptr, N, K, M};
-  gemv_kernel<false><<<gemv_blocks(N), kThreads, 0, stream>>>(p, gemv_tiles_per_wave());
+  gemv_kernel<false><<<gemv_blocks(N), kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -307,8 +288,7 @@ hipError_t launch_gemv_fused(int M, int N, int K, const float *x, const uint8_t 
                              float *x_scale_out, int32_t *acc_out, hipStream_t stream) {
   GemvProblem p{packed, x, nullptr, nullptr, nullptr, w_scale, y, acc_out,
                 xq_out, x_scale_out, N, K, M};
-  gemv_kernel<true><<<gemv_blocks(N), kThreads, (size_t)M * K, stream>>>(
-      p, gemv_tiles_per_wave());
+  gemv_kernel<true><<<gemv_blocks(N), kThreads, (size_t)M * K, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -316,12 +296,11 @@ hipError_t launch_gemv_grouped(const bitnet_problem *problems, const GroupTable 
                                const uint8_t *workspace, bool fused, int64_t kmax,
                                hipStream_t stream) {
   const unsigned blocks = tab.blk_end[tab.count - 1];
-  const int T = gemv_tiles_per_wave();
   if (fused)
     gemv_grouped_kernel<true><<<blocks, kThreads, (size_t)(tab.M * kmax), stream>>>(
-        problems, tab, workspace, T);
+        problems, tab, workspace);
   else
-    gemv_grouped_kernel<false><<<blocks, kThreads, 0, stream>>>(problems, tab, workspace, T);
+    gemv_grouped_kernel<false><<<blocks, kThreads, 0, stream>>>(problems, tab, workspace);
   return hipGetLastError();
 }
 

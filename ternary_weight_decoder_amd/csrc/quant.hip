@@ -1,13 +1,17 @@
 // Per-row int8 absmax activation quantization.
 //
 // s = fl32(127 / max|x|), xq = clamp(rint(fl32(x*s)), -127, 127); an all-zero
-// row gives s = 1 (and xq = 0).  The max is exact in any order, so a wave
-// reduces it freely.  One wave quantizes one row with wave-level reductions
-// only (four rows per workgroup, no barriers); rows of up to 2048 values stay
-// in registers between the absmax and the rounding pass, longer rows are read
-// twice.  Besides the natural-order int8 row the kernel can write the permuted
-// row used by the matmul kernels and the exact int32 row sum that removes the
-// +1 offset of the packed code fields.
+// row gives s = 1 (and xq = 0).  The max is exact in any order, so it is reduced
+// freely.  Every row is read from memory once, with all of its loads in flight
+// together, and kept in registers between the absmax and the rounding pass:
+//   - rows of up to 2048 values: one wave per row (four rows per workgroup),
+//     wave-level reductions only;
+//   - rows of up to 10240 values: one workgroup per row, reductions across its
+//     four waves through LDS;
+//   - longer rows: one workgroup per row, read twice.
+// Besides the natural-order int8 row the kernels can write the permuted row
+// used by the matmul kernels and the exact int32 row sum that removes the +1
+// offset of the packed code fields.
 #include "bitnet_device.hpp"
 #include "bitnet_internal.hpp"
 
@@ -16,7 +20,10 @@ namespace {
 
 constexpr int kQuantThreads = 256;
 constexpr int kRowsPerBlock = kQuantThreads / 64;
-constexpr int kRegVec = 8;   // f32x4 per lane kept in registers: K <= 64 * 4 * 8
+constexpr int kWaveVec = 8;                       // f32x4 per lane, wave per row
+constexpr int kBlockVec = 10;                     // f32x4 per thread, workgroup per row
+constexpr int kWaveMaxK = 64 * 4 * kWaveVec;      // 2048
+constexpr int kBlockMaxK = kQuantThreads * 4 * kBlockVec;   // 10240
 
 struct RowOut {
   int8_t *nat;        // natural order row, may be null
@@ -26,9 +33,16 @@ struct RowOut {
   int32_t *rowsum;    // may be null
 };
 
+struct QuantShared {
+  float red[kRowsPerBlock];
+  int ired[kRowsPerBlock];
+};
+
 __device__ __forceinline__ float absmax4(f32x4 v) {
   return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }
+
+__device__ __forceinline__ float scale_of(float a) { return (a == 0.0f) ? 1.0f : 127.0f / a; }
 
 // Quantize 4 values at input index 4*i; returns their sum and stores them.
 __device__ __forceinline__ int quant_store4(f32x4 v, float s, int i, const RowOut &o) {
@@ -40,78 +54,134 @@ __device__ __forceinline__ int quant_store4(f32x4 v, float s, int i, const RowOu
   return q0 + q1 + q2 + q3;
 }
 
-// One wave, one row of K fp32 values (K % 128 == 0).
+__device__ __forceinline__ void store_row_meta(const RowOut &o, float s, int sum) {
+  if (o.scale) st_global<float>(o.scale, s);
+  if (o.scale2) st_global<float>(o.scale2, s);
+  if (o.rowsum) st_global<int>(o.rowsum, sum);
+}
+
+// One wave, one row of K <= kWaveMaxK values (K % 128 == 0).
 __device__ __forceinline__ void quant_row_wave(const float *__restrict__ xr, int K,
                                                const RowOut &o) {
   const int lane = threadIdx.x & 63;
   const f32x4 *x4 = reinterpret_cast<const f32x4 *>(xr);
   const int n4 = K >> 2;
+  f32x4 v[kWaveVec];
   float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kWaveVec; ++j) {
+    const int i = lane + 64 * j;
+    v[j] = i < n4 ? ld_global<f32x4>(x4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int j = 0; j < kWaveVec; ++j) a = fmaxf(a, absmax4(v[j]));
+  const float s = scale_of(wave_max(a));
   int sum = 0;
-  float s;
-  if (n4 <= kRegVec * 64) {
-    f32x4 v[kRegVec];
 #pragma unroll
-    for (int j = 0; j < kRegVec; ++j) {
-      const int i = lane + 64 * j;
-      v[j] = i < n4 ? ld_global<f32x4>(x4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
-      a = fmaxf(a, absmax4(v[j]));
-    }
-    a = wave_max(a);
-    s = (a == 0.0f) ? 1.0f : 127.0f / a;
-#pragma unroll
-    for (int j = 0; j < kRegVec; ++j) {
-      const int i = lane + 64 * j;
-      if (i < n4) sum += quant_store4(v[j], s, i, o);
-    }
-  } else {
-    // Longer rows: two passes, each in chunks of kRegVec loads per lane so that
-    // several loads are in flight at once.
-    for (int c0 = 0; c0 < n4; c0 += kRegVec * 64) {
-      f32x4 v[kRegVec];
-#pragma unroll
-      for (int j = 0; j < kRegVec; ++j) {
-        const int i = c0 + lane + 64 * j;
-        v[j] = i < n4 ? ld_global<f32x4>(x4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int j = 0; j < kRegVec; ++j) a = fmaxf(a, absmax4(v[j]));
-    }
-    a = wave_max(a);
-    s = (a == 0.0f) ? 1.0f : 127.0f / a;
-    for (int c0 = 0; c0 < n4; c0 += kRegVec * 64) {
-      f32x4 v[kRegVec];
-#pragma unroll
-      for (int j = 0; j < kRegVec; ++j) {
-        const int i = c0 + lane + 64 * j;
-        v[j] = i < n4 ? ld_global<f32x4>(x4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int j = 0; j < kRegVec; ++j) {
-        const int i = c0 + lane + 64 * j;
-        if (i < n4) sum += quant_store4(v[j], s, i, o);
-      }
-    }
+  for (int j = 0; j < kWaveVec; ++j) {
+    const int i = lane + 64 * j;
+    if (i < n4) sum += quant_store4(v[j], s, i, o);
   }
   sum = wave_sum(sum);
-  if (lane == 0) {
-    if (o.scale) st_global<float>(o.scale, s);
-    if (o.scale2) st_global<float>(o.scale2, s);
-    if (o.rowsum) st_global<int>(o.rowsum, sum);
-  }
+  if (lane == 0) store_row_meta(o, s, sum);
 }
 
+__device__ __forceinline__ float block_max(float a, QuantShared &sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  a = wave_max(a);
+  if (lane == 0) sh.red[wave] = a;
+  __syncthreads();
+  return fmaxf(fmaxf(sh.red[0], sh.red[1]), fmaxf(sh.red[2], sh.red[3]));
+}
+
+__device__ __forceinline__ void block_finish(int sum, float s, const RowOut &o, QuantShared &sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  sum = wave_sum(sum);
+  if (lane == 0) sh.ired[wave] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) store_row_meta(o, s, sh.ired[0] + sh.ired[1] + sh.ired[2] + sh.ired[3]);
+}
+
+// One workgroup, one row of any K (K % 128 == 0).  Whole workgroup, uniform.
+__device__ __forceinline__ void quant_row_block(const float *__restrict__ xr, int K,
+                                                const RowOut &o, QuantShared &sh) {
+  const int tid = threadIdx.x;
+  const f32x4 *x4 = reinterpret_cast<const f32x4 *>(xr);
+  const int n4 = K >> 2;
+  int sum = 0;
+  if (K <= kBlockMaxK) {
+    f32x4 v[kBlockVec];
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kBlockVec; ++j) {
+      const int i = tid + kQuantThreads * j;
+      v[j] = i < n4 ? ld_global<f32x4>(x4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < kBlockVec; ++j) a = fmaxf(a, absmax4(v[j]));
+    const float s = scale_of(block_max(a, sh));
+#pragma unroll
+    for (int j = 0; j < kBlockVec; ++j) {
+      const int i = tid + kQuantThreads * j;
+      if (i < n4) sum += quant_store4(v[j], s, i, o);
+    }
+    block_finish(sum, s, o, sh);
+    return;
+  }
+  // Longer rows: two passes in chunks of kBlockVec loads per thread.
+  float a = 0.0f;
+  for (int c0 = 0; c0 < n4; c0 += kBlockVec * kQuantThreads) {
+    f32x4 v[kBlockVec];
+#pragma unroll
+    for (int j = 0; j < kBlockVec; ++j) {
+      const int i = c0 + tid + kQuantThreads * j;
+      v[j] = i < n4 ? ld_global<f32x4>(x4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < kBlockVec; ++j) a = fmaxf(a, absmax4(v[j]));
+  }
+  const float s = scale_of(block_max(a, sh));
+  for (int c0 = 0; c0 < n4; c0 += kBlockVec * kQuantThreads) {
+    f32x4 v[kBlockVec];
+#pragma unroll
+    for (int j = 0; j < kBlockVec; ++j) {
+      const int i = c0 + tid + kQuantThreads * j;
+      v[j] = i < n4 ? ld_global<f32x4>(x4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < kBlockVec; ++j) {
+      const int i = c0 + tid + kQuantThreads * j;
+      if (i < n4) sum += quant_store4(v[j], s, i, o);
+    }
+  }
+  block_finish(sum, s, o, sh);
+}
+
+__device__ __forceinline__ RowOut row_out(int8_t *xq_nat, int8_t *xq_perm, float *x_scale,
+                                          float *x_scale2, int32_t *rowsum, int row, int K) {
+  const size_t off = (size_t)row * K;
+  return RowOut{xq_nat ? xq_nat + off : nullptr, xq_perm ? xq_perm + off : nullptr,
+                x_scale ? x_scale + row : nullptr, x_scale2 ? x_scale2 + row : nullptr,
+                rowsum ? rowsum + row : nullptr};
+}
+
+// WAVE_ROWS: four rows per workgroup, one per wave; otherwise one row per workgroup.
+template <bool WAVE_ROWS>
 __global__ void __launch_bounds__(kQuantThreads)
     quant_rows_kernel(const float *__restrict__ x, int M, int K, int8_t *__restrict__ xq_nat,
                       int8_t *__restrict__ xq_perm, float *__restrict__ x_scale,
                       float *__restrict__ x_scale2, int32_t *__restrict__ rowsum) {
-  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= M) return;
-  const size_t off = (size_t)row * K;
-  RowOut o{xq_nat ? xq_nat + off : nullptr, xq_perm ? xq_perm + off : nullptr,
-           x_scale ? x_scale + row : nullptr, x_scale2 ? x_scale2 + row : nullptr,
-           rowsum ? rowsum + row : nullptr};
-  quant_row_wave(x + off, K, o);
+  if (WAVE_ROWS) {
+    const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= M) return;
+    quant_row_wave(x + (size_t)row * K, K,
+                   row_out(xq_nat, xq_perm, x_scale, x_scale2, rowsum, row, K));
+  } else {
+    __shared__ QuantShared sh;
+    const int row = blockIdx.x;
+    quant_row_block(x + (size_t)row * K, K,
+                    row_out(xq_nat, xq_perm, x_scale, x_scale2, rowsum, row, K), sh);
+  }
 }
 
 // Already-quantized rows: copy into the permuted order and form the row sums.
@@ -138,24 +208,38 @@ __global__ void __launch_bounds__(kQuantThreads)
   }
 }
 
-// Grouped: wave w of workgroup b quantizes flattened row 4b + w, i.e. row
-// (4b + w) % M of problem (4b + w) / M, into that problem's workspace.
+// Grouped: workgroups [wg_end[s-1], wg_end[s]) quantize the M rows of problem
+// order[s] into its workspace, four rows per workgroup when K <= kWaveMaxK and
+// one row per workgroup otherwise.
 __global__ void __launch_bounds__(kQuantThreads)
-    quant_grouped_kernel(const bitnet_problem *__restrict__ problems, GroupTable tab,
+    quant_grouped_kernel(const bitnet_problem *__restrict__ problems, QuantTable tab,
                          uint8_t *__restrict__ workspace) {
+  __shared__ QuantShared sh;
+  const uint32_t b = blockIdx.x;
+  int lo = 0, hi = tab.count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (b < tab.wg_end[mid]) hi = mid; else lo = mid + 1;
+  }
+  const uint32_t local = b - (lo ? tab.wg_end[lo - 1] : 0u);
+  const int p = tab.order[lo];
   const int M = tab.M;
-  const int flat = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (flat >= tab.count * M) return;
-  const int p = flat / M;
-  const int row = flat - p * M;
   const bitnet_problem pr = problems[p];
   const int K = (int)pr.K;
   const WsLayout L = ws_layout(M, K);
   uint8_t *ws = workspace + (size_t)tab.ws_off[p] * 256;
-  RowOut o{nullptr, reinterpret_cast<int8_t *>(ws + L.xq) + (size_t)row * K,
-           reinterpret_cast<float *>(ws + L.scale) + row, nullptr,
-           reinterpret_cast<int32_t *>(ws + L.rowsum) + row};
-  quant_row_wave(pr.x + (size_t)row * K, K, o);
+  int8_t *xq = reinterpret_cast<int8_t *>(ws + L.xq);
+  float *xs = reinterpret_cast<float *>(ws + L.scale);
+  int32_t *rs = reinterpret_cast<int32_t *>(ws + L.rowsum);
+  if (K <= kWaveMaxK) {
+    const int row = (int)local * kRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= M) return;
+    quant_row_wave(pr.x + (size_t)row * K, K, row_out(nullptr, xq, xs, nullptr, rs, row, K));
+  } else {
+    const int row = (int)local;
+    quant_row_block(pr.x + (size_t)row * K, K, row_out(nullptr, xq, xs, nullptr, rs, row, K),
+                    sh);
+  }
 }
 
 }  // namespace
@@ -163,9 +247,12 @@ __global__ void __launch_bounds__(kQuantThreads)
 hipError_t launch_quant_rows(const float *x, int M, int K, int8_t *xq_nat, int8_t *xq_perm,
                              float *x_scale, float *x_scale2, int32_t *rowsum,
                              hipStream_t stream) {
-  const int blocks = (M + kRowsPerBlock - 1) / kRowsPerBlock;
-  quant_rows_kernel<<<blocks, kQuantThreads, 0, stream>>>(x, M, K, xq_nat, xq_perm, x_scale,
-                                                          x_scale2, rowsum);
+  if (K <= kWaveMaxK)
+    quant_rows_kernel<true><<<(M + kRowsPerBlock - 1) / kRowsPerBlock, kQuantThreads, 0, stream>>>(
+        x, M, K, xq_nat, xq_perm, x_scale, x_scale2, rowsum);
+  else
+    quant_rows_kernel<false><<<M, kQuantThreads, 0, stream>>>(x, M, K, xq_nat, xq_perm, x_scale,
+                                                              x_scale2, rowsum);
   return hipGetLastError();
 }
 
@@ -178,11 +265,14 @@ hipError_t launch_permute_q8(const int8_t *xq, const float *x_scale_in, int M, i
   return hipGetLastError();
 }
 
-hipError_t launch_quant_grouped(const bitnet_problem *problems, const GroupTable &tab,
+int64_t quant_grouped_blocks(int64_t M, int64_t K) {
+  return K <= kWaveMaxK ? (M + kRowsPerBlock - 1) / kRowsPerBlock : M;
+}
+
+hipError_t launch_quant_grouped(const bitnet_problem *problems, const QuantTable &tab,
                                 uint8_t *workspace, hipStream_t stream) {
-  const int rows = tab.count * tab.M;
-  const int blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  quant_grouped_kernel<<<blocks, kQuantThreads, 0, stream>>>(problems, tab, workspace);
+  quant_grouped_kernel<<<tab.wg_end[tab.count - 1], kQuantThreads, 0, stream>>>(problems, tab,
+                                                                                 workspace);
   return hipGetLastError();
 }
 

@@ -148,7 +148,8 @@ def test_ternarize_golden_ties(tb):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,K", [(1, 1536), (4, 1536), (16, 8960), (17, 128), (256, 1536),
-                                 (1800, 1536), (3, 8960)])
+                                 (1800, 1536), (3, 8960), (5, 2048), (6, 2176), (2, 10240),
+                                 (3, 10368), (2, 24576)])
 def test_quant_act_parity(tb, M, K):
     import torch
     say(f"[quant_act] M={M} K={K}")
@@ -198,7 +199,7 @@ def test_quant_act_golden(tb):
 MATMUL_CASES = [(m, 200, 384) for m in range(1, 21)] + [
     (1, 1536, 1536), (1, 256, 1536), (1, 8960, 1536), (1, 1536, 8960), (4, 1536, 8960),
     (16, 1536, 8960), (16, 65, 128), (32, 300, 512), (64, 8960, 1536), (256, 1536, 1536),
-    (257, 520, 256), (1800, 300, 1536), (129, 257, 1280),
+    (257, 520, 256), (1800, 300, 1536), (129, 257, 1280), (20, 136, 10368), (40, 72, 2176),
 ]
 
 
