@@ -261,6 +261,7 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
   st = from_hip(launch_quant_grouped(problems_dev, qt, ws, hs));
   if (st != BITNET_OK) return st;
   if (gemv) return from_hip(launch_gemv_grouped(problems_dev, tab, ws, false, kmax, hs));
+  gemm_schedule(tab, problems_host);
   return from_hip(launch_gemm_grouped(problems_dev, tab, ws, hs));
 }
 

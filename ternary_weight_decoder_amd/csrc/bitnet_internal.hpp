@@ -10,6 +10,7 @@
 namespace bitnet {
 
 constexpr int kMaxGroup = BITNET_MAX_GROUP;
+constexpr int kXcds = 8;   // accelerator complex dies, each with its own L2
 
 // Workspace of one problem: permuted int8 activations [M][K], fp32 scales [M],
 // int32 row sums [M]; each region 256-byte aligned.
@@ -35,6 +36,11 @@ struct GroupTable {
   uint32_t blk_end[kMaxGroup];   // inclusive prefix sum of workgroups, in dispatch order
   uint16_t order[kMaxGroup];     // problem index of each dispatch slot
   uint32_t ws_off[kMaxGroup];    // workspace offset of each problem, in 256-byte units
+  // Prefill only.  spread == 0: the tiles (workgroups) are one list in slot
+  // order, cut into kXcds contiguous ranges of about equal work; XCD x runs
+  // [xcd_first[x], xcd_first[x + 1]).  spread != 0: workgroup b runs tile b.
+  int32_t spread;
+  uint32_t xcd_first[kXcds + 1];
 };
 
 // Per-launch table of a grouped quantization: workgroups [wg_end[s-1], wg_end[s])
@@ -104,6 +110,9 @@ hipError_t launch_gemm(int M, int N, int K, const int8_t *xq_perm, const float *
                        const int32_t *rowsum, const uint8_t *packed, const float *w_scale,
                        float *y, int32_t *acc_out, hipStream_t stream);
 int gemm_blocks(int64_t M, int64_t N);
+// Prefill launch schedule: reorders the slots (tab.order, tab.blk_end) and
+// fills tab.spread / tab.xcd_first.
+void gemm_schedule(GroupTable &tab, const bitnet_problem *problems_host);
 hipError_t launch_gemm_grouped(const bitnet_problem *problems, const GroupTable &tab,
                                const uint8_t *workspace, hipStream_t stream);
 

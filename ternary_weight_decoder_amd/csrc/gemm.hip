@@ -23,23 +23,33 @@
 // dword d = 4h + e of its column and the 16 permuted activations at 16*d of its
 // row, so the k positions of both operands agree by construction.
 //
-// Blocks are renumbered so that consecutive logical tiles (the row blocks of
-// one column tile first) stay on one XCD and share its L2.
+// A grouped launch gives each XCD a set of whole projections of about equal
+// work, and each projection's tiles are ordered in bands of row blocks, so the
+// data an XCD needs stays in its own L2 instead of every projection's
+// activations and codes being fetched by all eight.
+#include <algorithm>
+
 #include "bitnet_device.hpp"
 #include "bitnet_internal.hpp"
 
 namespace bitnet {
 namespace {
 
-constexpr int BM = 128;
+#ifndef BITNET_GEMM_BM
+#define BITNET_GEMM_BM 128
+#endif
+constexpr int BM = BITNET_GEMM_BM;     // rows of a tile, a multiple of 32
 constexpr int BN = 256;
 constexpr int WN = 64;                 // columns per wave
 constexpr int RB = BM / 32;            // 32-row MFMA blocks per wave
 constexpr int CB = WN / 32;            // 32-column MFMA blocks per wave
-constexpr int kStages = 3;             // LDS / register ring depth (units)
+#ifndef BITNET_GEMM_STAGES
+#define BITNET_GEMM_STAGES 3
+#endif
+constexpr int kStages = BITNET_GEMM_STAGES;   // LDS / register ring depth (units)
 constexpr int kStageBytes = BM * 128;  // one activation tile
+constexpr int kDma = BM / 32;          // 1 KB activation loads per wave and unit
 constexpr int kThreads = 256;
-constexpr int kXcds = 8;
 
 // Two workgroups per CU: the accumulators then live in arch VGPRs, leaving room
 // for a second wave per SIMD to cover the other's waits.
@@ -68,20 +78,48 @@ struct GemmShared {
   int rowsum[BM];
 };
 
-// Logical block index.  Blocks are dealt round-robin to the XCDs (block b to
-// XCD b % 8), so blocks b, b + 8, b + 16, ... share one L2.  Within each group
-// of 8 * mt consecutive blocks, renumber so that the mt row blocks of one column
-// tile are such a same-XCD sequence: they then read the tile's packed codes
-// through one L2.  The coarse order of the launch (and with it the balance of
-// long and short tiles across XCDs) is unchanged; a partial last group keeps
-// its order.
-__device__ __forceinline__ uint32_t xcd_logical(uint32_t b, uint32_t G, uint32_t mt) {
-  const uint32_t span = kXcds * mt;
-  const uint32_t base = b - b % span;
-  if (base + span > G) return b;
-  const uint32_t r = b - base;
-  return base + (r % kXcds) * mt + r / kXcds;
+// Tile order inside one projection: bands of kBand row blocks, column tiles
+// one after another inside a band, the band's row blocks consecutive.  The
+// tiles an XCD runs at one time then share a few activation row blocks and
+// code column tiles in its L2, and a band's activation rows stay there while
+// it sweeps the columns.
+// Cache policy of the output stores: non-temporal, so the output stream does
+// not evict the activation and code tiles that other workgroups still read.
+#ifndef BITNET_GEMM_STORE_AUX
+#define BITNET_GEMM_STORE_AUX 2
+#endif
+constexpr int kStoreAux = BITNET_GEMM_STORE_AUX;
+
+#ifndef BITNET_GEMM_FENCE
+#define BITNET_GEMM_FENCE 1
+#endif
+#ifndef BITNET_GEMM_BAND
+#define BITNET_GEMM_BAND 4
+#endif
+constexpr int kBand = BITNET_GEMM_BAND;
+
+__device__ __forceinline__ void band_tile(int t, int mt, int nt, int &rb, int &ct) {
+  const int band = t / (kBand * nt);
+  const int r0 = band * kBand;
+  const int rows = min(kBand, mt - r0);
+  const int tt = t - band * kBand * nt;
+  ct = tt / rows;
+  rb = r0 + tt % rows;
 }
+
+// Workgroups are dealt round-robin to the XCDs (block b to XCD b % 8), so
+// block b runs tile b / 8 of the range owned by XCD b % 8.  Each XCD then
+// works through its own projections (or, for a single projection, one compact
+// piece of it) instead of every projection being spread over all eight L2s.
+
+// Chunk swizzle of tile row r (16-byte chunks, 8 per 128-byte row).  An MFMA
+// operand read (ds_read_b128) serves 16 lanes per cycle: rows li = 0..15 of one
+// chunk column.  Pairs of rows share a 256-byte bank line, so rows 2i and 2i+1
+// fall in different halves and the 8 pairs need 8 different chunk positions.
+#ifndef BITNET_GEMM_SWZ_SHIFT
+#define BITNET_GEMM_SWZ_SHIFT 1
+#endif
+__device__ __forceinline__ int swz(int r) { return (r >> BITNET_GEMM_SWZ_SHIFT) & 7; }
 
 __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0, GemmShared &sh) {
   const int tid = threadIdx.x;
@@ -90,25 +128,26 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
   const int li = lane & 31, lh = lane >> 5;
   const int units = p.K >> 7;
 
-  // Activation DMA: wave w fills tile rows [32w, 32w + 32) with 4 loads of 1 KB;
-  // load j of the wave covers rows 32w + 8j .. +7, lane i lands at chunk
-  // position i % 8 of row 32w + 8j + i / 8 and so fetches chunk (i % 8) ^ (i / 8).
+  // Activation DMA: wave w fills tile rows [BM/4 w, BM/4 (w + 1)) with kDma
+  // loads of 1 KB; load j of the wave covers rows BM/4 w + 8j .. +7, lane i
+  // lands at chunk position i % 8 of row r = BM/4 w + 8j + i / 8 and so fetches
+  // chunk (i % 8) ^ swz(r).
   const uint32_t a_bytes = (uint32_t)((size_t)p.M * p.K);
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.xqp, a_bytes);
-  uint32_t dma_off[4];
+  uint32_t dma_off[kDma];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = m0 + 32 * wave + 8 * j + (lane >> 3);
-    const int chunk = (lane & 7) ^ (lane >> 3);
+  for (int j = 0; j < kDma; ++j) {
+    const int row = m0 + 8 * kDma * wave + 8 * j + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(8 * kDma * wave + 8 * j + (lane >> 3));
     dma_off[j] = row < p.M ? (uint32_t)row * p.K + 16 * chunk : a_bytes;
   }
   auto issue_dma = [&](int u, int stage) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kDma; ++j) {
       const uint32_t off = (u < units && dma_off[j] < a_bytes) ? dma_off[j] + (uint32_t)u * kUnit
                                                                : a_bytes;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          a_rsrc, (lds_ptr_t)(&sh.a[stage][(32 * wave + 8 * j) * 128]), 16, off, 0, 0, 0);
+          a_rsrc, (lds_ptr_t)(&sh.a[stage][(8 * kDma * wave + 8 * j) * 128]), 16, off, 0, 0, 0);
     }
   };
 
@@ -129,10 +168,10 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
           w_rsrc, u < units ? w_off[cb] + (uint32_t)u * ustride : w_bytes, 0, 0);
   };
 
-  // A operand reads: row 32rb + li, chunk 4lh + e at position (4lh + e) ^ (li % 8).
+  // A operand reads: row 32rb + li, chunk 4lh + e at position (4lh + e) ^ swz(li).
   uint32_t a_rd[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) a_rd[e] = li * 128 + (((4 * lh + e) ^ (li & 7)) * 16);
+  for (int e = 0; e < 4; ++e) a_rd[e] = li * 128 + (((4 * lh + e) ^ swz(li)) * 16);
 
   // Per-row dequantization factors and row sums of the tile.
   if (tid < BM) {
@@ -142,10 +181,11 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
   }
 
   v4i bq[kStages][CB];
-  load_b(0, bq[0]);
-  issue_dma(0, 0);
-  load_b(1, bq[1]);
-  issue_dma(1, 1);
+#pragma unroll
+  for (int u = 0; u < kStages - 1; ++u) {
+    load_b(u, bq[u]);
+    issue_dma(u, u);
+  }
   __syncthreads();
 
   // Accumulators start at -rowsum of their row, which removes the +1 offset of
@@ -168,16 +208,25 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
     for (int s = 0; s < kStages; ++s) {
       const int u = base + s;
       // This wave's loads of unit u are its oldest outstanding ones; those of
-      // unit u + 1 (4 activation loads + CB code loads) may stay in flight.
-      // After the barrier every wave's part of stage s is in LDS, and every
-      // wave has finished reading stage (s + 2) % 3 (its reads of unit u - 1
-      // completed before the MFMAs that consumed them), which the next loads
-      // overwrite.  A plain barrier: a memory fence here would drain the
-      // in-flight loads of unit u + 1 as well.
-      __builtin_amdgcn_s_waitcnt(vmcnt_wait(4 + CB));
+      // units u + 1 .. u + kStages - 2 (kDma activation loads + CB code loads
+      // each) may stay in flight.  After the barrier every wave's part of stage
+      // s is in LDS, and every wave has finished reading the stage of unit
+      // u - 1 (its reads completed before the MFMAs that consumed them), which
+      // the next loads overwrite.  A plain barrier: a memory fence here would
+      // drain the in-flight loads of the later units as well.
+      // Nothing is scheduled across this point: left free, the compiler pulls
+      // the next unit's code unpacking into this one, which then has to wait
+      // for that unit's loads.
+#if BITNET_GEMM_FENCE
+      __builtin_amdgcn_sched_barrier(0);
+#endif
+      __builtin_amdgcn_s_waitcnt(vmcnt_wait((kStages - 2) * (kDma + CB)));
       __builtin_amdgcn_s_barrier();
-      load_b(u + 2, bq[(s + 2) % kStages]);
-      issue_dma(u + 2, (s + 2) % kStages);
+      load_b(u + kStages - 1, bq[(s + kStages - 1) % kStages]);
+      issue_dma(u + kStages - 1, (s + kStages - 1) % kStages);
+#if BITNET_GEMM_FENCE
+      __builtin_amdgcn_sched_barrier(0);   // the loads go out before the MFMAs
+#endif
       // Operands of k-chunk e + 1 (LDS reads, code unpack) are fetched while
       // the MFMAs of chunk e run.
       const int8_t *a_stage = sh.a[s];
@@ -223,6 +272,10 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
     }
   }
 
+  // The last ring slots loaded zeros into LDS; let them land before the
+  // workgroup can end and its LDS be handed to another one.
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+
   // Epilogue through buffer stores: the lane's column offset is fixed and the
   // row offset is uniform, both in the vector offset (the range check covers
   // it): rows past M fall beyond the buffer and are dropped, columns past N are
@@ -251,7 +304,7 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
           const int a = acc[rb][cb][4 * g + k];
           const uint32_t off = col_off[cb] + row_off;
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, (float)a * f[k]), y_rsrc,
-                                                off, 0, 0);
+                                                off, 0, kStoreAux);
           if (p.acc_out) __builtin_amdgcn_raw_buffer_store_b32(a, c_rsrc, off, 0, 0);
         }
       }
@@ -262,17 +315,27 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
 __global__ void __launch_bounds__(kThreads) BITNET_GEMM_OCCUPANCY gemm_kernel(GemmProblem p) {
   __shared__ GemmShared sh;
   const int mt = (p.M + BM - 1) / BM;
-  const uint32_t L = xcd_logical(blockIdx.x, gridDim.x, mt);
-  gemm_block(p, (int)(L % mt) * BM, (int)(L / mt) * BN, sh);
+  const int nt = (p.N + BN - 1) / BN;
+  const uint32_t tiles = (uint32_t)(mt * nt);
+  const uint32_t x = blockIdx.x % kXcds;
+  const uint32_t t = x * tiles / kXcds + blockIdx.x / kXcds;
+  if (t >= (x + 1) * tiles / kXcds) return;
+  int rb, ct;
+  band_tile((int)t, mt, nt, rb, ct);
+  gemm_block(p, rb * BM, ct * BN, sh);
 }
 
 __global__ void __launch_bounds__(kThreads) BITNET_GEMM_OCCUPANCY
     gemm_grouped_kernel(const bitnet_problem *__restrict__ problems, GroupTable tab,
                         const uint8_t *__restrict__ workspace) {
   __shared__ GemmShared sh;
-  const uint32_t b = xcd_logical(blockIdx.x, gridDim.x, (tab.M + BM - 1) / BM);
-  const SlotInfo si = find_slot(tab, b);
-  const uint32_t first = si.first;
+  uint32_t g = blockIdx.x;
+  if (!tab.spread) {
+    const uint32_t x = blockIdx.x % kXcds;
+    g = tab.xcd_first[x] + blockIdx.x / kXcds;
+    if (g >= tab.xcd_first[x + 1]) return;
+  }
+  const SlotInfo si = find_slot(tab, g);
   const int pi = si.problem;
   const bitnet_problem pr = problems[pi];
   const int M = tab.M;
@@ -289,9 +352,9 @@ __global__ void __launch_bounds__(kThreads) BITNET_GEMM_OCCUPANCY
   p.M = M;
   p.N = (int)pr.N;
   p.K = (int)pr.K;
-  const int mt = (M + BM - 1) / BM;
-  const int local = (int)(b - first);
-  gemm_block(p, (local % mt) * BM, (local / mt) * BN, sh);
+  int rb, ct;
+  band_tile((int)(g - si.first), (M + BM - 1) / BM, (p.N + BN - 1) / BN, rb, ct);
+  gemm_block(p, rb * BM, ct * BN, sh);
 }
 
 }  // namespace
@@ -300,18 +363,79 @@ int gemm_blocks(int64_t M, int64_t N) {
   return (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
 }
 
+void gemm_schedule(GroupTable &tab, const bitnet_problem *problems_host) {
+  // Each XCD gets a set of whole projections of about equal work (a tile's
+  // work is its number of K units), assigned longest K first to the least
+  // loaded XCD, so every XCD holds its share of the long-K tiles and starts
+  // them first.  When the projections are too few for that to balance, the
+  // tiles are dealt to the XCDs round-robin instead.
+  const int count = tab.count;
+  int slot[kMaxGroup];
+  uint32_t tiles[kMaxGroup];
+  uint64_t work[kMaxGroup];
+  for (int s = 0; s < count; ++s) {
+    const int p = tab.order[s];
+    slot[s] = s;
+    tiles[s] = (uint32_t)gemm_blocks(tab.M, problems_host[p].N);
+    work[s] = (uint64_t)tiles[s] * (uint64_t)(problems_host[p].K / kUnit);
+  }
+  std::stable_sort(slot, slot + count, [&](int a, int b) {
+    const int64_t ka = problems_host[tab.order[a]].K, kb = problems_host[tab.order[b]].K;
+    return ka != kb ? ka > kb : work[a] > work[b];
+  });
+  uint64_t load[kXcds] = {0};
+  int bin[kMaxGroup];
+  uint64_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    int x = 0;
+    for (int y = 1; y < kXcds; ++y)
+      if (load[y] < load[x]) x = y;
+    bin[slot[i]] = x;
+    load[x] += work[slot[i]];
+    total += work[slot[i]];
+  }
+  const uint64_t most = *std::max_element(load, load + kXcds);
+  uint16_t order[kMaxGroup];
+  uint32_t end = 0;
+  int n = 0;
+  tab.spread = 10 * kXcds * most > 11 * total;   // over 10% above the mean
+  tab.xcd_first[0] = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    for (int i = 0; i < count; ++i) {
+      const int s = slot[i];
+      if (!tab.spread && bin[s] != x) continue;
+      if (tab.spread && x > 0) break;
+      order[n] = tab.order[s];
+      end += tiles[s];
+      tab.blk_end[n] = end;
+      ++n;
+    }
+    tab.xcd_first[x + 1] = end;
+  }
+  for (int i = 0; i < count; ++i) tab.order[i] = order[i];
+}
+
+static unsigned xcd_grid(const uint32_t *first) {
+  uint32_t most = 0;
+  for (int x = 0; x < kXcds; ++x) most = std::max(most, first[x + 1] - first[x]);
+  return most * kXcds;
+}
+
 hipError_t launch_gemm(int M, int N, int K, const int8_t *xq_perm, const float *x_scale,
                        const int32_t *rowsum, const uint8_t *packed, const float *w_scale,
                        float *y, int32_t *acc_out, hipStream_t stream) {
   GemmProblem p{packed, xq_perm, x_scale, rowsum, w_scale, y, acc_out, M, N, K};
-  gemm_kernel<<<gemm_blocks(M, N), kThreads, 0, stream>>>(p);
+  const uint32_t tiles = (uint32_t)gemm_blocks(M, N);
+  uint32_t first[kXcds + 1];
+  for (int x = 0; x <= kXcds; ++x) first[x] = (uint32_t)x * tiles / kXcds;
+  gemm_kernel<<<xcd_grid(first), kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_grouped(const bitnet_problem *problems, const GroupTable &tab,
                                const uint8_t *workspace, hipStream_t stream) {
-  const unsigned blocks = tab.blk_end[tab.count - 1];
-  gemm_grouped_kernel<<<blocks, kThreads, 0, stream>>>(problems, tab, workspace);
+  const unsigned grid = tab.spread ? tab.blk_end[tab.count - 1] : xcd_grid(tab.xcd_first);
+  gemm_grouped_kernel<<<grid, kThreads, 0, stream>>>(problems, tab, workspace);
   return hipGetLastError();
 }
 

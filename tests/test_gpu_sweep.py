@@ -1,0 +1,124 @@
+"""GPU parity at full size: all 196 projections of the 28-layer decoder, in the
+grouped launches the benchmark times, checked on sampled outputs.
+
+The weights are drawn once (seeded, on the host).  Every matrix is ternarized
+and packed twice, by the oracle and by the library, and the two packings must
+be bit-identical with identical scales.  The expected outputs use only the
+oracle's packing and the oracle's quantization of the sampled rows.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from ternary_weight_decoder_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 1e-6
+ROWS_PER_MATRIX = 4
+COLS_PER_MATRIX = 24
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def sweep():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ternary_weight_decoder_amd import binding as tb
+    tb.lib()
+    problems = synth.sweep_problems()
+    say(f"[sweep] ternarizing {len(problems)} matrices on the host and on the GPU")
+    ws = torch.empty(tb.bitnet_ternarize_workspace_bytes(synth.INTERMEDIATE), dtype=torch.uint8,
+                     device="cuda:0")
+    packs, packed_dev, scales_dev = [], [], []
+    for p in problems:
+        W = synth.problem_weights(p)
+        ref_packed, ref_scale = oracle.ternarize_pack(W)
+        pk = torch.empty(p.N * p.K // 4, dtype=torch.uint8, device="cuda:0")
+        sc = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda:0")
+        tb.bitnet_ternarize_pack_into(torch.from_numpy(W).to("cuda:0"), p.N, p.K, pk, sc, ws)
+        torch.cuda.synchronize()
+        assert sc.cpu().numpy()[0] == ref_scale, p.name
+        assert np.array_equal(pk.cpu().numpy(), ref_packed), p.name
+        packs.append((ref_packed, ref_scale))
+        packed_dev.append(pk)
+        scales_dev.append(sc)
+    return {"tb": tb, "problems": problems, "packs": packs, "packed": packed_dev,
+            "scales": scales_dev}
+
+
+def gpu_activations(M, K, seed):
+    """N(0,1) rows with 1% of the channels x20, drawn on the GPU (seeded)."""
+    import torch
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(seed)
+    x = torch.randn((M, K), generator=g, device="cuda:0")
+    cols = torch.randperm(K, generator=g, device="cuda:0")[:max(1, K // 100)]
+    x[:, cols] *= 20.0
+    return x
+
+
+def run_and_check(sweep, M, subset, host_x):
+    import torch
+    tb = sweep["tb"]
+    idx = [i for i, p in enumerate(sweep["problems"]) if subset(p)]
+    probs = [sweep["problems"][i] for i in idx]
+    if host_x:
+        xs = [torch.from_numpy(synth.problem_activations(p, M)).to("cuda:0") for p in probs]
+    else:
+        xs = [gpu_activations(M, p.K, 70000 + 7 * p.layer + p.proj) for p in probs]
+    ys = [torch.full((M, p.N), float("nan"), device="cuda:0") for p in probs]
+    plan = tb.GroupedPlan(M, xs, [sweep["packed"][i] for i in idx],
+                          [sweep["scales"][i] for i in idx], ys, [p.N for p in probs],
+                          [p.K for p in probs])
+    plan.run()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(M)
+    worst = 0.0
+    for j, (i, p) in enumerate(zip(idx, probs)):
+        rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, ROWS_PER_MATRIX)]))
+        cols = np.unique(np.concatenate([[0, p.N - 1], rng.integers(0, p.N, COLS_PER_MATRIX)]))
+        x_rows = xs[j][torch.from_numpy(rows).to("cuda:0")].cpu().numpy()
+        xq, xsc = oracle.quant_act(x_rows)
+        ms = np.repeat(np.arange(rows.size), cols.size).astype(np.int64)
+        ns = np.tile(cols, rows.size).astype(np.int64)
+        packed, w_scale = sweep["packs"][i]
+        _, yref = oracle.matmul_sampled(xq, xsc, packed, w_scale, p.N, ms, ns)
+        y = ys[j].cpu().numpy()[rows][:, cols].reshape(-1)
+        assert not np.isnan(ys[j].cpu().numpy()).any(), f"{p.name}: unwritten output"
+        zero = yref == 0
+        assert (y[zero] == 0).all(), p.name
+        rel = np.abs(y.astype(np.float64) - yref) / np.maximum(np.abs(yref.astype(np.float64)),
+                                                               1e-300)
+        if (~zero).any():
+            worst = max(worst, float(rel[~zero].max()))
+        assert worst <= REL_TOL, f"{p.name}: max relative error {worst:.3e}"
+    say(f"[sweep] M={M}: {len(probs)} matrices, max relative error {worst:.2e}")
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_decode_sweep_sampled(sweep, M):
+    """The 196-matrix decode sweep (one grouped launch) at M = 1, 4, 16."""
+    say(f"[sweep] decode M={M}")
+    run_and_check(sweep, M, lambda p: True, host_x=True)
+
+
+@pytest.mark.parametrize("M", [32, 64])
+def test_batched_decode_sampled(sweep, M):
+    """Batched decode on the 28 gate and 28 down projections."""
+    say(f"[sweep] batched decode M={M}")
+    run_and_check(sweep, M, lambda p: p.proj in (4, 6), host_x=False)
+
+
+@pytest.mark.parametrize("M", [256, 1800])
+def test_prefill_sweep_sampled(sweep, M):
+    """Prefill over all 196 projections in one grouped launch."""
+    say(f"[sweep] prefill M={M}")
+    run_and_check(sweep, M, lambda p: True, host_x=False)
