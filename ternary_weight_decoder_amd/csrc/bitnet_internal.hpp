@@ -88,9 +88,12 @@ hipError_t launch_quant_grouped(const bitnet_problem *problems, const QuantTable
 
 // gemv.hip  (M <= 16)
 constexpr int kGemvMaxM = 16;
-// Largest M*K whose int8 rows the decode kernel quantizes into LDS itself.
+// Largest M*K whose int8 rows the decode kernel quantizes into LDS itself
+// (one row of the longest projection).  Beyond it a separate quantization
+// launch and staged rows are faster: per-workgroup quantization of several
+// long rows costs more than it saves, and its LDS limits occupancy.
 #ifndef BITNET_GEMV_FUSED_MAX
-#define BITNET_GEMV_FUSED_MAX (36 * 1024)
+#define BITNET_GEMV_FUSED_MAX 8960
 #endif
 constexpr int64_t kGemvFusedLdsBytes = BITNET_GEMV_FUSED_MAX;
 hipError_t launch_gemv(int M, int N, int K, const int8_t *xq_perm, const float *x_scale,

@@ -26,7 +26,10 @@
 // Activation quantization is fused when the M x K int8 rows fit in LDS: every
 // workgroup quantizes the rows itself (absmax, scale, round, row sum) into LDS
 // in the permuted order, so one launch does the whole projection.  Otherwise a
-// separate quantization kernel writes the rows to the workspace first.
+// separate quantization kernel writes the rows to the workspace first, and the
+// workgroup streams them into LDS in chunks of kChunkUnits units (buffer_load
+// ... lds, double-buffered, one barrier per chunk), so its four waves share
+// one copy instead of each reading every row from L2.
 #include "bitnet_device.hpp"
 #include "bitnet_internal.hpp"
 
@@ -50,6 +53,14 @@ constexpr int kWeightAux = BITNET_GEMV_AUX;     // cache-policy bits of weight l
 constexpr int kWaveCols = 16 * kGemvC;          // columns of one wave tile
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+constexpr int kChunkUnits = 8;                   // units per staged activation chunk
+constexpr int kChunkBytes = kChunkUnits * kGemvMaxM * kUnit;   // 16 rows per unit
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// 16-byte chunk position of chunk c in staged row r: pairs of rows share a
+// 256-byte bank line, so the eight pairs use eight different positions and a
+// 16-lane operand read (rows 0..15, one chunk) is conflict-free.
+__device__ __forceinline__ int stage_pos(int c, int r) { return c ^ ((r >> 1) & 7); }
 
 struct GemvProblem {
   const uint8_t *packed;
@@ -117,6 +128,8 @@ __device__ __forceinline__ void quant_rows_to_lds(const GemvProblem &p, GemvShar
 }
 
 // Workgroup blk of a problem: wave w owns columns [(4 blk + w) * 64, +64).
+// FUSED: the rows are quantized into LDS here; otherwise they are staged into
+// LDS from the workspace chunk by chunk.
 template <bool FUSED>
 __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, GemvShared &sh,
                                            int8_t *lds) {
@@ -133,14 +146,35 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, GemvSh
   const uint32_t ustride = (uint32_t)p.N * kUnitBytes;
   const bool a_live = col < p.M;
   const uint32_t a_row = (uint32_t)(a_live ? col : 0) * p.K + 32 * h;
+  const int lane_col0 = (blk * kWaves + wave) * kWaveCols + col;   // column of block 0
+
+  // Staging: chunk k of the rows goes to LDS buffer k % 2; wave w copies units
+  // 2w and 2w + 1 of the chunk, 8 rows per 1 KB load: lane i takes row
+  // 8q + i / 8 of load q and lands at chunk position i % 8, so it fetches
+  // chunk stage_pos(i % 8, row) of that row.  Rows past M and units past K
+  // are aimed beyond the buffer and land as zeros.
   const uint32_t a_bytes = (uint32_t)((size_t)p.M * p.K);
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(FUSED ? nullptr : p.xqp, FUSED ? 0 : a_bytes);
-  const int lane_col0 = (blk * kWaves + wave) * kWaveCols + col;   // column of block 0
+  auto stage_chunk = [&](int k) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = 2 * wave + (q >> 1);             // unit within the chunk
+      const int row = 8 * (q & 1) + (lane >> 3);
+      const int u = k * kChunkUnits + j;
+      const int chunk = stage_pos(lane & 7, row);
+      const uint32_t off = (u < units && row < p.M)
+                               ? (uint32_t)row * p.K + (uint32_t)u * kUnit + 16 * chunk
+                               : a_bytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          a_rsrc,
+          (lds_ptr_t)(lds + (k & 1) * kChunkBytes + (j * kGemvMaxM + 8 * (q & 1)) * kUnit), 16,
+          off, 0, 0, 0);
+    }
+  };
 
   int lu = 0;   // next unit to fetch
   u32x2 wr[D][C];
-  v4i ar0[D], ar1[D];
-  auto load_item = [&](u32x2 *w, v4i &a0, v4i &a1) {
+  auto load_item = [&](u32x2 *w) {
     const bool live = lu < units;
     const uint32_t ub = (uint32_t)lu * ustride + 8 * h;
 #pragma unroll
@@ -149,15 +183,11 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, GemvSh
       const uint32_t off = (live && n < p.N) ? (uint32_t)n * kUnitBytes + ub : w_bytes;
       w[c] = __builtin_amdgcn_raw_buffer_load_b64(w_rsrc, off, 0, kWeightAux);
     }
-    if (!FUSED) {
-      const uint32_t ao = (live && a_live) ? a_row + (uint32_t)lu * kUnit : a_bytes;
-      a0 = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, ao, 0, 0);
-      a1 = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, ao + 16, 0, 0);
-    }
     ++lu;
   };
+  if (!FUSED) stage_chunk(0);
 #pragma unroll
-  for (int j = 0; j < D; ++j) load_item(wr[j], ar0[j], ar1[j]);
+  for (int j = 0; j < D; ++j) load_item(wr[j]);
 
   if (FUSED) quant_rows_to_lds(p, sh, lds, p.xq_out != nullptr && blk == 0);
 
@@ -176,21 +206,39 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, GemvSh
 #pragma unroll
   for (int c = 0; c < C; ++c) acc[c] = v4i{0, 0, 0, 0};
   const v4i zero4 = v4i{0, 0, 0, 0};
+  // Staged operand reads: row col of unit j, chunks 2h and 2h + 1.
+  const int s_row = col * kUnit;
+  const int s_c0 = stage_pos(2 * h, col) * 16, s_c1 = stage_pos(2 * h + 1, col) * 16;
 
   for (int base = 0; base < units; base += D) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int i = base + j;
+      if (!FUSED && i < units && i % kChunkUnits == 0) {
+        // Chunk i / 8 begins.  This wave's copy of it was issued before the
+        // code loads of the last kChunkUnits units (C each) or, for the first
+        // chunk, before those of the first D units; after the barrier every
+        // wave's part is in LDS and every wave is done with the other buffer,
+        // which the next chunk's copy overwrites.
+        if (i == 0)
+          __builtin_amdgcn_s_waitcnt(vmcnt_wait(D * C));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_wait(kChunkUnits * C));
+        __builtin_amdgcn_s_barrier();
+        stage_chunk(i / kChunkUnits + 1);
+      }
       v4i a0 = zero4, a1 = zero4;
-      if (FUSED) {
-        if (a_live && i < units) {
+      if (a_live && i < units) {
+        if (FUSED) {
           const v4i *ap = reinterpret_cast<const v4i *>(lds + a_row + (uint32_t)i * kUnit);
           a0 = ap[0];
           a1 = ap[1];
+        } else {
+          const int8_t *sp = lds + ((i / kChunkUnits) & 1) * kChunkBytes +
+                             (i % kChunkUnits) * kGemvMaxM * kUnit + s_row;
+          a0 = *reinterpret_cast<const v4i *>(sp + s_c0);
+          a1 = *reinterpret_cast<const v4i *>(sp + s_c1);
         }
-      } else {
-        a0 = ar0[j];
-        a1 = ar1[j];
       }
       // Items past the range carry zero codes: their MFMAs add nothing.
 #pragma unroll
@@ -200,9 +248,12 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, GemvSh
         acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, unpack_fields(wr[j][c].y), acc[c],
                                                        0, 0, 0);
       }
-      load_item(wr[j], ar0[j], ar1[j]);
+      load_item(wr[j]);
     }
   }
+  // The last chunk copy (units past K) must land before the workgroup's LDS
+  // can be handed on.
+  if (!FUSED) __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
 
   // Element (row = 4h + r, column col) of each 16-column block.
 #pragma unroll
@@ -279,7 +330,7 @@ hipError_t launch_gemv(int M, int N, int K, const int8_t *xq_perm, const float *
                        float *y, int32_t *acc_out, hipStream_t stream) {
   GemvProblem p{packed, nullptr, xq_perm, x_scale, rowsum, w_scale, y, acc_out,
                 nullptr, nullptr, N, K, M};
-  gemv_kernel<false><<<gemv_blocks(N), kThreads, 0, stream>>>(p);
+  gemv_kernel<false><<<gemv_blocks(N), kThreads, 2 * kChunkBytes, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -300,7 +351,8 @@ hipError_t launch_gemv_grouped(const bitnet_problem *problems, const GroupTable 
     gemv_grouped_kernel<true><<<blocks, kThreads, (size_t)(tab.M * kmax), stream>>>(
         problems, tab, workspace);
   else
-    gemv_grouped_kernel<false><<<blocks, kThreads, 0, stream>>>(problems, tab, workspace);
+    gemv_grouped_kernel<false><<<blocks, kThreads, 2 * kChunkBytes, stream>>>(problems, tab,
+                                                                              workspace);
   return hipGetLastError();
 }
 

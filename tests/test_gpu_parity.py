@@ -200,6 +200,8 @@ MATMUL_CASES = [(m, 200, 384) for m in range(1, 21)] + [
     (1, 1536, 1536), (1, 256, 1536), (1, 8960, 1536), (1, 1536, 8960), (4, 1536, 8960),
     (16, 1536, 8960), (16, 65, 128), (32, 300, 512), (64, 8960, 1536), (256, 1536, 1536),
     (257, 520, 256), (1800, 300, 1536), (129, 257, 1280), (20, 136, 10368), (40, 72, 2176),
+    # decode rows staged through LDS in 8-unit chunks: partial chunks, ragged N
+    (5, 200, 2048), (3, 72, 8960), (16, 300, 1280), (2, 520, 4608), (13, 1000, 768),
 ]
 
 
