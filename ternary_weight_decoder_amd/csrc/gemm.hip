@@ -35,29 +35,27 @@
 namespace bitnet {
 namespace {
 
-#ifndef BITNET_GEMM_BM
-#define BITNET_GEMM_BM 128
-#endif
-constexpr int BM = BITNET_GEMM_BM;     // rows of a tile, a multiple of 32
 constexpr int BN = 256;
 constexpr int WN = 64;                 // columns per wave
-constexpr int RB = BM / 32;            // 32-row MFMA blocks per wave
 constexpr int CB = WN / 32;            // 32-column MFMA blocks per wave
 #ifndef BITNET_GEMM_STAGES
 #define BITNET_GEMM_STAGES 3
 #endif
 constexpr int kStages = BITNET_GEMM_STAGES;   // LDS / register ring depth (units)
-constexpr int kStageBytes = BM * 128;  // one activation tile
-constexpr int kDma = BM / 32;          // 1 KB activation loads per wave and unit
 constexpr int kThreads = 256;
 
-// Two workgroups per CU: the accumulators then live in arch VGPRs, leaving room
-// for a second wave per SIMD to cover the other's waits.
-#ifndef BITNET_GEMM_WAVES_PER_EU
-#define BITNET_GEMM_WAVES_PER_EU 2
-#endif
-#define BITNET_GEMM_OCCUPANCY \
-  __attribute__((amdgpu_waves_per_eu(BITNET_GEMM_WAVES_PER_EU, BITNET_GEMM_WAVES_PER_EU)))
+// Tile heights: 128 rows for prefill, 64 or 32 rows for batched decode
+// (M <= 64), where a 128-row tile would mostly multiply padding.  Waves per
+// SIMD: with a 128-row tile two workgroups per CU keep the accumulators in arch
+// VGPRs and let each wave cover the other's waits; smaller tiles need fewer
+// registers and run more waves.
+template <int BM>
+struct TileCfg {
+  static constexpr int RB = BM / 32;             // 32-row MFMA blocks per wave
+  static constexpr int kStageBytes = BM * 128;   // one activation tile
+  static constexpr int kDma = BM / 32;           // 1 KB activation loads per wave and unit
+  static constexpr int kWavesPerEu = BM >= 128 ? 2 : BM >= 64 ? 4 : 5;
+};
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
@@ -72,8 +70,9 @@ struct GemmProblem {
   int M, N, K;
 };
 
+template <int BM>
 struct GemmShared {
-  __attribute__((aligned(16))) int8_t a[kStages][kStageBytes];
+  __attribute__((aligned(16))) int8_t a[kStages][TileCfg<BM>::kStageBytes];
   float factor[BM];   // w_scale / x_scale of each row of the tile
   int rowsum[BM];
 };
@@ -121,7 +120,11 @@ __device__ __forceinline__ void band_tile(int t, int mt, int nt, int &rb, int &c
 #endif
 __device__ __forceinline__ int swz(int r) { return (r >> BITNET_GEMM_SWZ_SHIFT) & 7; }
 
-__device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0, GemmShared &sh) {
+template <int BM>
+__device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
+                                           GemmShared<BM> &sh) {
+  constexpr int RB = TileCfg<BM>::RB;
+  constexpr int kDma = TileCfg<BM>::kDma;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -312,8 +315,11 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
   }
 }
 
-__global__ void __launch_bounds__(kThreads) BITNET_GEMM_OCCUPANCY gemm_kernel(GemmProblem p) {
-  __shared__ GemmShared sh;
+template <int BM>
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(TileCfg<BM>::kWavesPerEu, TileCfg<BM>::kWavesPerEu)))
+        gemm_kernel(GemmProblem p) {
+  __shared__ GemmShared<BM> sh;
   const int mt = (p.M + BM - 1) / BM;
   const int nt = (p.N + BN - 1) / BN;
   const uint32_t tiles = (uint32_t)(mt * nt);
@@ -322,13 +328,15 @@ __global__ void __launch_bounds__(kThreads) BITNET_GEMM_OCCUPANCY gemm_kernel(Ge
   if (t >= (x + 1) * tiles / kXcds) return;
   int rb, ct;
   band_tile((int)t, mt, nt, rb, ct);
-  gemm_block(p, rb * BM, ct * BN, sh);
+  gemm_block<BM>(p, rb * BM, ct * BN, sh);
 }
 
-__global__ void __launch_bounds__(kThreads) BITNET_GEMM_OCCUPANCY
-    gemm_grouped_kernel(const bitnet_problem *__restrict__ problems, GroupTable tab,
-                        const uint8_t *__restrict__ workspace) {
-  __shared__ GemmShared sh;
+template <int BM>
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(TileCfg<BM>::kWavesPerEu, TileCfg<BM>::kWavesPerEu)))
+        gemm_grouped_kernel(const bitnet_problem *__restrict__ problems, GroupTable tab,
+                            const uint8_t *__restrict__ workspace) {
+  __shared__ GemmShared<BM> sh;
   uint32_t g = blockIdx.x;
   if (!tab.spread) {
     const uint32_t x = blockIdx.x % kXcds;
@@ -354,13 +362,22 @@ __global__ void __launch_bounds__(kThreads) BITNET_GEMM_OCCUPANCY
   p.K = (int)pr.K;
   int rb, ct;
   band_tile((int)(g - si.first), (M + BM - 1) / BM, (p.N + BN - 1) / BN, rb, ct);
-  gemm_block(p, rb * BM, ct * BN, sh);
+  gemm_block<BM>(p, rb * BM, ct * BN, sh);
 }
 
 }  // namespace
 
+// Rows per tile for a launch of M rows.
+#ifndef BITNET_GEMM_BM32_MAXM
+#define BITNET_GEMM_BM32_MAXM 32
+#endif
+static int gemm_bm(int64_t M) {
+  return M <= BITNET_GEMM_BM32_MAXM ? 32 : M <= 64 ? 64 : 128;
+}
+
 int gemm_blocks(int64_t M, int64_t N) {
-  return (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
+  const int64_t bm = gemm_bm(M);
+  return (int)(((M + bm - 1) / bm) * ((N + BN - 1) / BN));
 }
 
 void gemm_schedule(GroupTable &tab, const bitnet_problem *problems_host) {
@@ -428,14 +445,24 @@ hipError_t launch_gemm(int M, int N, int K, const int8_t *xq_perm, const float *
   const uint32_t tiles = (uint32_t)gemm_blocks(M, N);
   uint32_t first[kXcds + 1];
   for (int x = 0; x <= kXcds; ++x) first[x] = (uint32_t)x * tiles / kXcds;
-  gemm_kernel<<<xcd_grid(first), kThreads, 0, stream>>>(p);
+  switch (gemm_bm(M)) {
+    case 32: gemm_kernel<32><<<xcd_grid(first), kThreads, 0, stream>>>(p); break;
+    case 64: gemm_kernel<64><<<xcd_grid(first), kThreads, 0, stream>>>(p); break;
+    default: gemm_kernel<128><<<xcd_grid(first), kThreads, 0, stream>>>(p); break;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_grouped(const bitnet_problem *problems, const GroupTable &tab,
                                const uint8_t *workspace, hipStream_t stream) {
   const unsigned grid = tab.spread ? tab.blk_end[tab.count - 1] : xcd_grid(tab.xcd_first);
-  gemm_grouped_kernel<<<grid, kThreads, 0, stream>>>(problems, tab, workspace);
+  switch (gemm_bm(tab.M)) {
+    case 32: gemm_grouped_kernel<32><<<grid, kThreads, 0, stream>>>(problems, tab, workspace); break;
+    case 64: gemm_grouped_kernel<64><<<grid, kThreads, 0, stream>>>(problems, tab, workspace); break;
+    default:
+      gemm_grouped_kernel<128><<<grid, kThreads, 0, stream>>>(problems, tab, workspace);
+      break;
+  }
   return hipGetLastError();
 }
 
