@@ -53,9 +53,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--layers", type=int, default=28)
-    ap.add_argument("--only", choices=("all", "decode", "prefill", "copy"), default="all",
+    ap.add_argument("--only", choices=("all", "decode", "prefill", "copy", "vendor"), default="all",
                     help="decode: headline only; prefill: one prefill step size (--prefill-m) "
-                         "only; copy: 1 GiB copy probe used to calibrate the byte counters")
+                         "only; copy: 1 GiB copy probe used to calibrate the byte counters; "
+                         "vendor: the vendor int8 GEMM (torch._int_mm) on the prefill shapes, "
+                         "a reference point for the int8 MFMA rate these shapes allow")
     ap.add_argument("--prefill-m", type=int, default=256)
     ap.add_argument("--decode-m", type=int, default=1,
                     help="rows of the headline decode sweep (1 unless profiling other sizes)")
@@ -120,6 +122,30 @@ def copy_probe(torch):
     print(json.dumps({"copy_probe_bytes": 4 * n, "launches": 5}), flush=True)
 
 
+def vendor_reference(torch):
+    """torch._int_mm (the vendor int8 GEMM library) on the prefill projection
+    shapes: int8 x int8 -> int32, no quantization, no dequantization."""
+    dev = "cuda:0"
+    out = []
+    for M, N, K in ((256, 8960, 1536), (256, 1536, 8960), (1800, 8960, 1536), (1800, 1536, 8960),
+                    (8192, 8192, 8192)):
+        a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev)
+        b = torch.randint(0, 3, (N, K), dtype=torch.int8, device=dev).t()   # column-major [K, N]
+        for _ in range(3):
+            torch._int_mm(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            torch._int_mm(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / 20 * 1e3
+        out.append({"M": M, "N": N, "K": K, "us": round(us, 1),
+                    "int8_TOPS": round(2.0 * M * N * K / us / 1e6, 1)})
+    print(json.dumps({"vendor_int8_gemm": out}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -134,6 +160,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.only == "copy":
         copy_probe(torch)
+        return
+    if args.only == "vendor":
+        vendor_reference(torch)
         return
     dev = torch.device("cuda:0")
     tb.lib()

@@ -232,20 +232,29 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
     return problems_host[a].K > problems_host[b].K;
   });
   const bool gemv = M <= kGemvMaxM;
-  uint64_t total = 0;
-  for (int32_t s = 0; s < count; ++s) {
-    const bitnet_problem &p = problems_host[idx[s]];
-    total += gemv ? (uint64_t)gemv_blocks(p.N) : (uint64_t)gemm_blocks(M, p.N);
-    if (total >= ((uint64_t)1 << 31)) return BITNET_ERR_SHAPE;
-    tab.blk_end[s] = (uint32_t)total;
-    tab.order[s] = (uint16_t)idx[s];
+  int64_t kmax = 0;
+  for (int32_t i = 0; i < count; ++i) kmax = std::max(kmax, problems_host[i].K);
+  const bool fused = gemv && gemv_fusable(M, kmax);
+  auto fill_blocks = [&](bool split) -> uint64_t {
+    uint64_t total = 0;
+    for (int32_t s = 0; s < count; ++s) {
+      const bitnet_problem &p = problems_host[idx[s]];
+      total += gemv ? (uint64_t)gemv_blocks(p.N, p.K, split) : (uint64_t)gemm_blocks(M, p.N);
+      tab.blk_end[s] = (uint32_t)std::min<uint64_t>(total, UINT32_MAX);
+      tab.order[s] = (uint16_t)idx[s];
+    }
+    return total;
+  };
+  uint64_t total = fill_blocks(false);
+  if (total >= ((uint64_t)1 << 31)) return BITNET_ERR_SHAPE;
+  // A single-row launch too small to fill the chip splits K across waves.
+  if (fused && total < (uint64_t)kGemvSplitBelow) {
+    tab.split = 1;
+    total = fill_blocks(true);
   }
   hipStream_t hs = as_stream(stream);
   uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
-  int64_t kmax = 0;
-  for (int32_t i = 0; i < count; ++i) kmax = std::max(kmax, problems_host[i].K);
-  if (gemv && gemv_fusable(M, kmax))
-    return from_hip(launch_gemv_grouped(problems_dev, tab, ws, true, kmax, hs));
+  if (fused) return from_hip(launch_gemv_grouped(problems_dev, tab, ws, true, kmax, hs));
   QuantTable qt;
   std::memset(&qt, 0, sizeof(qt));
   qt.count = count;

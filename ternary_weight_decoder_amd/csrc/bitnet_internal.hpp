@@ -33,6 +33,7 @@ __host__ __device__ inline WsLayout ws_layout(int64_t M, int64_t K) {
 struct GroupTable {
   int32_t count;
   int32_t M;
+  int32_t split;                 // decode only: K-split of single-row projections
   uint32_t blk_end[kMaxGroup];   // inclusive prefix sum of workgroups, in dispatch order
   uint16_t order[kMaxGroup];     // problem index of each dispatch slot
   uint32_t ws_off[kMaxGroup];    // workspace offset of each problem, in 256-byte units
@@ -102,7 +103,23 @@ hipError_t launch_gemv(int M, int N, int K, const int8_t *xq_perm, const float *
 hipError_t launch_gemv_fused(int M, int N, int K, const float *x, const uint8_t *packed,
                              const float *w_scale, float *y, int8_t *xq_out,
                              float *x_scale_out, int32_t *acc_out, hipStream_t stream);
-int gemv_blocks(int64_t N);
+// K-split of the single-row decode kernel in small launches: with fewer than
+// kGemvSplitBelow workgroups the chip is not filled, and a long-K projection's
+// waves are latency-bound chains, so the waves of a workgroup then share one
+// 64-column tile and split its K units (at least kGemvUnitsPerWave each).
+#ifndef BITNET_GEMV_SPLIT_BELOW
+#define BITNET_GEMV_SPLIT_BELOW 512
+#endif
+#ifndef BITNET_GEMV_UNITS_PER_WAVE
+#define BITNET_GEMV_UNITS_PER_WAVE 8
+#endif
+constexpr int kGemvSplitBelow = BITNET_GEMV_SPLIT_BELOW;
+__host__ __device__ inline int gemv_split(int units, bool split) {
+  if (!split) return 1;
+  const int s = units / BITNET_GEMV_UNITS_PER_WAVE;
+  return s >= 4 ? 4 : s >= 2 ? 2 : 1;
+}
+int gemv_blocks(int64_t N, int64_t K, bool split);
 bool gemv_fusable(int64_t M, int64_t K);
 hipError_t launch_gemv_grouped(const bitnet_problem *problems, const GroupTable &tab,
                                const uint8_t *workspace, bool fused, int64_t kmax,

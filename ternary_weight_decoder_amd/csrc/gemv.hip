@@ -10,12 +10,13 @@
 //
 // Work split: each wave owns one tile of 64 columns and walks its full K, so no
 // cross-wave reduction is needed; the 4 waves of a workgroup take adjacent
-// tiles, which keeps their reads of one unit adjacent in memory.  Lane
-// (col = lane%16, h = lane/16) loads 8 bytes = packed dwords 2h, 2h+1 of unit
-// u for column col: a wave reads 512 contiguous bytes per unit and 16-column
-// block.  Field values u = code+1 enter the MFMA; the epilogue subtracts the
-// activation row sum.  (Splitting the long-K projections' units between waves
-// measured no faster: the launch is bound by the aggregate stream.)
+// tiles, which keeps their reads of one unit adjacent in memory.  In launches
+// too small to fill the chip, the waves of a single-row workgroup instead share
+// one tile and split its K units (S = 2 or 4 ways); their int32 partial sums
+// are added through LDS.  Lane (col = lane%16, h = lane/16) loads 8 bytes =
+// packed dwords 2h, 2h+1 of unit u for column col: a wave reads 512 contiguous
+// bytes per unit and 16-column block.  Field values u = code+1 enter the MFMA;
+// the epilogue subtracts the activation row sum.
 //
 // Weights are read with buffer loads kept D (tile, unit) items ahead in a
 // register ring that runs across tile boundaries.  Loads for columns past N or
@@ -127,26 +128,35 @@ __device__ __forceinline__ void quant_rows_to_lds(const GemvProblem &p, GemvShar
   __syncthreads();
 }
 
-// Workgroup blk of a problem: wave w owns columns [(4 blk + w) * 64, +64).
-// FUSED: the rows are quantized into LDS here; otherwise they are staged into
-// LDS from the workspace chunk by chunk.
+// Workgroup blk of a problem: with S = 1, wave w owns columns
+// [(4 blk + w) * 64, +64) over all K units; with a K-split S (single-row fused
+// launches only), wave w owns the 64 columns of group g = w % (4/S) starting at
+// (blk * 4/S + g) * 64, over K units [q * units / S, (q + 1) * units / S) with
+// q = w / (4/S).  FUSED: the rows are quantized into LDS here; otherwise they
+// are staged into LDS from the workspace chunk by chunk.
 template <bool FUSED>
-__device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, GemvShared &sh,
-                                           int8_t *lds) {
+__device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, bool split,
+                                           GemvShared &sh, int8_t *lds) {
   constexpr int C = kGemvC;
   constexpr int D = kGemvDepth;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
   const int h = lane >> 4;
-  const int units = p.K >> 7;
+  const int total_units = p.K >> 7;
+  const int S = FUSED ? gemv_split(total_units, split) : 1;
+  const int G = kWaves / S;
+  const int cgrp = wave % G;
+  const int kq = wave / G;
+  const int u0 = kq * total_units / S;
+  const int units = (kq + 1) * total_units / S - u0;   // units of this wave
 
   const uint32_t w_bytes = (uint32_t)((size_t)p.N * p.K / 4);
   const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(p.packed, w_bytes);
   const uint32_t ustride = (uint32_t)p.N * kUnitBytes;
   const bool a_live = col < p.M;
   const uint32_t a_row = (uint32_t)(a_live ? col : 0) * p.K + 32 * h;
-  const int lane_col0 = (blk * kWaves + wave) * kWaveCols + col;   // column of block 0
+  const int lane_col0 = (blk * G + cgrp) * kWaveCols + col;   // column of block 0
 
   // Staging: chunk k of the rows goes to LDS buffer k % 2; wave w copies units
   // 2w and 2w + 1 of the chunk, 8 rows per 1 KB load: lane i takes row
@@ -172,11 +182,11 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, GemvSh
     }
   };
 
-  int lu = 0;   // next unit to fetch
+  int lu = 0;   // next unit to fetch, relative to u0
   u32x2 wr[D][C];
   auto load_item = [&](u32x2 *w) {
     const bool live = lu < units;
-    const uint32_t ub = (uint32_t)lu * ustride + 8 * h;
+    const uint32_t ub = (uint32_t)(u0 + lu) * ustride + 8 * h;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int n = lane_col0 + 16 * c;
@@ -230,7 +240,8 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, GemvSh
       v4i a0 = zero4, a1 = zero4;
       if (a_live && i < units) {
         if (FUSED) {
-          const v4i *ap = reinterpret_cast<const v4i *>(lds + a_row + (uint32_t)i * kUnit);
+          const v4i *ap =
+              reinterpret_cast<const v4i *>(lds + a_row + (uint32_t)(u0 + i) * kUnit);
           a0 = ap[0];
           a1 = ap[1];
         } else {
@@ -255,6 +266,23 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, GemvSh
   // can be handed on.
   if (!FUSED) __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
 
+  if (S > 1) {
+    // K-split partials: waves q > 0 park their accumulators in LDS (over the
+    // activation row, once every wave is done with it); wave q = 0 adds them.
+    v4i *part = reinterpret_cast<v4i *>(lds);
+    __syncthreads();
+    if (kq > 0) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) part[(((kq - 1) * G + cgrp) * C + c) * 64 + lane] = acc[c];
+    }
+    __syncthreads();
+    if (kq > 0) return;
+    for (int q = 1; q < S; ++q) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) acc[c] += part[(((q - 1) * G + cgrp) * C + c) * 64 + lane];
+    }
+  }
+
   // Element (row = 4h + r, column col) of each 16-column block.
 #pragma unroll
   for (int c = 0; c < C; ++c) {
@@ -272,10 +300,10 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, GemvSh
 }
 
 template <bool FUSED>
-__global__ void __launch_bounds__(kThreads) gemv_kernel(GemvProblem p) {
+__global__ void __launch_bounds__(kThreads) gemv_kernel(GemvProblem p, int split) {
   __shared__ GemvShared sh;
   extern __shared__ __attribute__((aligned(16))) int8_t xq_lds[];
-  gemv_block<FUSED>(p, blockIdx.x, sh, xq_lds);
+  gemv_block<FUSED>(p, blockIdx.x, split != 0, sh, xq_lds);
 }
 
 // Grouped: dispatch slot s of the table owns workgroups [blk_end[s-1], blk_end[s]).
@@ -313,24 +341,33 @@ __global__ void __launch_bounds__(kThreads)
   p.N = (int)pr.N;
   p.K = (int)pr.K;
   p.M = M;
-  gemv_block<FUSED>(p, (int)(b - first), sh, xq_lds);
+  gemv_block<FUSED>(p, (int)(b - first), tab.split != 0, sh, xq_lds);
 }
 
 }  // namespace
 
-int gemv_blocks(int64_t N) {
-  const int64_t cols = (int64_t)kWaves * kWaveCols;
+int gemv_blocks(int64_t N, int64_t K, bool split) {
+  const int64_t cols = (int64_t)(kWaves / gemv_split((int)(K >> 7), split)) * kWaveCols;
   return (int)((N + cols - 1) / cols);
 }
 
 bool gemv_fusable(int64_t M, int64_t K) { return M * K <= kGemvFusedLdsBytes; }
+
+// Dynamic LDS of a fused launch whose longest K is kmax: the quantized rows,
+// and the K-split partials, which reuse the same space afterwards.
+static size_t fused_lds_bytes(int64_t M, int64_t kmax, bool split) {
+  const int S = gemv_split((int)(kmax >> 7), split);
+  const size_t part = (size_t)(S - 1) * (kWaves / S) * kGemvC * 64 * sizeof(v4i);
+  const size_t rows = (size_t)(M * kmax);
+  return rows > part ? rows : part;
+}
 
 hipError_t launch_gemv(int M, int N, int K, const int8_t *xq_perm, const float *x_scale,
                        const int32_t *rowsum, const uint8_t *packed, const float *w_scale,
                        float *y, int32_t *acc_out, hipStream_t stream) {
   GemvProblem p{packed, nullptr, xq_perm, x_scale, rowsum, w_scale, y, acc_out,
                 nullptr, nullptr, N, K, M};
-  gemv_kernel<false><<<gemv_blocks(N), kThreads, 2 * kChunkBytes, stream>>>(p);
+  gemv_kernel<false><<<gemv_blocks(N, K, false), kThreads, 2 * kChunkBytes, stream>>>(p, 0);
   return hipGetLastError();
 }
 
@@ -339,7 +376,9 @@ hipError_t launch_gemv_fused(int M, int N, int K, const float *x, const uint8_t 
                              float *x_scale_out, int32_t *acc_out, hipStream_t stream) {
   GemvProblem p{packed, x, nullptr, nullptr, nullptr, w_scale, y, acc_out,
                 xq_out, x_scale_out, N, K, M};
-  gemv_kernel<true><<<gemv_blocks(N), kThreads, (size_t)M * K, stream>>>(p);
+  const bool split = gemv_blocks(N, K, false) < kGemvSplitBelow;
+  gemv_kernel<true><<<gemv_blocks(N, K, split), kThreads, fused_lds_bytes(M, K, split),
+                      stream>>>(p, split ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -348,8 +387,8 @@ hipError_t launch_gemv_grouped(const bitnet_problem *problems, const GroupTable 
                                hipStream_t stream) {
   const unsigned blocks = tab.blk_end[tab.count - 1];
   if (fused)
-    gemv_grouped_kernel<true><<<blocks, kThreads, (size_t)(tab.M * kmax), stream>>>(
-        problems, tab, workspace);
+    gemv_grouped_kernel<true><<<blocks, kThreads, fused_lds_bytes(tab.M, kmax, tab.split != 0),
+                                stream>>>(problems, tab, workspace);
   else
     gemv_grouped_kernel<false><<<blocks, kThreads, 2 * kChunkBytes, stream>>>(problems, tab,
                                                                               workspace);

@@ -202,6 +202,8 @@ MATMUL_CASES = [(m, 200, 384) for m in range(1, 21)] + [
     (257, 520, 256), (1800, 300, 1536), (129, 257, 1280), (20, 136, 10368), (40, 72, 2176),
     # decode rows staged through LDS in 8-unit chunks: partial chunks, ragged N
     (5, 200, 2048), (3, 72, 8960), (16, 300, 1280), (2, 520, 4608), (13, 1000, 768),
+    # single-row launches with K split 2 or 4 ways across the waves of a workgroup
+    (1, 300, 2048), (1, 130, 3072), (1, 72, 8960), (1, 1000, 4224),
 ]
 
 
