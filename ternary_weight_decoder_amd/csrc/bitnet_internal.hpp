@@ -111,7 +111,7 @@ hipError_t launch_gemv_fused(int M, int N, int K, const float *x, const uint8_t 
 #define BITNET_GEMV_SPLIT_BELOW 512
 #endif
 #ifndef BITNET_GEMV_UNITS_PER_WAVE
-#define BITNET_GEMV_UNITS_PER_WAVE 8
+#define BITNET_GEMV_UNITS_PER_WAVE 6
 #endif
 constexpr int kGemvSplitBelow = BITNET_GEMV_SPLIT_BELOW;
 __host__ __device__ inline int gemv_split(int units, bool split) {
