@@ -221,6 +221,26 @@ def test_matmul_parity(tb, M, N, K):
     assert_y_close(got["y"], ref["y"])
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 512, 256), (40, 768, 384), (20, 256, 1536),
+                                   (129, 520, 256), (5, 300, 2048), (1, 1536, 8960)])
+def test_matmul_y_only_parity(tb, M, N, K):
+    """Without the optional outputs (the form the grouped and benchmark calls
+    take): full 256-column prefill tiles use the transposed 16-byte stores."""
+    import torch
+    say(f"[matmul y only] M={M} N={N} K={K}")
+    W = synth.normal_weights(N, K, seed=3 * N + K)
+    x = synth.activations(M, K, seed=500 + M)
+    packed, s = oracle.ternarize_pack(W)
+    ref = oracle.ternary_matmul(x, packed, s, N)
+    ybuf, y = guarded(M * N, torch.float32, float("nan"))
+    ws = torch.empty(tb.bitnet_matmul_workspace_bytes(M, K), dtype=torch.uint8, device="cuda:0")
+    w_scale = torch.full((1,), float(s), dtype=torch.float32, device="cuda:0")
+    tb.bitnet_ternary_matmul_into(M, N, K, dev_tensor(x), dev_tensor(packed), w_scale, y, ws)
+    torch.cuda.synchronize()
+    check_canary(ybuf, M * N, float("nan"))
+    assert_y_close(y.cpu().numpy().reshape(M, N), ref["y"])
+
+
 @pytest.mark.parametrize("M", [1, 17])
 def test_matmul_worst_case_magnitude(tb, M):
     say(f"[matmul] worst-case magnitude M={M}")
