@@ -120,16 +120,20 @@ __device__ __forceinline__ void band_tile(int t, int mt, int nt, int &rb, int &c
 #endif
 __device__ __forceinline__ int swz(int r) { return (r >> BITNET_GEMM_SWZ_SHIFT) & 7; }
 
-template <int BM>
-__device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
-                                           GemmShared<BM> &sh) {
+// One output tile over K units [ub, ub + nunits).  SPLIT: the tile is one of
+// several K slices; its raw int32 sums (field values times activations, no
+// row-sum correction) are added atomically into the output buffer, which
+// holds int32 partial sums until the finishing pass.
+template <int BM, bool SPLIT>
+__device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0, int ub,
+                                           int nunits, GemmShared<BM> &sh) {
   constexpr int RB = TileCfg<BM>::RB;
   constexpr int kDma = TileCfg<BM>::kDma;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int li = lane & 31, lh = lane >> 5;
-  const int units = p.K >> 7;
+  const int units = nunits;
 
   // Activation DMA: wave w fills tile rows [BM/4 w, BM/4 (w + 1)) with kDma
   // loads of 1 KB; load j of the wave covers rows BM/4 w + 8j .. +7, lane i
@@ -142,7 +146,7 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
   for (int j = 0; j < kDma; ++j) {
     const int row = m0 + 8 * kDma * wave + 8 * j + (lane >> 3);
     const int chunk = (lane & 7) ^ swz(8 * kDma * wave + 8 * j + (lane >> 3));
-    dma_off[j] = row < p.M ? (uint32_t)row * p.K + 16 * chunk : a_bytes;
+    dma_off[j] = row < p.M ? (uint32_t)row * p.K + (uint32_t)ub * kUnit + 16 * chunk : a_bytes;
   }
   auto issue_dma = [&](int u, int stage) {
 #pragma unroll
@@ -162,7 +166,7 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int n = n0 + wave * WN + cb * 32 + li;
-    w_off[cb] = n < p.N ? (uint32_t)n * kUnitBytes + 16 * lh : w_bytes;
+    w_off[cb] = n < p.N ? (uint32_t)ub * ustride + (uint32_t)n * kUnitBytes + 16 * lh : w_bytes;
   }
   auto load_b = [&](int u, v4i *dst) {
 #pragma unroll
@@ -203,7 +207,7 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) acc[rb][cb][4 * g + k] = -rs[k];
+        for (int k = 0; k < 4; ++k) acc[rb][cb][4 * g + k] = SPLIT ? 0 : -rs[k];
     }
 
   for (int base = 0; base < units; base += kStages) {
@@ -286,6 +290,27 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
   // offset wraps.
   const uint32_t y_bytes = (uint32_t)((size_t)p.M * p.N * 4);
   const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(p.y, y_bytes);
+  if (SPLIT) {
+    uint32_t col_off[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int n = n0 + wave * WN + cb * 32 + li;
+      col_off[cb] = n < p.N ? (uint32_t)(4 * lh * p.N + n) * 4u : 0x80000000u;
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t row_off = (uint32_t)(m0 + rb * 32 + 8 * g + k) * (uint32_t)p.N * 4u;
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(acc[rb][cb][4 * g + k], y_rsrc,
+                                                           col_off[cb] + row_off, 0, 0);
+        }
+    return;
+  }
   const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(p.acc_out, p.acc_out ? y_bytes : 0);
   uint32_t col_off[CB];
 #pragma unroll
@@ -328,7 +353,46 @@ __global__ void __launch_bounds__(kThreads)
   if (t >= (x + 1) * tiles / kXcds) return;
   int rb, ct;
   band_tile((int)t, mt, nt, rb, ct);
-  gemm_block<BM>(p, rb * BM, ct * BN, sh);
+  gemm_block<BM, false>(p, rb * BM, ct * BN, 0, p.K >> 7, sh);
+}
+
+// K-split form for launches with few tiles: block b runs K slice b % S of tile
+// b / S (S consecutive blocks share a tile's rows and columns).
+template <int BM>
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(TileCfg<BM>::kWavesPerEu, TileCfg<BM>::kWavesPerEu)))
+        gemm_split_kernel(GemmProblem p, int S) {
+  __shared__ GemmShared<BM> sh;
+  const int mt = (p.M + BM - 1) / BM;
+  const int nt = (p.N + BN - 1) / BN;
+  const int t = (int)blockIdx.x / S;
+  const int q = (int)blockIdx.x % S;
+  const int units = p.K >> 7;
+  const int ub = q * units / S;
+  int rb, ct;
+  band_tile(t, mt, nt, rb, ct);
+  gemm_block<BM, true>(p, rb * BM, ct * BN, ub, (q + 1) * units / S - ub, sh);
+}
+
+// Zero the output before the K slices add into it (a fill kernel, so that the
+// sequence can be captured in a graph).
+__global__ void __launch_bounds__(256) zero_kernel(uint32_t *__restrict__ y, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) st_global<uint32_t>(y + i, 0u);
+}
+
+// Finish the K-split sums in place: y = (sum - rowsum) * w_scale / x_scale.
+__global__ void __launch_bounds__(256)
+    split_finish_kernel(float *__restrict__ y, int M, int N, const float *__restrict__ x_scale,
+                        const int32_t *__restrict__ rowsum, const float *__restrict__ w_scale,
+                        int32_t *__restrict__ acc_out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)M * N) return;
+  const int m = (int)(i / N);
+  const int a = ld_global<int>(y + i) - ld_global<int>(rowsum + m);
+  const float f = ld_global<float>(w_scale) / ld_global<float>(x_scale + m);
+  if (acc_out) st_global<int>(acc_out + i, a);
+  st_global<float>(y + i, (float)a * f);
 }
 
 template <int BM>
@@ -362,7 +426,7 @@ __global__ void __launch_bounds__(kThreads)
   p.K = (int)pr.K;
   int rb, ct;
   band_tile((int)(g - si.first), (M + BM - 1) / BM, (p.N + BN - 1) / BN, rb, ct);
-  gemm_block<BM>(p, rb * BM, ct * BN, sh);
+  gemm_block<BM, false>(p, rb * BM, ct * BN, 0, p.K >> 7, sh);
 }
 
 }  // namespace
@@ -438,11 +502,46 @@ static unsigned xcd_grid(const uint32_t *first) {
   return most * kXcds;
 }
 
+// A single projection with fewer tiles than this splits K across workgroups
+// (at least kSplitUnits units per slice, about kSplitTarget workgroups), as
+// long as M is small enough that the slices' atomic additions into the output
+// stay cheap next to the weight stream (measured: a win up to M = 256, a loss
+// at M = 1800).
+#ifndef BITNET_GEMM_SPLIT_BELOW
+#define BITNET_GEMM_SPLIT_BELOW 256
+#endif
+constexpr int kSplitBelow = BITNET_GEMM_SPLIT_BELOW;
+constexpr int kSplitTarget = 512;
+constexpr int kSplitUnits = 6;
+constexpr int kSplitMaxM = 512;
+
+static int gemm_split_factor(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = gemm_blocks(M, N);
+  if (tiles >= kSplitBelow || M > kSplitMaxM) return 1;
+  const int64_t by_units = (K / kUnit) / kSplitUnits;
+  const int64_t by_fill = (kSplitTarget + tiles - 1) / tiles;
+  const int64_t s = std::min(by_units, by_fill);
+  return s >= 2 ? (int)s : 1;
+}
+
 hipError_t launch_gemm(int M, int N, int K, const int8_t *xq_perm, const float *x_scale,
                        const int32_t *rowsum, const uint8_t *packed, const float *w_scale,
                        float *y, int32_t *acc_out, hipStream_t stream) {
   GemmProblem p{packed, xq_perm, x_scale, rowsum, w_scale, y, acc_out, M, N, K};
   const uint32_t tiles = (uint32_t)gemm_blocks(M, N);
+  const int S = gemm_split_factor(M, N, K);
+  if (S > 1) {
+    const int64_t n = (int64_t)M * N;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    zero_kernel<<<blocks, 256, 0, stream>>>(reinterpret_cast<uint32_t *>(y), n);
+    switch (gemm_bm(M)) {
+      case 32: gemm_split_kernel<32><<<tiles * S, kThreads, 0, stream>>>(p, S); break;
+      case 64: gemm_split_kernel<64><<<tiles * S, kThreads, 0, stream>>>(p, S); break;
+      default: gemm_split_kernel<128><<<tiles * S, kThreads, 0, stream>>>(p, S); break;
+    }
+    split_finish_kernel<<<blocks, 256, 0, stream>>>(y, M, N, x_scale, rowsum, w_scale, acc_out);
+    return hipGetLastError();
+  }
   uint32_t first[kXcds + 1];
   for (int x = 0; x <= kXcds; ++x) first[x] = (uint32_t)x * tiles / kXcds;
   switch (gemm_bm(M)) {
