@@ -24,8 +24,12 @@
  *   x_scale  = fl32(127 / max_k |x[m,k]|) per row; xq = clamp(rint(fl32(x*s)), -127, 127).
  *              An all-zero row gives xq = 0 and x_scale = 1.
  *   acc      = sum_k xq[m,k] * code[n,k]   (exact, int32; |acc| <= 127*K)
- *   y[m,n]   = acc * w_scale / x_scale[m]  (fp32; within 1e-6 relative of the
- *              exactly rounded value; acc == 0 gives exactly 0)
+ *   y[m,n]   = acc * w_scale / x_scale[m], rounded to fp32.  The reference
+ *              value is the product in fp64 (exact), divided in fp64 (correctly
+ *              rounded) and rounded once more to fp32.  Decode calls (M <= 16)
+ *              return exactly that value; prefill calls (M > 16) are within
+ *              1e-6 relative of it (one fp32 factor w_scale / x_scale per row).
+ *              acc == 0 gives exactly 0.
  *   NaN/Inf inputs and rows whose 127/absmax overflows are outside the contract.
  *
  * Packed layout (2 bits per code, N*K/4 bytes, K a multiple of 128):
@@ -179,6 +183,44 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
                                             int32_t count, const bitnet_problem *problems_host,
                                             void *workspace, size_t workspace_bytes,
                                             void *stream);
+
+/* ------------------------------------------------------------------------
+ * Dependent decode stages in one launch.  The decoder reads all of its
+ * weights for every token (blog "The Paper Says ARM Support...", section
+ * "What the model is trying to do"), and its projections depend on each
+ * other in order: q,k,v, then o, then gate,up, then down, layer after layer.
+ * This call runs such a sequence of stages: problems [stage_end[s-1],
+ * stage_end[s]) form stage s (stage_end[-1] = 0), the stages run in order,
+ * and everything a stage writes is visible to the stages after it, so a
+ * problem's x may be the y of an earlier stage.  Problems of one stage run
+ * concurrently and must not write what another problem of the stage reads.
+ *
+ * M             1..16, and M*K <= 8960 for every problem (rows quantized in
+ *               the same workgroup; one row of the longest projection).
+ * count         1..BITNET_MAX_GROUP problems in stage order; nstages
+ *               1..BITNET_MAX_STAGES; stage_end (host) strictly increasing,
+ *               stage_end[nstages-1] == count.
+ * problems_dev / problems_host as for the grouped call.
+ * workspace     bitnet_stages_workspace_bytes() bytes, 256-byte aligned, no
+ *               initial contents.  Word 1 (uint32) is nonzero after the call
+ *               completes if a wait between stages ran past its bound
+ *               (200 ms of the device's wall clock; once one wait has run
+ *               out the later ones return at once); the outputs are then not
+ *               valid.  The call never waits without bound.
+ * One cooperative launch (all workgroups resident at once), preceded by a
+ * two-word fill of the workspace.  Outputs are those of the single calls
+ * (decode: exactly rounded).  BITNET_ERR_HIP if the device cannot run the
+ * workgroups together.
+ * ------------------------------------------------------------------------ */
+#define BITNET_MAX_STAGES 256
+
+size_t bitnet_stages_workspace_bytes(void);
+
+bitnet_status bitnet_ternary_matmul_stages(int64_t M, const bitnet_problem *problems_dev,
+                                           int32_t count, const int32_t *stage_end,
+                                           int32_t nstages, const bitnet_problem *problems_host,
+                                           void *workspace, size_t workspace_bytes,
+                                           void *stream);
 
 #ifdef __cplusplus
 }

@@ -42,7 +42,8 @@ EXPORTS = (
     "bitnet_status_string", "bitnet_packed_bytes", "bitnet_ternarize_workspace_bytes",
     "bitnet_ternarize_pack", "bitnet_quant_act", "bitnet_matmul_workspace_bytes",
     "bitnet_ternary_matmul", "bitnet_ternary_matmul_q8", "bitnet_grouped_workspace_bytes",
-    "bitnet_ternary_matmul_grouped",
+    "bitnet_ternary_matmul_grouped", "bitnet_stages_workspace_bytes",
+    "bitnet_ternary_matmul_stages",
 )
 
 _lib = None
@@ -79,6 +80,10 @@ def lib():
         L.bitnet_grouped_workspace_bytes.restype = _sz
         L.bitnet_ternary_matmul_grouped.argtypes = [_i64, _p, _i32, _p, _p, _sz, _p]
         L.bitnet_ternary_matmul_grouped.restype = _i32
+        L.bitnet_stages_workspace_bytes.argtypes = []
+        L.bitnet_stages_workspace_bytes.restype = _sz
+        L.bitnet_ternary_matmul_stages.argtypes = [_i64, _p, _i32, _p, _i32, _p, _p, _sz, _p]
+        L.bitnet_ternary_matmul_stages.restype = _i32
         _lib = L
     return _lib
 
@@ -257,3 +262,55 @@ def bitnet_ternary_matmul_grouped(M, problems_dev, count, problems_host, workspa
                                                _c.byref(problems_host), _ptr(workspace),
                                                ws_bytes, _stream(stream)),
            "bitnet_ternary_matmul_grouped")
+
+
+def bitnet_stages_workspace_bytes() -> int:
+    return int(lib().bitnet_stages_workspace_bytes())
+
+
+def bitnet_ternary_matmul_stages(M, problems_dev, count, stage_end_host, nstages, problems_host,
+                                 workspace, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().bitnet_ternary_matmul_stages(M, _ptr(problems_dev), count,
+                                              _c.byref(stage_end_host), nstages,
+                                              _c.byref(problems_host), _ptr(workspace), ws_bytes,
+                                              _stream(stream)),
+           "bitnet_ternary_matmul_stages")
+
+
+class StagedPlan:
+    """A fixed sequence of dependent stages of single-row projections (for
+    example one decode token through a decoder: q,k,v | o | gate,up | down per
+    layer), run by one call.  stages: list of lists of
+    (x, packed, w_scale, y, N, K) tuples; a later stage's x may be an earlier
+    stage's y."""
+
+    def __init__(self, M: int, stages, device=None):
+        flat = [pr for st in stages for pr in st]
+        count = len(flat)
+        if not 1 <= count <= BITNET_MAX_GROUP:
+            raise ValueError(f"at most {BITNET_MAX_GROUP} problems")
+        self.M, self.count, self.nstages = int(M), count, len(stages)
+        arr = (bitnet_problem * count)()
+        for i, (x, pk, ws, y, N, K) in enumerate(flat):
+            arr[i] = bitnet_problem(x.data_ptr(), pk.data_ptr(), ws.data_ptr(), y.data_ptr(),
+                                    int(N), int(K))
+        ends = (_i32 * self.nstages)()
+        e = 0
+        for s, st in enumerate(stages):
+            e += len(st)
+            ends[s] = e
+        self._keep = flat
+        self.host, self.ends = arr, ends
+        dev = device if device is not None else flat[0][0].device
+        self.dev = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8).to(dev)
+        self.workspace = torch.empty(bitnet_stages_workspace_bytes(), dtype=torch.uint8,
+                                     device=dev)
+
+    def run(self, stream=None) -> None:
+        bitnet_ternary_matmul_stages(self.M, self.dev, self.count, self.ends, self.nstages,
+                                     self.host, self.workspace, stream)
+
+    def timed_out(self) -> bool:
+        """After the call has completed: did a wait between stages run out?"""
+        return int(self.workspace[4:8].view(torch.int32).item()) != 0

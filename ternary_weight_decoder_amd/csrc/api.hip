@@ -274,4 +274,52 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
   return from_hip(launch_gemm_grouped(problems_dev, tab, ws, hs));
 }
 
+size_t bitnet_stages_workspace_bytes(void) { return 256; }
+
+bitnet_status bitnet_ternary_matmul_stages(int64_t M, const bitnet_problem *problems_dev,
+                                           int32_t count, const int32_t *stage_end,
+                                           int32_t nstages, const bitnet_problem *problems_host,
+                                           void *workspace, size_t workspace_bytes,
+                                           void *stream) {
+  if (!problems_dev || !problems_host || !stage_end) return BITNET_ERR_NULL;
+  if (count < 1 || count > kMaxGroup || nstages < 1 || nstages > kMaxStages)
+    return BITNET_ERR_SHAPE;
+  if (M < 1 || M > kGemvMaxM) return BITNET_ERR_SHAPE;
+  if (!aligned(problems_dev, 8)) return BITNET_ERR_ALIGN;
+  int64_t kmax = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    bitnet_status st = check_problem(M, problems_host[i]);
+    if (st != BITNET_OK) return st;
+    if (!gemv_fusable(M, problems_host[i].K)) return BITNET_ERR_SHAPE;
+    kmax = std::max(kmax, problems_host[i].K);
+  }
+  int32_t prev = 0;
+  for (int32_t s = 0; s < nstages; ++s) {
+    if (stage_end[s] <= prev || stage_end[s] > count) return BITNET_ERR_SHAPE;
+    prev = stage_end[s];
+  }
+  if (prev != count) return BITNET_ERR_SHAPE;
+  if (!workspace || workspace_bytes < bitnet_stages_workspace_bytes()) return BITNET_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BITNET_ERR_ALIGN;
+  bitnet_status st = device_check();
+  if (st != BITNET_OK) return st;
+
+  StageTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  tab.count = count;
+  tab.nstages = nstages;
+  tab.M = (int32_t)M;
+  uint64_t total = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    total += (uint64_t)gemv_blocks(problems_host[i].N, problems_host[i].K, true);
+    if (total >= ((uint64_t)1 << 31)) return BITNET_ERR_SHAPE;
+    tab.blk_end[i] = (uint32_t)total;
+  }
+  tab.stage_tile[0] = 0;
+  for (int32_t s = 0; s < nstages; ++s) tab.stage_tile[s + 1] = tab.blk_end[stage_end[s] - 1];
+  return from_hip(launch_gemv_stages(problems_dev, tab, kmax,
+                                     reinterpret_cast<uint32_t *>(workspace),
+                                     as_stream(stream)));
+}
+
 }  // extern "C"

@@ -96,10 +96,14 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
          ((uint32_t)(d & 0xff) << 24);
 }
 
-// Dequantization epilogue: acc * w_scale / x_scale, two correctly rounded fp32
-// operations (|acc| < 2^24 converts exactly).
-__device__ __forceinline__ float dequant(int acc, float w_scale, float x_scale) {
-  return ((float)acc * w_scale) / x_scale;
+// Dequantization epilogue, exactly rounded: acc * w_scale is exact in fp64
+// (|acc| < 2^21 times a 24-bit significand), the fp64 division is correctly
+// rounded, and the result is rounded once more to fp32 -- the same operations
+// in the same order as the plain definition, so the value is reproduced bit for
+// bit.  Used where outputs are few (decode); the prefill epilogue uses one fp32
+// factor per row instead.
+__device__ __forceinline__ float dequant_exact(int acc, float w_scale, float x_scale) {
+  return (float)((double)acc * (double)w_scale / (double)x_scale);
 }
 
 }  // namespace bitnet

@@ -54,6 +54,18 @@ struct QuantTable {
   uint32_t ws_off[kMaxGroup];
 };
 
+// Per-launch table of a staged decode launch: problem i owns tiles
+// [blk_end[i-1], blk_end[i]) of one list in problem order; stage s runs tiles
+// [stage_tile[s], stage_tile[s + 1]).
+constexpr int kMaxStages = BITNET_MAX_STAGES;
+struct StageTable {
+  int32_t count;
+  int32_t nstages;
+  int32_t M;
+  uint32_t blk_end[kMaxGroup];
+  uint32_t stage_tile[kMaxStages + 1];
+};
+
 // Dispatch slot of workgroup b in a grouped launch (binary search over the
 // block ranges; the index is uniform, so the table is read through the scalar
 // cache), the first workgroup of that slot and its problem index.
@@ -124,6 +136,11 @@ bool gemv_fusable(int64_t M, int64_t K);
 hipError_t launch_gemv_grouped(const bitnet_problem *problems, const GroupTable &tab,
                                const uint8_t *workspace, bool fused, int64_t kmax,
                                hipStream_t stream);
+
+// Staged single-row decode: every stage's tiles, a device-wide barrier between
+// stages, one cooperative launch.  sync: 2 zeroed words (counter, timeout flag).
+hipError_t launch_gemv_stages(const bitnet_problem *problems, const StageTable &tab,
+                              int64_t kmax, uint32_t *sync, hipStream_t stream);
 
 // gemm.hip  (M > 16)
 hipError_t launch_gemm(int M, int N, int K, const int8_t *xq_perm, const float *x_scale,

@@ -31,6 +31,8 @@
 // workgroup streams them into LDS in chunks of kChunkUnits units (buffer_load
 // ... lds, double-buffered, one barrier per chunk), so its four waves share
 // one copy instead of each reading every row from L2.
+#include <algorithm>
+
 #include "bitnet_device.hpp"
 #include "bitnet_internal.hpp"
 
@@ -293,7 +295,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, bool s
       if (row < p.M && n < p.N) {
         const int a = acc[c][r] - row_rs[r];
         if (p.acc_out) st_global<int>(p.acc_out + (size_t)row * p.N + n, a);
-        st_global<float>(p.y + (size_t)row * p.N + n, dequant(a, ws, row_xs[r]));
+        st_global<float>(p.y + (size_t)row * p.N + n, dequant_exact(a, ws, row_xs[r]));
       }
     }
   }
@@ -344,6 +346,76 @@ __global__ void __launch_bounds__(kThreads)
   gemv_block<FUSED>(p, (int)(b - first), tab.split != 0, sh, xq_lds);
 }
 
+__global__ void zero_words_kernel(uint32_t *__restrict__ w, int n) {
+  if ((int)threadIdx.x < n) st_global<uint32_t>(w + threadIdx.x, 0u);
+}
+
+// Device-wide barrier between stages, for a cooperative (co-resident) grid.
+// Every thread first publishes its own stores at device scope (release); then
+// thread 0 of each workgroup counts the workgroup in and waits for the count
+// to reach `target`, and acquires.  The wait is bounded by `timeout` ticks of
+// the constant-rate wall clock: a wait that runs out raises the flag in
+// sync[1] instead of hanging, later waits return at once, and the results are
+// then not valid.
+__device__ __forceinline__ void grid_barrier(uint32_t *sync, uint32_t target, uint64_t timeout) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    atomicAdd(&sync[0], 1u);
+    if (__hip_atomic_load(&sync[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+      const uint64_t t0 = wall_clock64();
+      while (__hip_atomic_load(&sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        if (wall_clock64() - t0 > timeout) {
+          atomicOr(&sync[1], 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __threadfence();
+  }
+  __syncthreads();
+}
+
+// Staged single-row decode: workgroup b runs tiles b, b + G, ... of each stage
+// (G = grid size), then meets every other workgroup at the barrier, so a stage
+// may read the outputs of the stages before it.
+__global__ void __launch_bounds__(kThreads)
+    gemv_stages_kernel(const bitnet_problem *__restrict__ problems, StageTable tab,
+                       uint32_t *__restrict__ sync, uint64_t timeout) {
+  __shared__ GemvShared sh;
+  extern __shared__ __attribute__((aligned(16))) int8_t xq_lds[];
+  const uint32_t G = gridDim.x;
+  for (int s = 0; s < tab.nstages; ++s) {
+    for (uint32_t t = tab.stage_tile[s] + blockIdx.x; t < tab.stage_tile[s + 1]; t += G) {
+      int lo = 0, hi = tab.count - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (t < tab.blk_end[mid]) hi = mid; else lo = mid + 1;
+      }
+      const bitnet_problem pr = problems[lo];
+      GemvProblem p;
+      p.packed = pr.packed;
+      p.x = pr.x;
+      p.xqp = nullptr;
+      p.x_scale = nullptr;
+      p.rowsum = nullptr;
+      p.w_scale = pr.w_scale;
+      p.y = pr.y;
+      p.acc_out = nullptr;
+      p.xq_out = nullptr;
+      p.x_scale_out = nullptr;
+      p.N = (int)pr.N;
+      p.K = (int)pr.K;
+      p.M = tab.M;
+      // Every wave is done with the previous tile's LDS before this one starts.
+      __syncthreads();
+      gemv_block<true>(p, (int)(t - (lo ? tab.blk_end[lo - 1] : 0u)), true, sh, xq_lds);
+    }
+    if (s + 1 < tab.nstages) grid_barrier(sync, (uint32_t)(s + 1) * G, timeout);
+  }
+}
+
 }  // namespace
 
 int gemv_blocks(int64_t N, int64_t K, bool split) {
@@ -380,6 +452,36 @@ hipError_t launch_gemv_fused(int M, int N, int K, const float *x, const uint8_t 
   gemv_kernel<true><<<gemv_blocks(N, K, split), kThreads, fused_lds_bytes(M, K, split),
                       stream>>>(p, split ? 1 : 0);
   return hipGetLastError();
+}
+
+hipError_t launch_gemv_stages(const bitnet_problem *problems, const StageTable &tab,
+                              int64_t kmax, uint32_t *sync, hipStream_t stream) {
+  const size_t lds = fused_lds_bytes(tab.M, kmax, true);
+  int dev = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_stages_kernel, kThreads, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  // Enough workgroups for the largest stage, at most what can be co-resident.
+  uint32_t widest = 1;
+  for (int s = 0; s < tab.nstages; ++s)
+    widest = std::max(widest, tab.stage_tile[s + 1] - tab.stage_tile[s]);
+  const unsigned grid =
+      (unsigned)std::min<int64_t>((int64_t)per_cu * prop.multiProcessorCount, widest);
+  // Bound each wait between stages at 200 ms of the wall clock.
+  int clock_khz = 0;
+  e = hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, dev);
+  if (e != hipSuccess) return e;
+  uint64_t timeout = (uint64_t)std::max(clock_khz, 1) * 200u;
+  zero_words_kernel<<<1, 64, 0, stream>>>(sync, 2);
+  StageTable t = tab;
+  void *args[] = {(void *)&problems, (void *)&t, (void *)&sync, (void *)&timeout};
+  return hipLaunchCooperativeKernel((const void *)gemv_stages_kernel, dim3(grid), dim3(kThreads),
+                                    args, lds, stream);
 }
 
 hipError_t launch_gemv_grouped(const bitnet_problem *problems, const GroupTable &tab,

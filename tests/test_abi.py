@@ -131,3 +131,33 @@ def test_grouped_validation(L):
     assert g(1, A, 2, ref, A, 1 << 30, NULL) == ERR["NULL"]
     arr[1] = bitnet_problem(A, A, A, A, 256, 1536)
     assert g(1, A, 2, ref, A, 16, NULL) == ERR["WORKSPACE"]
+
+
+def test_stages_validation(L):
+    from ternary_weight_decoder_amd.binding import bitnet_problem
+    p, i64, sz, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int32
+    L.bitnet_ternary_matmul_stages.argtypes = [i64, p, i32, p, i32, p, p, sz, p]
+    L.bitnet_ternary_matmul_stages.restype = i32
+    L.bitnet_stages_workspace_bytes.restype = sz
+    assert L.bitnet_stages_workspace_bytes() >= 8
+    arr = (bitnet_problem * 3)()
+    arr[0] = bitnet_problem(A, A, A, A, 1536, 1536)
+    arr[1] = bitnet_problem(A, A, A, A, 256, 1536)
+    arr[2] = bitnet_problem(A, A, A, A, 1536, 8960)
+    ref = ctypes.cast(ctypes.byref(arr), ctypes.c_void_p)
+    ends = (i32 * 2)(2, 3)
+    eref = ctypes.cast(ctypes.byref(ends), ctypes.c_void_p)
+    g = L.bitnet_ternary_matmul_stages
+    assert g(1, NULL, 3, eref, 2, ref, A, 256, NULL) == ERR["NULL"]
+    assert g(1, A, 3, NULL, 2, ref, A, 256, NULL) == ERR["NULL"]
+    assert g(1, A, 0, eref, 2, ref, A, 256, NULL) == ERR["SHAPE"]
+    assert g(17, A, 3, eref, 2, ref, A, 256, NULL) == ERR["SHAPE"]      # M > 16
+    assert g(2, A, 3, eref, 2, ref, A, 256, NULL) == ERR["SHAPE"]       # 2 x 8960 > one row
+    bad = (i32 * 2)(2, 2)                                                  # not increasing
+    assert g(1, A, 3, ctypes.cast(ctypes.byref(bad), ctypes.c_void_p), 2, ref, A, 256,
+             NULL) == ERR["SHAPE"]
+    short = (i32 * 2)(1, 2)                                                # does not end at count
+    assert g(1, A, 3, ctypes.cast(ctypes.byref(short), ctypes.c_void_p), 2, ref, A, 256,
+             NULL) == ERR["SHAPE"]
+    assert g(1, A, 3, eref, 2, ref, A, 4, NULL) == ERR["WORKSPACE"]
+    assert g(1, A, 3, eref, 2, ref, A + 16, 256, NULL) == ERR["ALIGN"]

@@ -67,6 +67,16 @@ def assert_y_close(y, ref):
     assert worst <= REL_TOL, f"max relative error {worst:.3e}"
 
 
+def assert_y_matches(y, ref, M):
+    """Decode calls (M <= 16) reproduce the exactly rounded value bit for bit;
+    prefill calls are held to the relative tolerance."""
+    if M <= 16:
+        assert not np.isnan(y).any(), "unwritten output (NaN sentinel survived)"
+        np.testing.assert_array_equal(y.view(np.uint32), ref.astype(np.float32).view(np.uint32))
+    else:
+        assert_y_close(y, ref)
+
+
 def gpu_ternarize_pack(tb, W):
     import torch
     N, K = W.shape
@@ -218,7 +228,7 @@ def test_matmul_parity(tb, M, N, K):
     np.testing.assert_array_equal(got["xq"], ref["xq"])
     assert got["x_scale"].tobytes() == ref["x_scale"].tobytes()
     np.testing.assert_array_equal(got["acc"], ref["acc"])
-    assert_y_close(got["y"], ref["y"])
+    assert_y_matches(got["y"], ref["y"], M)
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 512, 256), (40, 768, 384), (20, 256, 1536),
@@ -238,7 +248,7 @@ def test_matmul_y_only_parity(tb, M, N, K):
     tb.bitnet_ternary_matmul_into(M, N, K, dev_tensor(x), dev_tensor(packed), w_scale, y, ws)
     torch.cuda.synchronize()
     check_canary(ybuf, M * N, float("nan"))
-    assert_y_close(y.cpu().numpy().reshape(M, N), ref["y"])
+    assert_y_matches(y.cpu().numpy().reshape(M, N), ref["y"], M)
 
 
 @pytest.mark.parametrize("M", [1, 17])
@@ -252,7 +262,7 @@ def test_matmul_worst_case_magnitude(tb, M):
     got = gpu_matmul(tb, x, packed, s, N, K)
     want = np.where(np.arange(N) % 2 == 0, 127 * K, -127 * K)
     np.testing.assert_array_equal(got["acc"], np.tile(want, (M, 1)))
-    assert_y_close(got["y"], oracle.ternary_matmul(x, packed, s, N)["y"])
+    assert_y_matches(got["y"], oracle.ternary_matmul(x, packed, s, N)["y"], M)
 
 
 @pytest.mark.parametrize("M", [5, 64])
@@ -269,7 +279,7 @@ def test_matmul_q8_parity(tb, M):
                                          return_acc=True)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
-    assert_y_close(y.cpu().numpy(), ref["y"])
+    assert_y_matches(y.cpu().numpy(), ref["y"], M)
 
 
 def test_zero_activation_row_and_zero_weights(tb):
@@ -343,4 +353,4 @@ def test_grouped_layer_parity(tb, M):
     torch.cuda.synchronize()
     for i, p in enumerate(problems):
         ref = oracle.ternary_matmul(xs[i], packs[i][0], packs[i][1], p.N)
-        assert_y_close(ys[i].cpu().numpy(), ref["y"])
+        assert_y_matches(ys[i].cpu().numpy(), ref["y"], M)

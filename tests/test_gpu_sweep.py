@@ -93,6 +93,9 @@ def run_and_check(sweep, M, subset, host_x):
         _, yref = oracle.matmul_sampled(xq, xsc, packed, w_scale, p.N, ms, ns)
         y = ys[j].cpu().numpy()[rows][:, cols].reshape(-1)
         assert not np.isnan(ys[j].cpu().numpy()).any(), f"{p.name}: unwritten output"
+        if M <= 16:
+            # decode: the exactly rounded value, bit for bit
+            np.testing.assert_array_equal(y.view(np.uint32), yref.view(np.uint32), p.name)
         zero = yref == 0
         assert (y[zero] == 0).all(), p.name
         rel = np.abs(y.astype(np.float64) - yref) / np.maximum(np.abs(yref.astype(np.float64)),
