@@ -430,6 +430,46 @@ def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, a
         "note": "28 layers x 4 dependent grouped launches (qkv, o, gate+up, down), HIP graph"}
     del chain, chain_ys, eager, graph
 
+    # The same token as one staged call: 112 stages in one cooperative launch,
+    # each stage reading what the one before it wrote (q,k,v read h; o reads
+    # y_q; gate and up read y_o; down reads y_up; the next layer's h is
+    # y_down).  Checked bit-exact against the same flow run as 112 grouped
+    # launches over the same buffers.
+    h = torch.from_numpy(synth.activations(1, synth.HIDDEN, seed=4242)).to(dev)
+    stages, flow_ys = [], []
+    for l in range(layers):
+        P = problems[7 * l:7 * l + 7]
+        yl = [torch.empty((1, p.N), dtype=torch.float32, device=dev) for p in P]
+
+        def pr(j, x, l=l, P=P, yl=yl):
+            return (x, packed[7 * l + j], w_scales[7 * l + j], yl[j], P[j].N, P[j].K)
+        stages += [[pr(0, h), pr(1, h), pr(2, h)], [pr(3, yl[0])], [pr(4, yl[3]), pr(5, yl[3])],
+                   [pr(6, yl[5])]]
+        flow_ys += yl
+        h = yl[6]
+    staged = tb.StagedPlan(1, stages)
+    launches = [tb.GroupedPlan(1, [t[0] for t in st], [t[1] for t in st], [t[2] for t in st],
+                               [t[3] for t in st], [t[4] for t in st], [t[5] for t in st])
+                for st in stages]
+    for pl in launches:
+        pl.run()
+    torch.cuda.synchronize()
+    ref = [y.clone() for y in flow_ys]
+    for y in flow_ys:
+        y.fill_(float("nan"))
+    staged.run()
+    torch.cuda.synchronize()
+    staged_ok = all(torch.equal(a, b) for a, b in zip(flow_ys, ref)) and not staged.timed_out()
+    ms = timer.time(lambda i=0: staged.run(), 100)
+    timed_out = staged.timed_out()
+    out["decode_token_staged_m1"] = {
+        "us_per_token": round(ms * 1e3, 2), "launches": 1, "stages": len(stages),
+        "weight_GBps": round(sum(p.N * p.K // 4 for p in problems) / (ms * 1e-3) / 1e9, 1),
+        "frac_of_hbm_peak": round(alg_bytes(1, problems) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "matches_grouped_launches": bool(staged_ok), "wait_timed_out": bool(timed_out),
+        "note": "one token, 28 layers x 4 dependent stages, one cooperative launch"}
+    del staged, launches, stages, flow_ys, ref
+
     pbytes = sum(p.N * p.K // 4 for p in problems)
     for M in (4, 16):
         plans, _, _ = decode_plans(M)

@@ -207,8 +207,10 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
  *               (200 ms of the device's wall clock; once one wait has run
  *               out the later ones return at once); the outputs are then not
  *               valid.  The call never waits without bound.
- * One cooperative launch (all workgroups resident at once), preceded by a
- * two-word fill of the workspace.  Outputs are those of the single calls
+ * One cooperative launch (all workgroups resident at once, at most 2048),
+ * preceded by a small fill kernel that clears the workspace's flags.  Between
+ * stages, outputs are written and read with device-coherent accesses and the
+ * workgroups meet at a flag barrier in the workspace.  Outputs are those of the single calls
  * (decode: exactly rounded).  BITNET_ERR_HIP if the device cannot run the
  * workgroups together.
  * ------------------------------------------------------------------------ */

@@ -274,7 +274,7 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
   return from_hip(launch_gemm_grouped(problems_dev, tab, ws, hs));
 }
 
-size_t bitnet_stages_workspace_bytes(void) { return 256; }
+size_t bitnet_stages_workspace_bytes(void) { return kStageWorkspaceBytes; }
 
 bitnet_status bitnet_ternary_matmul_stages(int64_t M, const bitnet_problem *problems_dev,
                                            int32_t count, const int32_t *stage_end,

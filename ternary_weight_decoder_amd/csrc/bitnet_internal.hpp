@@ -58,6 +58,12 @@ struct QuantTable {
 // [blk_end[i-1], blk_end[i]) of one list in problem order; stage s runs tiles
 // [stage_tile[s], stage_tile[s + 1]).
 constexpr int kMaxStages = BITNET_MAX_STAGES;
+// Workspace of a staged launch: words 0 (release) and 1 (timeout flag), then
+// one arrival flag per workgroup from word kStageFlag0; at most kMaxStageGrid
+// workgroups.
+constexpr int kStageFlag0 = 64;
+constexpr int kMaxStageGrid = 2048;
+constexpr size_t kStageWorkspaceBytes = (size_t)(kStageFlag0 + kMaxStageGrid) * 4;
 struct StageTable {
   int32_t count;
   int32_t nstages;

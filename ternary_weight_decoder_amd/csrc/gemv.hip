@@ -86,16 +86,31 @@ struct GemvShared {
   int rowsum[kGemvMaxM];
 };
 
+// Cache-policy bits of a device-coherent load (sc1): it reads what another
+// workgroup's device-scope stores wrote earlier in the same launch.
+constexpr int kCoherentAux = 16;
+
 // Quantize the M rows of x into LDS (permuted order) with the scales and row sums.
+// COHERENT: x was written earlier in the same launch (staged decode), so it is
+// read with device-coherent loads.
+template <bool COHERENT>
 __device__ __forceinline__ void quant_rows_to_lds(const GemvProblem &p, GemvShared &sh,
                                                   int8_t *xq_lds, bool write_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n4 = p.K >> 2;
+  const __amdgpu_buffer_rsrc_t x_rsrc =
+      make_rsrc(COHERENT ? p.x : nullptr, COHERENT ? (uint32_t)(p.M * p.K * 4) : 0u);
+  auto ld_x4 = [&](int m, int i) -> f32x4 {
+    if (COHERENT)
+      return __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, (uint32_t)(m * p.K + 4 * i) * 4, 0,
+                                                       kCoherentAux));
+    return ld_global<f32x4>(reinterpret_cast<const f32x4 *>(p.x + (size_t)m * p.K) + i);
+  };
   for (int m = 0; m < p.M; ++m) {
-    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(p.x + (size_t)m * p.K);
     float a = 0.0f;
     for (int i = tid; i < n4; i += kThreads) {
-      const f32x4 v = ld_global<f32x4>(x4 + i);
+      const f32x4 v = ld_x4(m, i);
       a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     }
     a = wave_max(a);
@@ -105,11 +120,10 @@ __device__ __forceinline__ void quant_rows_to_lds(const GemvProblem &p, GemvShar
   for (int m = 0; m < p.M; ++m) {
     const float a = fmaxf(fmaxf(sh.red[m][0], sh.red[m][1]), fmaxf(sh.red[m][2], sh.red[m][3]));
     const float s = (a == 0.0f) ? 1.0f : 127.0f / a;
-    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(p.x + (size_t)m * p.K);
     int8_t *dst = xq_lds + (size_t)m * p.K;
     int sum = 0;
     for (int i = tid; i < n4; i += kThreads) {
-      const f32x4 v = ld_global<f32x4>(x4 + i);
+      const f32x4 v = ld_x4(m, i);
       const int q0 = quant_one(v.x, s), q1 = quant_one(v.y, s);
       const int q2 = quant_one(v.z, s), q3 = quant_one(v.w, s);
       sum += q0 + q1 + q2 + q3;
@@ -135,10 +149,18 @@ __device__ __forceinline__ void quant_rows_to_lds(const GemvProblem &p, GemvShar
 // launches only), wave w owns the 64 columns of group g = w % (4/S) starting at
 // (blk * 4/S + g) * 64, over K units [q * units / S, (q + 1) * units / S) with
 // q = w / (4/S).  FUSED: the rows are quantized into LDS here; otherwise they
-// are staged into LDS from the workspace chunk by chunk.
-template <bool FUSED>
+// are staged into LDS from the workspace chunk by chunk.  `before_x` runs once
+// the first weight loads are in flight and before x is read (the staged decode
+// waits there for the previous stage); COHERENT reads x and writes y with
+// device-coherent accesses.
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
+template <bool FUSED, bool COHERENT = false, typename Hook = NoHook>
 __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, bool split,
-                                           GemvShared &sh, int8_t *lds) {
+                                           GemvShared &sh, int8_t *lds,
+                                           const Hook &before_x = Hook()) {
   constexpr int C = kGemvC;
   constexpr int D = kGemvDepth;
   const int lane = threadIdx.x & 63;
@@ -201,7 +223,8 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, bool s
 #pragma unroll
   for (int j = 0; j < D; ++j) load_item(wr[j]);
 
-  if (FUSED) quant_rows_to_lds(p, sh, lds, p.xq_out != nullptr && blk == 0);
+  before_x();
+  if (FUSED) quant_rows_to_lds<COHERENT>(p, sh, lds, p.xq_out != nullptr && blk == 0);
 
   // Dequantization inputs of accumulator element r of this lane (row 4h + r).
   const float ws = ld_global<float>(p.w_scale);
@@ -295,7 +318,12 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, bool s
       if (row < p.M && n < p.N) {
         const int a = acc[c][r] - row_rs[r];
         if (p.acc_out) st_global<int>(p.acc_out + (size_t)row * p.N + n, a);
-        st_global<float>(p.y + (size_t)row * p.N + n, dequant_exact(a, ws, row_xs[r]));
+        const float v = dequant_exact(a, ws, row_xs[r]);
+        if (COHERENT)
+          __hip_atomic_store((BITNET_GLOBAL float *)(p.y + (size_t)row * p.N + n), v,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          st_global<float>(p.y + (size_t)row * p.N + n, v);
       }
     }
   }
@@ -347,39 +375,68 @@ __global__ void __launch_bounds__(kThreads)
 }
 
 __global__ void zero_words_kernel(uint32_t *__restrict__ w, int n) {
-  if ((int)threadIdx.x < n) st_global<uint32_t>(w + threadIdx.x, 0u);
+  for (int i = threadIdx.x; i < n; i += blockDim.x) st_global<uint32_t>(w + i, 0u);
 }
 
-// Device-wide barrier between stages, for a cooperative (co-resident) grid.
-// Every thread first publishes its own stores at device scope (release); then
-// thread 0 of each workgroup counts the workgroup in and waits for the count
-// to reach `target`, and acquires.  The wait is bounded by `timeout` ticks of
-// the constant-rate wall clock: a wait that runs out raises the flag in
-// sync[1] instead of hanging, later waits return at once, and the results are
-// then not valid.
-__device__ __forceinline__ void grid_barrier(uint32_t *sync, uint32_t target, uint64_t timeout) {
-  __threadfence();
+// Stage handoff in the staged decode, for a cooperative (co-resident) grid.
+// Data crosses stages only through device-coherent accesses (y written with
+// device-scope stores, x read with sc1 loads), so no cache writeback or
+// invalidate is needed, only order: a workgroup arrives once its own stores
+// have completed (vmcnt 0 in every wave, then the workgroup barrier) by
+// storing the stage number into its flag; workgroup 0 waits for every flag
+// and then publishes the stage number in the release word, which the others
+// poll.  Waits are bounded by `timeout` ticks of the constant-rate wall clock:
+// a wait that runs out raises the flag in sync[1] instead of hanging, later
+// waits return at once, and the outputs are then not valid.
+// Workspace words: [0] release, [1] timeout flag, [kStageFlag0 + b] flag of
+// workgroup b.
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void stage_arrive(uint32_t *sync, uint32_t gen) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    atomicAdd(&sync[0], 1u);
-    if (__hip_atomic_load(&sync[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
-      const uint64_t t0 = wall_clock64();
-      while (__hip_atomic_load(&sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+  if (threadIdx.x == 0) st_agent(&sync[kStageFlag0 + blockIdx.x], gen);
+}
+
+__device__ __forceinline__ void stage_wait(uint32_t *sync, uint32_t gen, uint64_t timeout) {
+  if (blockIdx.x == 0) {
+    const bool skip = ld_agent(&sync[1]) != 0;
+    const uint64_t t0 = wall_clock64();
+    for (uint32_t i = threadIdx.x; i < gridDim.x && !skip; i += kThreads) {
+      while (ld_agent(&sync[kStageFlag0 + i]) < gen) {
         if (wall_clock64() - t0 > timeout) {
           atomicOr(&sync[1], 1u);
           break;
         }
-        __builtin_amdgcn_s_sleep(2);
       }
     }
-    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) st_agent(&sync[0], gen);
+  } else if (threadIdx.x == 0 && ld_agent(&sync[1]) == 0) {
+    const uint64_t t0 = wall_clock64();
+    while (ld_agent(&sync[0]) < gen) {
+      if (wall_clock64() - t0 > timeout) {
+        atomicOr(&sync[1], 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
   }
   __syncthreads();
 }
 
 // Staged single-row decode: workgroup b runs tiles b, b + G, ... of each stage
-// (G = grid size), then meets every other workgroup at the barrier, so a stage
-// may read the outputs of the stages before it.
+// (G = grid size).  Before stage s > 0 reads its activations it waits for
+// every workgroup to have arrived from stage s - 1; the wait sits after the
+// first weight loads of the workgroup's first tile of the stage are issued, so
+// that latency overlaps the handoff.
 __global__ void __launch_bounds__(kThreads)
     gemv_stages_kernel(const bitnet_problem *__restrict__ problems, StageTable tab,
                        uint32_t *__restrict__ sync, uint64_t timeout) {
@@ -387,6 +444,8 @@ __global__ void __launch_bounds__(kThreads)
   extern __shared__ __attribute__((aligned(16))) int8_t xq_lds[];
   const uint32_t G = gridDim.x;
   for (int s = 0; s < tab.nstages; ++s) {
+    const uint32_t gen = (uint32_t)s;    // stage s waits for arrivals from stage s - 1
+    bool waited = s == 0;
     for (uint32_t t = tab.stage_tile[s] + blockIdx.x; t < tab.stage_tile[s + 1]; t += G) {
       int lo = 0, hi = tab.count - 1;
       while (lo < hi) {
@@ -410,9 +469,15 @@ __global__ void __launch_bounds__(kThreads)
       p.M = tab.M;
       // Every wave is done with the previous tile's LDS before this one starts.
       __syncthreads();
-      gemv_block<true>(p, (int)(t - (lo ? tab.blk_end[lo - 1] : 0u)), true, sh, xq_lds);
+      const bool first = !waited;
+      gemv_block<true, true>(p, (int)(t - (lo ? tab.blk_end[lo - 1] : 0u)), true, sh, xq_lds,
+                             [&]() {
+                               if (first) stage_wait(sync, gen, timeout);
+                             });
+      waited = true;
     }
-    if (s + 1 < tab.nstages) grid_barrier(sync, (uint32_t)(s + 1) * G, timeout);
+    if (!waited) stage_wait(sync, gen, timeout);
+    if (s + 1 < tab.nstages) stage_arrive(sync, gen + 1);
   }
 }
 
@@ -470,14 +535,14 @@ hipError_t launch_gemv_stages(const bitnet_problem *problems, const StageTable &
   uint32_t widest = 1;
   for (int s = 0; s < tab.nstages; ++s)
     widest = std::max(widest, tab.stage_tile[s + 1] - tab.stage_tile[s]);
-  const unsigned grid =
-      (unsigned)std::min<int64_t>((int64_t)per_cu * prop.multiProcessorCount, widest);
+  const unsigned grid = (unsigned)std::min<int64_t>(
+      std::min<int64_t>((int64_t)per_cu * prop.multiProcessorCount, widest), kMaxStageGrid);
   // Bound each wait between stages at 200 ms of the wall clock.
   int clock_khz = 0;
   e = hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, dev);
   if (e != hipSuccess) return e;
   uint64_t timeout = (uint64_t)std::max(clock_khz, 1) * 200u;
-  zero_words_kernel<<<1, 64, 0, stream>>>(sync, 2);
+  zero_words_kernel<<<1, kThreads, 0, stream>>>(sync, kStageFlag0 + (int)grid);
   StageTable t = tab;
   void *args[] = {(void *)&problems, (void *)&t, (void *)&sync, (void *)&timeout};
   return hipLaunchCooperativeKernel((const void *)gemv_stages_kernel, dim3(grid), dim3(kThreads),

@@ -139,7 +139,8 @@ def test_stages_validation(L):
     L.bitnet_ternary_matmul_stages.argtypes = [i64, p, i32, p, i32, p, p, sz, p]
     L.bitnet_ternary_matmul_stages.restype = i32
     L.bitnet_stages_workspace_bytes.restype = sz
-    assert L.bitnet_stages_workspace_bytes() >= 8
+    # release word, timeout flag and one arrival flag per workgroup (up to 2048)
+    assert L.bitnet_stages_workspace_bytes() >= 8 + 4 * 2048
     arr = (bitnet_problem * 3)()
     arr[0] = bitnet_problem(A, A, A, A, 1536, 1536)
     arr[1] = bitnet_problem(A, A, A, A, 256, 1536)
@@ -159,5 +160,6 @@ def test_stages_validation(L):
     short = (i32 * 2)(1, 2)                                                # does not end at count
     assert g(1, A, 3, ctypes.cast(ctypes.byref(short), ctypes.c_void_p), 2, ref, A, 256,
              NULL) == ERR["SHAPE"]
-    assert g(1, A, 3, eref, 2, ref, A, 4, NULL) == ERR["WORKSPACE"]
-    assert g(1, A, 3, eref, 2, ref, A + 16, 256, NULL) == ERR["ALIGN"]
+    wsb = L.bitnet_stages_workspace_bytes()
+    assert g(1, A, 3, eref, 2, ref, A, wsb - 4, NULL) == ERR["WORKSPACE"]
+    assert g(1, A, 3, eref, 2, ref, A + 16, wsb, NULL) == ERR["ALIGN"]
