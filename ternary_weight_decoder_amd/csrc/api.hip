@@ -286,12 +286,10 @@ bitnet_status bitnet_ternary_matmul_stages(int64_t M, const bitnet_problem *prob
     return BITNET_ERR_SHAPE;
   if (M < 1 || M > kGemvMaxM) return BITNET_ERR_SHAPE;
   if (!aligned(problems_dev, 8)) return BITNET_ERR_ALIGN;
-  int64_t kmax = 0;
   for (int32_t i = 0; i < count; ++i) {
     bitnet_status st = check_problem(M, problems_host[i]);
     if (st != BITNET_OK) return st;
     if (!gemv_fusable(M, problems_host[i].K)) return BITNET_ERR_SHAPE;
-    kmax = std::max(kmax, problems_host[i].K);
   }
   int32_t prev = 0;
   for (int32_t s = 0; s < nstages; ++s) {
@@ -304,22 +302,9 @@ bitnet_status bitnet_ternary_matmul_stages(int64_t M, const bitnet_problem *prob
   bitnet_status st = device_check();
   if (st != BITNET_OK) return st;
 
-  StageTable tab;
-  std::memset(&tab, 0, sizeof(tab));
-  tab.count = count;
-  tab.nstages = nstages;
-  tab.M = (int32_t)M;
-  uint64_t total = 0;
-  for (int32_t i = 0; i < count; ++i) {
-    total += (uint64_t)gemv_blocks(problems_host[i].N, problems_host[i].K, true);
-    if (total >= ((uint64_t)1 << 31)) return BITNET_ERR_SHAPE;
-    tab.blk_end[i] = (uint32_t)total;
-  }
-  tab.stage_tile[0] = 0;
-  for (int32_t s = 0; s < nstages; ++s) tab.stage_tile[s + 1] = tab.blk_end[stage_end[s] - 1];
-  return from_hip(launch_gemv_stages(problems_dev, tab, kmax,
-                                     reinterpret_cast<uint32_t *>(workspace),
-                                     as_stream(stream)));
+  return from_hip(launch_stages(problems_dev, problems_host, count, stage_end, nstages,
+                                (int)M, reinterpret_cast<uint32_t *>(workspace),
+                                as_stream(stream)));
 }
 
 }  // extern "C"

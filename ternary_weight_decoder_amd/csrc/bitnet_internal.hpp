@@ -55,8 +55,9 @@ struct QuantTable {
 };
 
 // Per-launch table of a staged decode launch: problem i owns tiles
-// [blk_end[i-1], blk_end[i]) of one list in problem order; stage s runs tiles
-// [stage_tile[s], stage_tile[s + 1]).
+// [blk_end[i-1], blk_end[i]) of one list in problem order, each tile one
+// workgroup whose waves share kStageWaves / split[i] 16-column blocks and split
+// their K units split[i] ways; stage s runs tiles [stage_tile[s], stage_tile[s + 1]).
 constexpr int kMaxStages = BITNET_MAX_STAGES;
 // Workspace of a staged launch: words 0 (release) and 1 (timeout flag), then
 // one arrival flag per workgroup from word kStageFlag0; at most kMaxStageGrid
@@ -70,6 +71,7 @@ struct StageTable {
   int32_t M;
   uint32_t blk_end[kMaxGroup];
   uint32_t stage_tile[kMaxStages + 1];
+  uint8_t split[kMaxGroup];
 };
 
 // Dispatch slot of workgroup b in a grouped launch (binary search over the
@@ -143,10 +145,12 @@ hipError_t launch_gemv_grouped(const bitnet_problem *problems, const GroupTable 
                                const uint8_t *workspace, bool fused, int64_t kmax,
                                hipStream_t stream);
 
-// Staged single-row decode: every stage's tiles, a device-wide barrier between
-// stages, one cooperative launch.  sync: 2 zeroed words (counter, timeout flag).
-hipError_t launch_gemv_stages(const bitnet_problem *problems, const StageTable &tab,
-                              int64_t kmax, uint32_t *sync, hipStream_t stream);
+// stages.hip: dependent decode stages in one cooperative launch.  Builds the
+// tile table (per-stage K-split) from the host copy of the problems and
+// launches; sync is the workspace (kStageWorkspaceBytes).
+hipError_t launch_stages(const bitnet_problem *problems_dev, const bitnet_problem *problems_host,
+                         int count, const int32_t *stage_end, int nstages, int M,
+                         uint32_t *sync, hipStream_t stream);
 
 // gemm.hip  (M > 16)
 hipError_t launch_gemm(int M, int N, int K, const int8_t *xq_perm, const float *x_scale,

@@ -31,8 +31,6 @@
 // workgroup streams them into LDS in chunks of kChunkUnits units (buffer_load
 // ... lds, double-buffered, one barrier per chunk), so its four waves share
 // one copy instead of each reading every row from L2.
-#include <algorithm>
-
 #include "bitnet_device.hpp"
 #include "bitnet_internal.hpp"
 
@@ -86,31 +84,16 @@ struct GemvShared {
   int rowsum[kGemvMaxM];
 };
 
-// Cache-policy bits of a device-coherent load (sc1): it reads what another
-// workgroup's device-scope stores wrote earlier in the same launch.
-constexpr int kCoherentAux = 16;
-
 // Quantize the M rows of x into LDS (permuted order) with the scales and row sums.
-// COHERENT: x was written earlier in the same launch (staged decode), so it is
-// read with device-coherent loads.
-template <bool COHERENT>
 __device__ __forceinline__ void quant_rows_to_lds(const GemvProblem &p, GemvShared &sh,
                                                   int8_t *xq_lds, bool write_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n4 = p.K >> 2;
-  const __amdgpu_buffer_rsrc_t x_rsrc =
-      make_rsrc(COHERENT ? p.x : nullptr, COHERENT ? (uint32_t)(p.M * p.K * 4) : 0u);
-  auto ld_x4 = [&](int m, int i) -> f32x4 {
-    if (COHERENT)
-      return __builtin_bit_cast(
-          f32x4, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, (uint32_t)(m * p.K + 4 * i) * 4, 0,
-                                                       kCoherentAux));
-    return ld_global<f32x4>(reinterpret_cast<const f32x4 *>(p.x + (size_t)m * p.K) + i);
-  };
   for (int m = 0; m < p.M; ++m) {
+    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(p.x + (size_t)m * p.K);
     float a = 0.0f;
     for (int i = tid; i < n4; i += kThreads) {
-      const f32x4 v = ld_x4(m, i);
+      const f32x4 v = ld_global<f32x4>(x4 + i);
       a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     }
     a = wave_max(a);
@@ -120,10 +103,11 @@ __device__ __forceinline__ void quant_rows_to_lds(const GemvProblem &p, GemvShar
   for (int m = 0; m < p.M; ++m) {
     const float a = fmaxf(fmaxf(sh.red[m][0], sh.red[m][1]), fmaxf(sh.red[m][2], sh.red[m][3]));
     const float s = (a == 0.0f) ? 1.0f : 127.0f / a;
+    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(p.x + (size_t)m * p.K);
     int8_t *dst = xq_lds + (size_t)m * p.K;
     int sum = 0;
     for (int i = tid; i < n4; i += kThreads) {
-      const f32x4 v = ld_x4(m, i);
+      const f32x4 v = ld_global<f32x4>(x4 + i);
       const int q0 = quant_one(v.x, s), q1 = quant_one(v.y, s);
       const int q2 = quant_one(v.z, s), q3 = quant_one(v.w, s);
       sum += q0 + q1 + q2 + q3;
@@ -149,18 +133,10 @@ __device__ __forceinline__ void quant_rows_to_lds(const GemvProblem &p, GemvShar
 // launches only), wave w owns the 64 columns of group g = w % (4/S) starting at
 // (blk * 4/S + g) * 64, over K units [q * units / S, (q + 1) * units / S) with
 // q = w / (4/S).  FUSED: the rows are quantized into LDS here; otherwise they
-// are staged into LDS from the workspace chunk by chunk.  `before_x` runs once
-// the first weight loads are in flight and before x is read (the staged decode
-// waits there for the previous stage); COHERENT reads x and writes y with
-// device-coherent accesses.
-struct NoHook {
-  __device__ void operator()() const {}
-};
-
-template <bool FUSED, bool COHERENT = false, typename Hook = NoHook>
+// are staged into LDS from the workspace chunk by chunk.
+template <bool FUSED>
 __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, bool split,
-                                           GemvShared &sh, int8_t *lds,
-                                           const Hook &before_x = Hook()) {
+                                           GemvShared &sh, int8_t *lds) {
   constexpr int C = kGemvC;
   constexpr int D = kGemvDepth;
   const int lane = threadIdx.x & 63;
@@ -223,8 +199,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, bool s
 #pragma unroll
   for (int j = 0; j < D; ++j) load_item(wr[j]);
 
-  before_x();
-  if (FUSED) quant_rows_to_lds<COHERENT>(p, sh, lds, p.xq_out != nullptr && blk == 0);
+  if (FUSED) quant_rows_to_lds(p, sh, lds, p.xq_out != nullptr && blk == 0);
 
   // Dequantization inputs of accumulator element r of this lane (row 4h + r).
   const float ws = ld_global<float>(p.w_scale);
@@ -318,12 +293,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, bool s
       if (row < p.M && n < p.N) {
         const int a = acc[c][r] - row_rs[r];
         if (p.acc_out) st_global<int>(p.acc_out + (size_t)row * p.N + n, a);
-        const float v = dequant_exact(a, ws, row_xs[r]);
-        if (COHERENT)
-          __hip_atomic_store((BITNET_GLOBAL float *)(p.y + (size_t)row * p.N + n), v,
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else
-          st_global<float>(p.y + (size_t)row * p.N + n, v);
+        st_global<float>(p.y + (size_t)row * p.N + n, dequant_exact(a, ws, row_xs[r]));
       }
     }
   }
@@ -374,113 +344,6 @@ __global__ void __launch_bounds__(kThreads)
   gemv_block<FUSED>(p, (int)(b - first), tab.split != 0, sh, xq_lds);
 }
 
-__global__ void zero_words_kernel(uint32_t *__restrict__ w, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) st_global<uint32_t>(w + i, 0u);
-}
-
-// Stage handoff in the staged decode, for a cooperative (co-resident) grid.
-// Data crosses stages only through device-coherent accesses (y written with
-// device-scope stores, x read with sc1 loads), so no cache writeback or
-// invalidate is needed, only order: a workgroup arrives once its own stores
-// have completed (vmcnt 0 in every wave, then the workgroup barrier) by
-// storing the stage number into its flag; workgroup 0 waits for every flag
-// and then publishes the stage number in the release word, which the others
-// poll.  Waits are bounded by `timeout` ticks of the constant-rate wall clock:
-// a wait that runs out raises the flag in sync[1] instead of hanging, later
-// waits return at once, and the outputs are then not valid.
-// Workspace words: [0] release, [1] timeout flag, [kStageFlag0 + b] flag of
-// workgroup b.
-__device__ __forceinline__ uint32_t ld_agent(const uint32_t *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent(uint32_t *p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void stage_arrive(uint32_t *sync, uint32_t gen) {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();
-  if (threadIdx.x == 0) st_agent(&sync[kStageFlag0 + blockIdx.x], gen);
-}
-
-__device__ __forceinline__ void stage_wait(uint32_t *sync, uint32_t gen, uint64_t timeout) {
-  if (blockIdx.x == 0) {
-    const bool skip = ld_agent(&sync[1]) != 0;
-    const uint64_t t0 = wall_clock64();
-    for (uint32_t i = threadIdx.x; i < gridDim.x && !skip; i += kThreads) {
-      while (ld_agent(&sync[kStageFlag0 + i]) < gen) {
-        if (wall_clock64() - t0 > timeout) {
-          atomicOr(&sync[1], 1u);
-          break;
-        }
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) st_agent(&sync[0], gen);
-  } else if (threadIdx.x == 0 && ld_agent(&sync[1]) == 0) {
-    const uint64_t t0 = wall_clock64();
-    while (ld_agent(&sync[0]) < gen) {
-      if (wall_clock64() - t0 > timeout) {
-        atomicOr(&sync[1], 1u);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-  }
-  __syncthreads();
-}
-
-// Staged single-row decode: workgroup b runs tiles b, b + G, ... of each stage
-// (G = grid size).  Before stage s > 0 reads its activations it waits for
-// every workgroup to have arrived from stage s - 1; the wait sits after the
-// first weight loads of the workgroup's first tile of the stage are issued, so
-// that latency overlaps the handoff.
-__global__ void __launch_bounds__(kThreads)
-    gemv_stages_kernel(const bitnet_problem *__restrict__ problems, StageTable tab,
-                       uint32_t *__restrict__ sync, uint64_t timeout) {
-  __shared__ GemvShared sh;
-  extern __shared__ __attribute__((aligned(16))) int8_t xq_lds[];
-  const uint32_t G = gridDim.x;
-  for (int s = 0; s < tab.nstages; ++s) {
-    const uint32_t gen = (uint32_t)s;    // stage s waits for arrivals from stage s - 1
-    bool waited = s == 0;
-    for (uint32_t t = tab.stage_tile[s] + blockIdx.x; t < tab.stage_tile[s + 1]; t += G) {
-      int lo = 0, hi = tab.count - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (t < tab.blk_end[mid]) hi = mid; else lo = mid + 1;
-      }
-      const bitnet_problem pr = problems[lo];
-      GemvProblem p;
-      p.packed = pr.packed;
-      p.x = pr.x;
-      p.xqp = nullptr;
-      p.x_scale = nullptr;
-      p.rowsum = nullptr;
-      p.w_scale = pr.w_scale;
-      p.y = pr.y;
-      p.acc_out = nullptr;
-      p.xq_out = nullptr;
-      p.x_scale_out = nullptr;
-      p.N = (int)pr.N;
-      p.K = (int)pr.K;
-      p.M = tab.M;
-      // Every wave is done with the previous tile's LDS before this one starts.
-      __syncthreads();
-      const bool first = !waited;
-      gemv_block<true, true>(p, (int)(t - (lo ? tab.blk_end[lo - 1] : 0u)), true, sh, xq_lds,
-                             [&]() {
-                               if (first) stage_wait(sync, gen, timeout);
-                             });
-      waited = true;
-    }
-    if (!waited) stage_wait(sync, gen, timeout);
-    if (s + 1 < tab.nstages) stage_arrive(sync, gen + 1);
-  }
-}
-
 }  // namespace
 
 int gemv_blocks(int64_t N, int64_t K, bool split) {
@@ -517,36 +380,6 @@ hipError_t launch_gemv_fused(int M, int N, int K, const float *x, const uint8_t 
   gemv_kernel<true><<<gemv_blocks(N, K, split), kThreads, fused_lds_bytes(M, K, split),
                       stream>>>(p, split ? 1 : 0);
   return hipGetLastError();
-}
-
-hipError_t launch_gemv_stages(const bitnet_problem *problems, const StageTable &tab,
-                              int64_t kmax, uint32_t *sync, hipStream_t stream) {
-  const size_t lds = fused_lds_bytes(tab.M, kmax, true);
-  int dev = 0, per_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  hipDeviceProp_t prop;
-  e = hipGetDeviceProperties(&prop, dev);
-  if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_stages_kernel, kThreads, lds);
-  if (e != hipSuccess) return e;
-  if (per_cu < 1) return hipErrorInvalidConfiguration;
-  // Enough workgroups for the largest stage, at most what can be co-resident.
-  uint32_t widest = 1;
-  for (int s = 0; s < tab.nstages; ++s)
-    widest = std::max(widest, tab.stage_tile[s + 1] - tab.stage_tile[s]);
-  const unsigned grid = (unsigned)std::min<int64_t>(
-      std::min<int64_t>((int64_t)per_cu * prop.multiProcessorCount, widest), kMaxStageGrid);
-  // Bound each wait between stages at 200 ms of the wall clock.
-  int clock_khz = 0;
-  e = hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, dev);
-  if (e != hipSuccess) return e;
-  uint64_t timeout = (uint64_t)std::max(clock_khz, 1) * 200u;
-  zero_words_kernel<<<1, kThreads, 0, stream>>>(sync, kStageFlag0 + (int)grid);
-  StageTable t = tab;
-  void *args[] = {(void *)&problems, (void *)&t, (void *)&sync, (void *)&timeout};
-  return hipLaunchCooperativeKernel((const void *)gemv_stages_kernel, dim3(grid), dim3(kThreads),
-                                    args, lds, stream);
 }
 
 hipError_t launch_gemv_grouped(const bitnet_problem *problems, const GroupTable &tab,

@@ -1,0 +1,400 @@
+// Staged decode: a sequence of dependent single-token projection stages in one
+// cooperative launch.
+//
+// Per token the decoder streams all of its ternary weights (blog "The Paper
+// Says ARM Support...", section "What the model is trying to do"), and its
+// projections depend on each other: q,k,v read the layer input, o reads the
+// attention output, gate and up read o's, down reads the MLP product, and the
+// next layer reads down's.  Each stage is small (0.6 to 7 MB of codes), so
+// its time is memory latency, not bandwidth: the tile shape here is chosen for
+// one round trip per stage, not for streaming.
+//
+// Tile = one workgroup of 4 waves.  A wave owns one 16-column block and
+// kq-th of its K units when the block's K is split S ways (S = 1, 2, 4 per
+// problem, chosen on the host so that each stage fills the chip without a
+// workgroup taking two tiles); the 4/S blocks of a tile are adjacent.  Every
+// weight load of the wave (at most kStageItems units of 512 bytes per wave)
+// is issued before the wave waits for the previous stage, so weight latency
+// overlaps the handoff.  The activation row is then read once into registers
+// (device-coherent loads: it was written by other workgroups in this launch),
+// quantized (absmax scale, round half to even, clamp to 127) into LDS in the
+// permuted order, and contracted with v_mfma_i32_16x16x64_i8 on the field
+// values u = code + 1; the epilogue subtracts the activation row sum and
+// dequantizes exactly (acc * w_scale / x_scale in fp64, rounded to fp32).
+//
+// Handoff: data crosses stages only through device-coherent accesses (y
+// written with device-scope stores, x read with sc1 loads), so no cache
+// writeback or invalidate is needed, only order.  A workgroup arrives once
+// its own stores have completed (vmcnt 0 in every wave, then the workgroup
+// barrier) by storing the stage number into its flag; workgroup 0 waits for
+// every flag (its threads poll them in parallel) and then publishes the stage
+// number in the release word, which the others poll before they read the
+// next stage's activations.  So no workgroup starts stage s + 1 before every
+// workgroup has finished stage s, and a later stage may also overwrite what
+// an earlier one read.  (Every workgroup polling every flag instead of the
+// release word costs more: the polls of all workgroups crowd the memory
+// system.)  Every wait is bounded by a wall-clock timeout: a wait that runs
+// out raises the flag in sync[1] instead of hanging, later waits return at
+// once, and the outputs are then not valid.
+#include <algorithm>
+#include <cstring>
+
+#include "bitnet_device.hpp"
+#include "bitnet_internal.hpp"
+
+namespace bitnet {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kStageWaves = kWaves;
+constexpr int kStageItems = 18;    // K units per wave: ceil(70 / 4) for K <= 8960
+constexpr int kStageXVec = (int)((kGemvFusedLdsBytes / 4 + kThreads - 1) / kThreads);
+constexpr int kWeightAux = 2;      // weights are read once: non-temporal
+constexpr int kCoherentAux = 16;   // sc1: device-coherent load
+
+struct StageShared {
+  __attribute__((aligned(16))) int8_t xq[kGemvFusedLdsBytes];   // permuted rows [M][K]
+  v4i part[kStageWaves - 1][64];                                 // K-split partials
+  float red[kGemvMaxM][kWaves];
+  int ired[kGemvMaxM][kWaves];
+  float scale[kGemvMaxM];
+};
+
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void stage_arrive(uint32_t *sync, uint32_t gen) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0) st_agent(&sync[kStageFlag0 + blockIdx.x], gen);
+}
+
+__device__ __forceinline__ void stage_wait(uint32_t *sync, uint32_t gen, uint64_t timeout) {
+  if (blockIdx.x == 0) {
+    const bool skip = ld_agent(&sync[1]) != 0;
+    const uint64_t t0 = wall_clock64();
+    for (uint32_t i = threadIdx.x; i < gridDim.x && !skip; i += kThreads) {
+      while (ld_agent(&sync[kStageFlag0 + i]) < gen) {
+        if (wall_clock64() - t0 > timeout) {
+          atomicOr(&sync[1], 1u);
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) st_agent(&sync[0], gen);
+  } else if (threadIdx.x == 0 && ld_agent(&sync[1]) == 0) {
+    const uint64_t t0 = wall_clock64();
+    while (ld_agent(&sync[0]) < gen) {
+      if (wall_clock64() - t0 > timeout) {
+        atomicOr(&sync[1], 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+}
+
+// Wave-wide max / sum with DPP row operations (lane 63 collects the result):
+// swaps within quads, mirrors within 8 and 16 lanes, then row broadcasts of
+// lanes 15 and 31.  Max is taken over non-negative values.
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_dpp(int v, Op op) {
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));   // row_mirror
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false));   // row_bcast:15
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false));   // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ float wave_absmax_dpp(float a) {
+  return __builtin_bit_cast(float, wave_reduce_dpp(__builtin_bit_cast(int, a), [](int x, int y) {
+    return __builtin_bit_cast(int, fmaxf(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y)));
+  }));
+}
+__device__ __forceinline__ int wave_sum_dpp(int v) {
+  return wave_reduce_dpp(v, [](int x, int y) { return x + y; });
+}
+
+// The M rows of x (M * K <= kGemvFusedLdsBytes) into LDS as permuted int8,
+// with per-row scales and per-wave row-sum partials.  Element vector e (4
+// floats) of the flattened rows is held by thread e % 256 in register e / 256,
+// so the whole activation block is read in one round of loads.  ONE_ROW: M = 1.
+template <bool ONE_ROW>
+__device__ __forceinline__ void stage_quant(const float *x, int M_, int K, StageShared &sh) {
+  const int M = ONE_ROW ? 1 : M_;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n4 = K >> 2, total = M * n4;
+  const uint32_t x_bytes = (uint32_t)total * 16;
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(x, x_bytes);
+  f32x4 v[kStageXVec];
+  int row[kStageXVec];
+#pragma unroll
+  for (int j = 0; j < kStageXVec; ++j) {
+    const int e = tid + j * kThreads;
+    const uint32_t off = e < total ? (uint32_t)e * 16 : x_bytes;
+    v[j] = __builtin_bit_cast(f32x4,
+                              __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kCoherentAux));
+    row[j] = e < total ? (ONE_ROW ? 0 : e / n4) : -1;
+  }
+  for (int m = 0; m < M; ++m) {
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kStageXVec; ++j) {
+      if (row[j] == m)
+        a = fmaxf(a, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)),
+                           fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+    }
+    a = wave_absmax_dpp(a);
+    if (lane == 0) sh.red[m][wave] = a;
+  }
+  __syncthreads();
+  // Every thread derives the scales of the rows it holds; thread m < M also
+  // publishes row m's scale for the epilogue (read after the next barrier).
+  int qsum[kStageXVec];
+#pragma unroll
+  for (int j = 0; j < kStageXVec; ++j) {
+    qsum[j] = 0;
+    if (row[j] >= 0) {
+      const int r = row[j];
+      const float a = fmaxf(fmaxf(sh.red[r][0], sh.red[r][1]), fmaxf(sh.red[r][2], sh.red[r][3]));
+      const float s = (a == 0.0f) ? 1.0f : 127.0f / a;
+      const int q0 = quant_one(v[j].x, s), q1 = quant_one(v[j].y, s);
+      const int q2 = quant_one(v[j].z, s), q3 = quant_one(v[j].w, s);
+      qsum[j] = q0 + q1 + q2 + q3;
+      const int i = tid + j * kThreads - r * n4;   // vector within the row
+      *reinterpret_cast<uint32_t *>(sh.xq + r * K + perm_offset(4 * i)) = pack4_i8(q0, q1, q2, q3);
+    }
+  }
+  if (tid < M) {
+    const float a = fmaxf(fmaxf(sh.red[tid][0], sh.red[tid][1]),
+                          fmaxf(sh.red[tid][2], sh.red[tid][3]));
+    sh.scale[tid] = (a == 0.0f) ? 1.0f : 127.0f / a;
+  }
+  for (int m = 0; m < M; ++m) {
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < kStageXVec; ++j) sum += row[j] == m ? qsum[j] : 0;
+    sum = wave_sum_dpp(sum);
+    if (lane == 0) sh.ired[m][wave] = sum;
+  }
+  __syncthreads();
+}
+
+// Tile `tile` of problem pr with K-split S; NI >= the units of any wave.
+// `before_x` runs after the weight loads are issued and before the
+// activations are read.
+template <int NI, bool ONE_ROW, typename Hook>
+__device__ __forceinline__ void stage_tile(const bitnet_problem &pr, int M, int tile, int S,
+                                           StageShared &sh, const Hook &before_x) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, h = lane >> 4;
+  const int N = (int)pr.N, K = (int)pr.K, U = K >> 7;
+  const int G4 = kStageWaves / S, cgrp = wave % G4, kq = wave / G4;
+  const int u0 = kq * U / S, units = (kq + 1) * U / S - u0;   // 1 <= units <= NI
+  const int n = (tile * G4 + cgrp) * 16 + col;
+
+  // Items past the wave's units are aimed past the buffer: they load zeros
+  // without a memory access, and their MFMAs add nothing.
+  const uint32_t w_bytes = (uint32_t)((size_t)N * K / 4);
+  const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(pr.packed, w_bytes);
+  const uint32_t ustride = (uint32_t)N * kUnitBytes;
+  u32x2 wr[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint32_t off = (i < units && n < N)
+                             ? (uint32_t)(u0 + i) * ustride + (uint32_t)n * kUnitBytes + 8 * h
+                             : w_bytes;
+    wr[i] = __builtin_amdgcn_raw_buffer_load_b64(w_rsrc, off, 0, kWeightAux);
+  }
+
+  before_x();
+  stage_quant<ONE_ROW>(pr.x, M, K, sh);
+
+  // Four independent accumulation chains (item i feeds chain i % 4), so the
+  // MFMAs of consecutive items do not wait for each other.
+  constexpr int kChains = NI < 4 ? NI : 4;
+  const v4i zero4 = v4i{0, 0, 0, 0};
+  v4i accs[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) accs[c] = zero4;
+  const bool a_live = col < (ONE_ROW ? 1 : M);
+  const int8_t *arow = sh.xq + (a_live ? col : 0) * K + 32 * h;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int ui = u0 + (i < units ? i : units - 1);   // in range; codes are zero past units
+    v4i a0 = zero4, a1 = zero4;
+    if (a_live) {
+      const v4i *ap = reinterpret_cast<const v4i *>(arow + ui * kUnit);
+      a0 = ap[0];
+      a1 = ap[1];
+    }
+    v4i &acc = accs[i % kChains];
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, unpack_fields(wr[i].x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, unpack_fields(wr[i].y), acc, 0, 0, 0);
+  }
+  v4i acc = accs[0];
+#pragma unroll
+  for (int c = 1; c < kChains; ++c) acc += accs[c];
+
+  if (S > 1) {
+    if (kq > 0) sh.part[(kq - 1) * G4 + cgrp][lane] = acc;
+    __syncthreads();
+    if (kq > 0) return;
+    for (int q = 1; q < S; ++q) acc += sh.part[(q - 1) * G4 + cgrp][lane];
+  }
+
+  // Element (row 4h + r, column col) of the 16-column block.
+  const float ws = ld_global<float>(pr.w_scale);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int rw = 4 * h + r;
+    if (rw < (ONE_ROW ? 1 : M) && n < N) {
+      const int rowsum = sh.ired[rw][0] + sh.ired[rw][1] + sh.ired[rw][2] + sh.ired[rw][3];
+      const float y = dequant_exact(acc[r] - rowsum, ws, sh.scale[rw]);
+      __hip_atomic_store((BITNET_GLOBAL float *)(pr.y + (size_t)rw * N + n), y, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// The tile routine for the largest per-wave unit count ni of the tile.
+template <bool ONE_ROW, typename Hook>
+__device__ __forceinline__ void stage_tile_any(int ni, const bitnet_problem &pr, int M, int tile,
+                                               int S, StageShared &sh, const Hook &before_x) {
+  if (ni <= 3)
+    stage_tile<3, ONE_ROW>(pr, M, tile, S, sh, before_x);
+  else if (ni <= 6)
+    stage_tile<6, ONE_ROW>(pr, M, tile, S, sh, before_x);
+  else if (ni <= 12)
+    stage_tile<12, ONE_ROW>(pr, M, tile, S, sh, before_x);
+  else
+    stage_tile<kStageItems, ONE_ROW>(pr, M, tile, S, sh, before_x);
+}
+
+// Workgroup b runs tiles b, b + G, ... of each stage (G = grid size).  Before
+// stage s > 0 reads its activations it waits for every workgroup to have
+// arrived from stage s - 1.
+__global__ void __launch_bounds__(kThreads)
+    stages_kernel(const bitnet_problem *__restrict__ problems, StageTable tab,
+                  uint32_t *__restrict__ sync, uint64_t timeout) {
+  __shared__ StageShared sh;
+  const uint32_t G = gridDim.x;
+  for (int s = 0; s < tab.nstages; ++s) {
+    const uint32_t gen = (uint32_t)s;   // arrivals from stage s - 1 carry s
+    bool waited = s == 0;
+    for (uint32_t t = tab.stage_tile[s] + blockIdx.x; t < tab.stage_tile[s + 1]; t += G) {
+      int lo = 0, hi = tab.count - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (t < tab.blk_end[mid]) hi = mid; else lo = mid + 1;
+      }
+      const bitnet_problem pr = problems[lo];
+      const int tile = (int)(t - (lo ? tab.blk_end[lo - 1] : 0u));
+      // Every wave is done with the previous tile's LDS before this one starts.
+      __syncthreads();
+      const bool first = !waited;
+      const int S = (int)tab.split[lo];
+      const int ni = ((int)(pr.K >> 7) + S - 1) / S;
+      auto hook = [&]() {
+        if (first) stage_wait(sync, gen, timeout);
+      };
+      if (tab.M == 1)
+        stage_tile_any<true>(ni, pr, 1, tile, S, sh, hook);
+      else
+        stage_tile_any<false>(ni, pr, tab.M, tile, S, sh, hook);
+      waited = true;
+    }
+    if (!waited) stage_wait(sync, gen, timeout);
+    if (s + 1 < tab.nstages) stage_arrive(sync, gen + 1);
+  }
+}
+
+__global__ void zero_words_kernel(uint32_t *__restrict__ w, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) st_global<uint32_t>(w + i, 0u);
+}
+
+// Tiles of one problem at K-split S.
+int64_t stage_tiles(int64_t N, int S) {
+  const int64_t blocks = (N + 15) / 16;
+  const int64_t per = kStageWaves / S;
+  return (blocks + per - 1) / per;
+}
+
+// K-split of a problem for a stage-wide choice S: at least what keeps a
+// wave's units within kStageItems, at most what leaves every wave a unit.
+int problem_split(int64_t K, int S) {
+  const int64_t U = K >> 7;
+  const int need = U <= kStageItems ? 1 : U <= 2 * kStageItems ? 2 : 4;
+  const int most = U >= 4 ? 4 : U >= 2 ? 2 : 1;
+  return std::max(need, std::min(S, most));
+}
+
+}  // namespace
+
+hipError_t launch_stages(const bitnet_problem *problems_dev, const bitnet_problem *problems_host,
+                         int count, const int32_t *stage_end, int nstages, int M,
+                         uint32_t *sync, hipStream_t stream) {
+  int dev = 0, per_cu = 0, cus = 0, clock_khz = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stages_kernel, kThreads, 0);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
+
+  // Per stage, the largest K-split (more, shorter waves) whose tiles still fit
+  // one per compute unit; if none fits, the smallest.
+  StageTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  tab.count = count;
+  tab.nstages = nstages;
+  tab.M = M;
+  int64_t total = 0, widest = 1;
+  int first = 0;
+  for (int s = 0; s < nstages; ++s) {
+    const int last = stage_end[s];
+    int chosen = 1;
+    for (int S : {4, 2, 1}) {
+      int64_t tiles = 0;
+      for (int i = first; i < last; ++i)
+        tiles += stage_tiles(problems_host[i].N, problem_split(problems_host[i].K, S));
+      chosen = S;
+      if (tiles <= cus) break;
+    }
+    int64_t tiles = 0;
+    for (int i = first; i < last; ++i) {
+      const int Si = problem_split(problems_host[i].K, chosen);
+      tab.split[i] = (uint8_t)Si;
+      tiles += stage_tiles(problems_host[i].N, Si);
+      total += stage_tiles(problems_host[i].N, Si);
+      if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+      tab.blk_end[i] = (uint32_t)total;
+    }
+    tab.stage_tile[s + 1] = (uint32_t)total;
+    widest = std::max(widest, tiles);
+    first = last;
+  }
+  const unsigned grid = (unsigned)std::min<int64_t>(
+      std::min<int64_t>((int64_t)per_cu * cus, widest), kMaxStageGrid);
+  // Bound each wait between stages at 200 ms of the wall clock.
+  uint64_t timeout = (uint64_t)std::max(clock_khz, 1) * 200u;
+  zero_words_kernel<<<1, kThreads, 0, stream>>>(sync, kStageFlag0 + (int)grid);
+  void *args[] = {(void *)&problems_dev, (void *)&tab, (void *)&sync, (void *)&timeout};
+  return hipLaunchCooperativeKernel((const void *)stages_kernel, dim3(grid), dim3(kThreads), args,
+                                    0, stream);
+}
+
+}  // namespace bitnet

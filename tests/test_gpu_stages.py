@@ -123,3 +123,40 @@ def test_stages_single_stage_matches_grouped(tb):
     assert not plan.timed_out()
     for a, b in zip(y1, y2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("M", [1, 3, 16])
+def test_stages_general_shapes_bit_exact(tb, M):
+    """Several rows, ragged N, a one-unit K, two problems per stage:
+    A,B <- x | C <- y_A | D <- y_C | E,F <- y_D."""
+    import torch
+    say(f"[stages] general chain, M={M}")
+    Kc = min(1024, (8960 // M) // 128 * 128)
+    shapes = {"A": (Kc, Kc), "B": (Kc, 200), "C": (Kc, 128), "D": (128, Kc),
+              "E": (Kc, 77), "F": (Kc, Kc)}
+    src = {"A": "x", "B": "x", "C": "A", "D": "C", "E": "D", "F": "D"}
+    order = [["A", "B"], ["C"], ["D"], ["E", "F"]]
+    dev = "cuda:0"
+    packs, W = {}, {}
+    for i, (name, (K, N)) in enumerate(shapes.items()):
+        pk, s = oracle.ternarize_pack(synth.normal_weights(N, K, 700 + i))
+        packs[name] = (pk, s)
+        W[name] = (torch.from_numpy(pk).to(dev), torch.tensor([s], dtype=torch.float32, device=dev))
+    x0 = synth.activations(M, Kc, seed=701)
+    xd = torch.from_numpy(x0).to(dev)
+    ys = {n: torch.full((M, shapes[n][1]), float("nan"), device=dev) for n in shapes}
+    stages = [[(xd if src[n] == "x" else ys[src[n]], W[n][0], W[n][1], ys[n], shapes[n][1],
+                shapes[n][0]) for n in st] for st in order]
+    plan = tb.StagedPlan(M, stages)
+    plan.run()
+    torch.cuda.synchronize()
+    assert not plan.timed_out()
+    ref = {}
+    for st in order:
+        for n in st:
+            xin = x0 if src[n] == "x" else ref[src[n]]
+            pk, s = packs[n]
+            ref[n] = oracle.ternary_matmul(xin, pk, s, shapes[n][1])["y"]
+    for n in shapes:
+        got = ys[n].cpu().numpy()
+        np.testing.assert_array_equal(got.view(np.uint32), ref[n].view(np.uint32), n)
