@@ -77,6 +77,7 @@ typedef int32_t bitnet_status;
 #define BITNET_ERR_WORKSPACE 4  /* workspace missing or smaller than required      */
 #define BITNET_ERR_HIP       5  /* a HIP call or kernel launch reported an error   */
 #define BITNET_ERR_DEVICE    6  /* the current device is not a gfx950             */
+#define BITNET_ERR_ALIAS     7  /* outputs overlap each other or an input          */
 
 /* Maximum number of problems in one grouped call. */
 #define BITNET_MAX_GROUP     256
@@ -190,10 +191,11 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
  * "What the model is trying to do"), and its projections depend on each
  * other in order: q,k,v, then o, then gate,up, then down, layer after layer.
  * This call runs such a sequence of stages: problems [stage_end[s-1],
- * stage_end[s]) form stage s (stage_end[-1] = 0), the stages run in order,
- * and everything a stage writes is visible to the stages after it, so a
- * problem's x may be the y of an earlier stage.  Problems of one stage run
- * concurrently and must not write what another problem of the stage reads.
+ * stage_end[s]) form stage s (stage_end[-1] = 0), in order.  A problem whose
+ * x pointer equals the y pointer of a problem of an earlier stage reads that
+ * problem's output (its K must equal that problem's N); every other x is an
+ * input written before the call.  Outputs are those of the single calls
+ * (decode: exactly rounded).
  *
  * M             1..16, and M*K <= 8960 for every problem (rows quantized in
  *               the same workgroup; one row of the longest projection).
@@ -201,22 +203,26 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
  *               1..BITNET_MAX_STAGES; stage_end (host) strictly increasing,
  *               stage_end[nstages-1] == count.
  * problems_dev / problems_host as for the grouped call.
- * workspace     bitnet_stages_workspace_bytes() bytes, 256-byte aligned, no
- *               initial contents.  Word 1 (uint32) is nonzero after the call
- *               completes if a wait between stages ran past its bound
- *               (200 ms of the device's wall clock; once one wait has run
- *               out the later ones return at once); the outputs are then not
- *               valid.  The call never waits without bound.
- * One cooperative launch (all workgroups resident at once, at most 2048),
- * preceded by a small fill kernel that clears the workspace's flags.  Between
- * stages, outputs are written and read with device-coherent accesses and the
- * workgroups meet at a flag barrier in the workspace.  Outputs are those of the single calls
- * (decode: exactly rounded).  BITNET_ERR_HIP if the device cannot run the
- * workgroups together.
+ * y ranges      must not overlap each other nor any input x (one written
+ *               before the call): BITNET_ERR_ALIAS.
+ * workspace     bitnet_stages_workspace_bytes(M, problems_host, count)
+ *               bytes, 256-byte aligned, ZERO-FILLED before its first use
+ *               and written by nothing else afterwards (it carries a call
+ *               counter and the outputs that later stages read, each tagged
+ *               with that counter; later calls may reuse it).  Word 1 (uint32) is nonzero after the call
+ *               completes if a wait for a producer ran past its bound (200 ms
+ *               of the device's wall clock; once one wait has run out the
+ *               later ones return at once); the outputs are then not valid.
+ *               The call never waits without bound.
+ * One one-thread kernel (advances the counter), then one cooperative launch
+ * (all workgroups resident at once); no device-wide barrier: each tile waits
+ * only for the outputs it reads.  BITNET_ERR_HIP if the device cannot run
+ * the workgroups together.  Calls that share a workspace must not overlap.
  * ------------------------------------------------------------------------ */
 #define BITNET_MAX_STAGES 256
 
-size_t bitnet_stages_workspace_bytes(void);
+size_t bitnet_stages_workspace_bytes(int64_t M, const bitnet_problem *problems_host,
+                                     int32_t count);
 
 bitnet_status bitnet_ternary_matmul_stages(int64_t M, const bitnet_problem *problems_dev,
                                            int32_t count, const int32_t *stage_end,

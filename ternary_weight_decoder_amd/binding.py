@@ -80,7 +80,7 @@ def lib():
         L.bitnet_grouped_workspace_bytes.restype = _sz
         L.bitnet_ternary_matmul_grouped.argtypes = [_i64, _p, _i32, _p, _p, _sz, _p]
         L.bitnet_ternary_matmul_grouped.restype = _i32
-        L.bitnet_stages_workspace_bytes.argtypes = []
+        L.bitnet_stages_workspace_bytes.argtypes = [_i64, _p, _i32]
         L.bitnet_stages_workspace_bytes.restype = _sz
         L.bitnet_ternary_matmul_stages.argtypes = [_i64, _p, _i32, _p, _i32, _p, _p, _sz, _p]
         L.bitnet_ternary_matmul_stages.restype = _i32
@@ -264,8 +264,8 @@ def bitnet_ternary_matmul_grouped(M, problems_dev, count, problems_host, workspa
            "bitnet_ternary_matmul_grouped")
 
 
-def bitnet_stages_workspace_bytes() -> int:
-    return int(lib().bitnet_stages_workspace_bytes())
+def bitnet_stages_workspace_bytes(M: int, problems_host, count: int) -> int:
+    return int(lib().bitnet_stages_workspace_bytes(M, _c.byref(problems_host), count))
 
 
 def bitnet_ternary_matmul_stages(M, problems_dev, count, stage_end_host, nstages, problems_host,
@@ -279,11 +279,11 @@ def bitnet_ternary_matmul_stages(M, problems_dev, count, stage_end_host, nstages
 
 
 class StagedPlan:
-    """A fixed sequence of dependent stages of single-row projections (for
-    example one decode token through a decoder: q,k,v | o | gate,up | down per
-    layer), run by one call.  stages: list of lists of
-    (x, packed, w_scale, y, N, K) tuples; a later stage's x may be an earlier
-    stage's y."""
+    """A fixed sequence of dependent stages of decode projections (for example
+    one token through a decoder: q,k,v | o | gate,up | down per layer), run by
+    one call.  stages: list of lists of (x, packed, w_scale, y, N, K) tuples; a
+    problem whose x is the y tensor of a problem of an earlier stage reads that
+    output.  The workspace is zero-filled here, once."""
 
     def __init__(self, M: int, stages, device=None):
         flat = [pr for st in stages for pr in st]
@@ -304,8 +304,10 @@ class StagedPlan:
         self.host, self.ends = arr, ends
         dev = device if device is not None else flat[0][0].device
         self.dev = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8).to(dev)
-        self.workspace = torch.empty(bitnet_stages_workspace_bytes(), dtype=torch.uint8,
-                                     device=dev)
+        nbytes = bitnet_stages_workspace_bytes(self.M, arr, count)
+        if nbytes == 0:
+            raise ValueError("invalid staged problem list")
+        self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
 
     def run(self, stream=None) -> None:
         bitnet_ternary_matmul_stages(self.M, self.dev, self.count, self.ends, self.nstages,

@@ -82,6 +82,7 @@ const char *bitnet_status_string(bitnet_status s) {
     case BITNET_ERR_WORKSPACE: return "workspace missing or too small";
     case BITNET_ERR_HIP: return "HIP runtime or launch error";
     case BITNET_ERR_DEVICE: return "current device is not a gfx950";
+    case BITNET_ERR_ALIAS: return "outputs overlap each other or an input";
     default: return "unknown status";
   }
 }
@@ -274,7 +275,13 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
   return from_hip(launch_gemm_grouped(problems_dev, tab, ws, hs));
 }
 
-size_t bitnet_stages_workspace_bytes(void) { return kStageWorkspaceBytes; }
+size_t bitnet_stages_workspace_bytes(int64_t M, const bitnet_problem *problems_host,
+                                     int32_t count) {
+  if (!problems_host || count < 1 || count > kMaxGroup || M < 1 || M > kGemvMaxM) return 0;
+  for (int32_t i = 0; i < count; ++i)
+    if (!shape_ok(M, problems_host[i].N, problems_host[i].K)) return 0;
+  return stages_workspace_bytes(M, problems_host, count);
+}
 
 bitnet_status bitnet_ternary_matmul_stages(int64_t M, const bitnet_problem *problems_dev,
                                            int32_t count, const int32_t *stage_end,
@@ -292,19 +299,43 @@ bitnet_status bitnet_ternary_matmul_stages(int64_t M, const bitnet_problem *prob
     if (!gemv_fusable(M, problems_host[i].K)) return BITNET_ERR_SHAPE;
   }
   int32_t prev = 0;
+  int32_t stage_of[kMaxGroup];
   for (int32_t s = 0; s < nstages; ++s) {
     if (stage_end[s] <= prev || stage_end[s] > count) return BITNET_ERR_SHAPE;
+    for (int32_t i = prev; i < stage_end[s]; ++i) stage_of[i] = s;
     prev = stage_end[s];
   }
   if (prev != count) return BITNET_ERR_SHAPE;
-  if (!workspace || workspace_bytes < bitnet_stages_workspace_bytes()) return BITNET_ERR_WORKSPACE;
+  // Producers: an x equal to the y of a problem of an earlier stage.  Every
+  // other x is an input and must not overlap any y; y ranges are disjoint.
+  int16_t src[kMaxGroup];
+  auto y_lo = [&](int32_t j) { return reinterpret_cast<uintptr_t>(problems_host[j].y); };
+  auto y_hi = [&](int32_t j) { return y_lo(j) + (uintptr_t)(M * problems_host[j].N) * 4; };
+  for (int32_t i = 0; i < count; ++i) {
+    src[i] = -1;
+    for (int32_t j = 0; j < count; ++j)
+      if (stage_of[j] < stage_of[i] && (const void *)problems_host[j].y == problems_host[i].x)
+        src[i] = (int16_t)j;
+    if (src[i] >= 0) {
+      if (problems_host[src[i]].N != problems_host[i].K) return BITNET_ERR_SHAPE;
+      continue;
+    }
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(problems_host[i].x);
+    const uintptr_t hi = lo + (uintptr_t)(M * problems_host[i].K) * 4;
+    for (int32_t j = 0; j < count; ++j)
+      if (lo < y_hi(j) && y_lo(j) < hi) return BITNET_ERR_ALIAS;
+  }
+  for (int32_t i = 0; i < count; ++i)
+    for (int32_t j = i + 1; j < count; ++j)
+      if (y_lo(i) < y_hi(j) && y_lo(j) < y_hi(i)) return BITNET_ERR_ALIAS;
+  if (!workspace || workspace_bytes < stages_workspace_bytes(M, problems_host, count))
+    return BITNET_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return BITNET_ERR_ALIGN;
   bitnet_status st = device_check();
   if (st != BITNET_OK) return st;
 
-  return from_hip(launch_stages(problems_dev, problems_host, count, stage_end, nstages,
-                                (int)M, reinterpret_cast<uint32_t *>(workspace),
-                                as_stream(stream)));
+  return from_hip(launch_stages(problems_dev, problems_host, count, stage_end, nstages, (int)M,
+                                src, reinterpret_cast<uint8_t *>(workspace), as_stream(stream)));
 }
 
 }  // extern "C"

@@ -55,22 +55,23 @@ struct QuantTable {
 };
 
 // Per-launch table of a staged decode launch: problem i owns tiles
-// [blk_end[i-1], blk_end[i]) of one list in problem order, each tile one
-// workgroup whose waves share kStageWaves / split[i] 16-column blocks and split
-// their K units split[i] ways; stage s runs tiles [stage_tile[s], stage_tile[s + 1]).
+// [blk_end[i-1], blk_end[i]) of one list in problem (= stage) order, each tile
+// one workgroup whose waves share 4 / split[i] 16-column blocks and split
+// their K units split[i] ways.  src[i]: the earlier problem whose output is
+// problem i's x, or -1 for an input written before the call.  tag_off[i]:
+// workspace offset (256-byte units) of problem i's tagged outputs, kNoTag if
+// no later problem reads them.
 constexpr int kMaxStages = BITNET_MAX_STAGES;
-// Workspace of a staged launch: words 0 (release) and 1 (timeout flag), then
-// one arrival flag per workgroup from word kStageFlag0; at most kMaxStageGrid
-// workgroups.
-constexpr int kStageFlag0 = 64;
-constexpr int kMaxStageGrid = 2048;
-constexpr size_t kStageWorkspaceBytes = (size_t)(kStageFlag0 + kMaxStageGrid) * 4;
+constexpr size_t kStageHeaderBytes = 256;   // [0] epoch, [1] timeout flag
+constexpr uint32_t kNoTag = 0xffffffffu;
+constexpr int kMaxStageGrid = 2048;   // workgroups of one staged launch
 struct StageTable {
   int32_t count;
-  int32_t nstages;
   int32_t M;
+  uint32_t ntiles;
   uint32_t blk_end[kMaxGroup];
-  uint32_t stage_tile[kMaxStages + 1];
+  uint32_t tag_off[kMaxGroup];
+  int16_t src[kMaxGroup];
   uint8_t split[kMaxGroup];
 };
 
@@ -145,12 +146,13 @@ hipError_t launch_gemv_grouped(const bitnet_problem *problems, const GroupTable 
                                const uint8_t *workspace, bool fused, int64_t kmax,
                                hipStream_t stream);
 
-// stages.hip: dependent decode stages in one cooperative launch.  Builds the
-// tile table (per-stage K-split) from the host copy of the problems and
-// launches; sync is the workspace (kStageWorkspaceBytes).
+// stages.hip: dependent decode stages in one cooperative launch.  src[i]: the
+// earlier problem whose y is problem i's x, or -1.  ws: the workspace
+// (stages_workspace_bytes), zero-filled before its first use.
+size_t stages_workspace_bytes(int64_t M, const bitnet_problem *problems_host, int count);
 hipError_t launch_stages(const bitnet_problem *problems_dev, const bitnet_problem *problems_host,
                          int count, const int32_t *stage_end, int nstages, int M,
-                         uint32_t *sync, hipStream_t stream);
+                         const int16_t *src, uint8_t *ws, hipStream_t stream);
 
 // gemm.hip  (M > 16)
 hipError_t launch_gemm(int M, int N, int K, const int8_t *xq_perm, const float *x_scale,

@@ -14,28 +14,28 @@
 // problem, chosen on the host so that each stage fills the chip without a
 // workgroup taking two tiles); the 4/S blocks of a tile are adjacent.  Every
 // weight load of the wave (at most kStageItems units of 512 bytes per wave)
-// is issued before the wave waits for the previous stage, so weight latency
-// overlaps the handoff.  The activation row is then read once into registers
-// (device-coherent loads: it was written by other workgroups in this launch),
+// is issued before the wave waits for its activations, so weight latency
+// overlaps the wait.  The activation rows are read once into registers,
 // quantized (absmax scale, round half to even, clamp to 127) into LDS in the
 // permuted order, and contracted with v_mfma_i32_16x16x64_i8 on the field
 // values u = code + 1; the epilogue subtracts the activation row sum and
 // dequantizes exactly (acc * w_scale / x_scale in fp64, rounded to fp32).
 //
-// Handoff: data crosses stages only through device-coherent accesses (y
-// written with device-scope stores, x read with sc1 loads), so no cache
-// writeback or invalidate is needed, only order.  A workgroup arrives once
-// its own stores have completed (vmcnt 0 in every wave, then the workgroup
-// barrier) by storing the stage number into its flag; workgroup 0 waits for
-// every flag (its threads poll them in parallel) and then publishes the stage
-// number in the release word, which the others poll before they read the
-// next stage's activations.  So no workgroup starts stage s + 1 before every
-// workgroup has finished stage s, and a later stage may also overwrite what
-// an earlier one read.  (Every workgroup polling every flag instead of the
-// release word costs more: the polls of all workgroups crowd the memory
-// system.)  Every wait is bounded by a wall-clock timeout: a wait that runs
-// out raises the flag in sync[1] instead of hanging, later waits return at
-// once, and the outputs are then not valid.
+// Dataflow between stages, without a device-wide barrier: a problem whose
+// output a later stage reads also writes each output as a 64-bit pair (value
+// bits, call epoch) into the workspace with one device-scope store, and the
+// consumer reads those pairs with device-coherent loads, re-reading the ones
+// whose tag is not yet the current epoch.  A single atomic store carries value
+// and tag together, so no fence, flag or store acknowledgement sits between a
+// producer and its consumers.  A consumer first polls one probe pair (the last
+// one, written by the producer's last tile) so that waiting workgroups do not
+// flood the memory system, then reads everything.  Each workgroup runs its
+// tiles in stage order and the grid is co-resident, so the lowest unfinished
+// tile never waits on an unfinished one.  Every wait is bounded by a
+// wall-clock timeout: a wait that runs out raises the flag in workspace word 1
+// instead of hanging, later waits return at once, and the outputs are then
+// not valid.  The epoch (workspace word 0) is advanced by a one-thread kernel
+// before each launch.
 #include <algorithm>
 #include <cstring>
 
@@ -61,46 +61,17 @@ struct StageShared {
   float scale[kGemvMaxM];
 };
 
+// Where a tile reads its activations and writes its tagged outputs.
+struct StageIo {
+  const uint64_t *x_tagged;   // producer's (value, epoch) pairs, or null: read x
+  uint64_t *y_tagged;         // this problem's pairs, or null: no later reader
+  uint32_t epoch;
+  uint32_t *flags;            // workspace words: [0] epoch, [1] timeout flag
+  uint64_t timeout;           // wall-clock ticks per wait
+};
+
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent(uint32_t *p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void stage_arrive(uint32_t *sync, uint32_t gen) {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();
-  if (threadIdx.x == 0) st_agent(&sync[kStageFlag0 + blockIdx.x], gen);
-}
-
-__device__ __forceinline__ void stage_wait(uint32_t *sync, uint32_t gen, uint64_t timeout) {
-  if (blockIdx.x == 0) {
-    const bool skip = ld_agent(&sync[1]) != 0;
-    const uint64_t t0 = wall_clock64();
-    for (uint32_t i = threadIdx.x; i < gridDim.x && !skip; i += kThreads) {
-      while (ld_agent(&sync[kStageFlag0 + i]) < gen) {
-        if (wall_clock64() - t0 > timeout) {
-          atomicOr(&sync[1], 1u);
-          break;
-        }
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) st_agent(&sync[0], gen);
-  } else if (threadIdx.x == 0 && ld_agent(&sync[1]) == 0) {
-    const uint64_t t0 = wall_clock64();
-    while (ld_agent(&sync[0]) < gen) {
-      if (wall_clock64() - t0 > timeout) {
-        atomicOr(&sync[1], 1u);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-  }
-  __syncthreads();
 }
 
 // Wave-wide max / sum with DPP row operations (lane 63 collects the result):
@@ -125,25 +96,104 @@ __device__ __forceinline__ int wave_sum_dpp(int v) {
   return wave_reduce_dpp(v, [](int x, int y) { return x + y; });
 }
 
+// Pair i of a tagged array (uniform base, 32-bit element offset).
+__device__ __forceinline__ uint64_t ld_pair(const uint64_t *base, uint32_t i) {
+  const BITNET_GLOBAL uint64_t *p =
+      (const BITNET_GLOBAL uint64_t *)((const BITNET_GLOBAL char *)base + (size_t)(i * 8u));
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool pair_ok(uint64_t q, uint32_t epoch) {
+  return (uint32_t)(q >> 32) == epoch;
+}
+
+// Read vector e (4 activations) of every thread's share of the M x K block
+// into v[]: directly from x, or from the producer's tagged pairs (one 64-bit
+// atomic load per pair), waiting until every pair carries the current epoch.
+__device__ __forceinline__ void stage_load_x(const float *x, const StageIo &io, int total,
+                                             f32x4 (&v)[kStageXVec]) {
+  const int tid = threadIdx.x;
+  if (io.x_tagged == nullptr) {
+    const uint32_t bytes = (uint32_t)total * 16;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(x, bytes);
+#pragma unroll
+    for (int j = 0; j < kStageXVec; ++j) {
+      const int e = tid + j * kThreads;
+      const uint32_t off = e < total ? (uint32_t)e * 16 : bytes;
+      v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+    }
+    return;
+  }
+  const uint64_t *xt = io.x_tagged;
+  bool expired = ld_agent(&io.flags[1]) != 0;
+  uint64_t t0 = wall_clock64();
+  // Probe: poll the last pair (written by the producer's last tile) first.
+  while (!expired && !pair_ok(ld_pair(xt, 4u * total - 1u), io.epoch)) {
+    if (wall_clock64() - t0 > io.timeout) {
+      atomicOr(&io.flags[1], 1u);
+      expired = true;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  // Vectors past the block re-read the last one (in range) and are ignored.
+  uint64_t q[kStageXVec][4];
+  uint32_t pending = 0;
+#pragma unroll
+  for (int j = 0; j < kStageXVec; ++j) {
+    const int e = tid + j * kThreads;
+    const uint32_t ev = (uint32_t)(e < total ? e : total - 1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) q[j][c] = ld_pair(xt, 4u * ev + c);
+  }
+#pragma unroll
+  for (int j = 0; j < kStageXVec; ++j) {
+    if (tid + j * kThreads < total &&
+        !(pair_ok(q[j][0], io.epoch) && pair_ok(q[j][1], io.epoch) &&
+          pair_ok(q[j][2], io.epoch) && pair_ok(q[j][3], io.epoch)))
+      pending |= 1u << j;
+  }
+  t0 = wall_clock64();
+  while (pending != 0 && !expired) {
+    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+    for (int j = 0; j < kStageXVec; ++j) {
+      if ((pending >> j) & 1u) {
+        const int e = tid + j * kThreads;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) q[j][c] = ld_pair(xt, 4u * e + c);
+        if (pair_ok(q[j][0], io.epoch) && pair_ok(q[j][1], io.epoch) &&
+            pair_ok(q[j][2], io.epoch) && pair_ok(q[j][3], io.epoch))
+          pending &= ~(1u << j);
+      }
+    }
+    if (pending != 0 && wall_clock64() - t0 > io.timeout) {
+      atomicOr(&io.flags[1], 1u);
+      expired = true;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kStageXVec; ++j)
+    v[j] = f32x4{__builtin_bit_cast(float, (uint32_t)q[j][0]),
+                 __builtin_bit_cast(float, (uint32_t)q[j][1]),
+                 __builtin_bit_cast(float, (uint32_t)q[j][2]),
+                 __builtin_bit_cast(float, (uint32_t)q[j][3])};
+}
+
 // The M rows of x (M * K <= kGemvFusedLdsBytes) into LDS as permuted int8,
 // with per-row scales and per-wave row-sum partials.  Element vector e (4
 // floats) of the flattened rows is held by thread e % 256 in register e / 256,
 // so the whole activation block is read in one round of loads.  ONE_ROW: M = 1.
 template <bool ONE_ROW>
-__device__ __forceinline__ void stage_quant(const float *x, int M_, int K, StageShared &sh) {
+__device__ __forceinline__ void stage_quant(const float *x, const StageIo &io, int M_, int K,
+                                            StageShared &sh) {
   const int M = ONE_ROW ? 1 : M_;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n4 = K >> 2, total = M * n4;
-  const uint32_t x_bytes = (uint32_t)total * 16;
-  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(x, x_bytes);
   f32x4 v[kStageXVec];
+  stage_load_x(x, io, total, v);
   int row[kStageXVec];
 #pragma unroll
   for (int j = 0; j < kStageXVec; ++j) {
     const int e = tid + j * kThreads;
-    const uint32_t off = e < total ? (uint32_t)e * 16 : x_bytes;
-    v[j] = __builtin_bit_cast(f32x4,
-                              __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kCoherentAux));
     row[j] = e < total ? (ONE_ROW ? 0 : e / n4) : -1;
   }
   for (int m = 0; m < M; ++m) {
@@ -191,11 +241,10 @@ __device__ __forceinline__ void stage_quant(const float *x, int M_, int K, Stage
 }
 
 // Tile `tile` of problem pr with K-split S; NI >= the units of any wave.
-// `before_x` runs after the weight loads are issued and before the
-// activations are read.
-template <int NI, bool ONE_ROW, typename Hook>
-__device__ __forceinline__ void stage_tile(const bitnet_problem &pr, int M, int tile, int S,
-                                           StageShared &sh, const Hook &before_x) {
+template <int NI, bool ONE_ROW>
+__device__ __forceinline__ void stage_tile(const bitnet_problem &pr, int M_, int tile, int S,
+                                           StageShared &sh, const StageIo &io) {
+  const int M = ONE_ROW ? 1 : M_;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, h = lane >> 4;
   const int N = (int)pr.N, K = (int)pr.K, U = K >> 7;
@@ -217,8 +266,7 @@ __device__ __forceinline__ void stage_tile(const bitnet_problem &pr, int M, int 
     wr[i] = __builtin_amdgcn_raw_buffer_load_b64(w_rsrc, off, 0, kWeightAux);
   }
 
-  before_x();
-  stage_quant<ONE_ROW>(pr.x, M, K, sh);
+  stage_quant<ONE_ROW>(pr.x, io, M, K, sh);
 
   // Four independent accumulation chains (item i feeds chain i % 4), so the
   // MFMAs of consecutive items do not wait for each other.
@@ -227,7 +275,7 @@ __device__ __forceinline__ void stage_tile(const bitnet_problem &pr, int M, int 
   v4i accs[kChains];
 #pragma unroll
   for (int c = 0; c < kChains; ++c) accs[c] = zero4;
-  const bool a_live = col < (ONE_ROW ? 1 : M);
+  const bool a_live = col < M;
   const int8_t *arow = sh.xq + (a_live ? col : 0) * K + 32 * h;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -258,69 +306,76 @@ __device__ __forceinline__ void stage_tile(const bitnet_problem &pr, int M, int 
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int rw = 4 * h + r;
-    if (rw < (ONE_ROW ? 1 : M) && n < N) {
+    if (rw < M && n < N) {
       const int rowsum = sh.ired[rw][0] + sh.ired[rw][1] + sh.ired[rw][2] + sh.ired[rw][3];
       const float y = dequant_exact(acc[r] - rowsum, ws, sh.scale[rw]);
-      __hip_atomic_store((BITNET_GLOBAL float *)(pr.y + (size_t)rw * N + n), y, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      const size_t idx = (size_t)rw * N + n;
+      st_global<float>(pr.y + idx, y);
+      if (io.y_tagged)
+        __hip_atomic_store((BITNET_GLOBAL uint64_t *)(io.y_tagged + idx),
+                           (uint64_t)__builtin_bit_cast(uint32_t, y) | ((uint64_t)io.epoch << 32),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
 // The tile routine for the largest per-wave unit count ni of the tile.
-template <bool ONE_ROW, typename Hook>
+template <bool ONE_ROW>
 __device__ __forceinline__ void stage_tile_any(int ni, const bitnet_problem &pr, int M, int tile,
-                                               int S, StageShared &sh, const Hook &before_x) {
+                                               int S, StageShared &sh, const StageIo &io) {
   if (ni <= 3)
-    stage_tile<3, ONE_ROW>(pr, M, tile, S, sh, before_x);
+    stage_tile<3, ONE_ROW>(pr, M, tile, S, sh, io);
   else if (ni <= 6)
-    stage_tile<6, ONE_ROW>(pr, M, tile, S, sh, before_x);
+    stage_tile<6, ONE_ROW>(pr, M, tile, S, sh, io);
   else if (ni <= 12)
-    stage_tile<12, ONE_ROW>(pr, M, tile, S, sh, before_x);
+    stage_tile<12, ONE_ROW>(pr, M, tile, S, sh, io);
   else
-    stage_tile<kStageItems, ONE_ROW>(pr, M, tile, S, sh, before_x);
+    stage_tile<kStageItems, ONE_ROW>(pr, M, tile, S, sh, io);
 }
 
-// Workgroup b runs tiles b, b + G, ... of each stage (G = grid size).  Before
-// stage s > 0 reads its activations it waits for every workgroup to have
-// arrived from stage s - 1.
-__global__ void __launch_bounds__(kThreads)
+// Workgroup b runs tiles b, b + G, ... (G = grid size) in order; tiles are
+// numbered problem by problem, and problems come in stage order.
+__global__ void __launch_bounds__(kThreads, 2)
     stages_kernel(const bitnet_problem *__restrict__ problems, StageTable tab,
-                  uint32_t *__restrict__ sync, uint64_t timeout) {
+                  uint8_t *__restrict__ ws, uint64_t timeout) {
   __shared__ StageShared sh;
-  const uint32_t G = gridDim.x;
-  for (int s = 0; s < tab.nstages; ++s) {
-    const uint32_t gen = (uint32_t)s;   // arrivals from stage s - 1 carry s
-    bool waited = s == 0;
-    for (uint32_t t = tab.stage_tile[s] + blockIdx.x; t < tab.stage_tile[s + 1]; t += G) {
-      int lo = 0, hi = tab.count - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (t < tab.blk_end[mid]) hi = mid; else lo = mid + 1;
-      }
-      const bitnet_problem pr = problems[lo];
-      const int tile = (int)(t - (lo ? tab.blk_end[lo - 1] : 0u));
-      // Every wave is done with the previous tile's LDS before this one starts.
-      __syncthreads();
-      const bool first = !waited;
-      const int S = (int)tab.split[lo];
-      const int ni = ((int)(pr.K >> 7) + S - 1) / S;
-      auto hook = [&]() {
-        if (first) stage_wait(sync, gen, timeout);
-      };
-      if (tab.M == 1)
-        stage_tile_any<true>(ni, pr, 1, tile, S, sh, hook);
-      else
-        stage_tile_any<false>(ni, pr, tab.M, tile, S, sh, hook);
-      waited = true;
+  StageIo io;
+  io.flags = reinterpret_cast<uint32_t *>(ws);
+  io.epoch = ld_agent(&io.flags[0]);
+  io.timeout = timeout;
+  for (uint32_t t = blockIdx.x; t < tab.ntiles; t += gridDim.x) {
+    int lo = 0, hi = tab.count - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (t < tab.blk_end[mid]) hi = mid; else lo = mid + 1;
     }
-    if (!waited) stage_wait(sync, gen, timeout);
-    if (s + 1 < tab.nstages) stage_arrive(sync, gen + 1);
+    const bitnet_problem pr = problems[lo];
+    const int tile = (int)(t - (lo ? tab.blk_end[lo - 1] : 0u));
+    const int src = tab.src[lo];
+    io.x_tagged = src >= 0 ? reinterpret_cast<const uint64_t *>(ws + (size_t)tab.tag_off[src] * 256)
+                           : nullptr;
+    io.y_tagged = tab.tag_off[lo] != kNoTag
+                      ? reinterpret_cast<uint64_t *>(ws + (size_t)tab.tag_off[lo] * 256)
+                      : nullptr;
+    const int S = (int)tab.split[lo];
+    const int ni = ((int)(pr.K >> 7) + S - 1) / S;
+    // Every wave is done with the previous tile's LDS before this one starts.
+    __syncthreads();
+    if (tab.M == 1)
+      stage_tile_any<true>(ni, pr, 1, tile, S, sh, io);
+    else
+      stage_tile_any<false>(ni, pr, tab.M, tile, S, sh, io);
   }
 }
 
-__global__ void zero_words_kernel(uint32_t *__restrict__ w, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) st_global<uint32_t>(w + i, 0u);
+// Advance the call epoch (never 0, the value of a zero-filled workspace) and
+// clear the timeout flag.
+__global__ void stage_epoch_kernel(uint32_t *__restrict__ w) {
+  if (threadIdx.x == 0) {
+    uint32_t e = w[0] + 1u;
+    w[0] = e == 0u ? 1u : e;
+    w[1] = 0u;
+  }
 }
 
 // Tiles of one problem at K-split S.
@@ -341,9 +396,15 @@ int problem_split(int64_t K, int S) {
 
 }  // namespace
 
+size_t stages_workspace_bytes(int64_t M, const bitnet_problem *problems_host, int count) {
+  size_t total = kStageHeaderBytes;
+  for (int i = 0; i < count; ++i) total += align256((size_t)(M * problems_host[i].N) * 8);
+  return total;
+}
+
 hipError_t launch_stages(const bitnet_problem *problems_dev, const bitnet_problem *problems_host,
                          int count, const int32_t *stage_end, int nstages, int M,
-                         uint32_t *sync, hipStream_t stream) {
+                         const int16_t *src, uint8_t *ws, hipStream_t stream) {
   int dev = 0, per_cu = 0, cus = 0, clock_khz = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -355,14 +416,24 @@ hipError_t launch_stages(const bitnet_problem *problems_dev, const bitnet_proble
   if (e != hipSuccess) return e;
   if (per_cu < 1 || cus < 1) return hipErrorInvalidConfiguration;
 
-  // Per stage, the largest K-split (more, shorter waves) whose tiles still fit
-  // one per compute unit; if none fits, the smallest.
   StageTable tab;
   std::memset(&tab, 0, sizeof(tab));
   tab.count = count;
-  tab.nstages = nstages;
   tab.M = M;
-  int64_t total = 0, widest = 1;
+  // Tagged outputs: only for problems that a later one reads.
+  bool consumed[kMaxGroup] = {};
+  for (int i = 0; i < count; ++i)
+    if (src[i] >= 0) consumed[src[i]] = true;
+  size_t off = kStageHeaderBytes;
+  for (int i = 0; i < count; ++i) {
+    tab.src[i] = src[i];
+    tab.tag_off[i] = consumed[i] ? (uint32_t)(off / 256) : kNoTag;
+    off += align256((size_t)((int64_t)M * problems_host[i].N) * 8);
+  }
+  // Per stage, the largest K-split (more, shorter waves) whose tiles still fit
+  // the resident grid at once; if none fits, the smallest.
+  const int64_t resident = std::min<int64_t>((int64_t)per_cu * cus, kMaxStageGrid);
+  int64_t total = 0;
   int first = 0;
   for (int s = 0; s < nstages; ++s) {
     const int last = stage_end[s];
@@ -372,27 +443,25 @@ hipError_t launch_stages(const bitnet_problem *problems_dev, const bitnet_proble
       for (int i = first; i < last; ++i)
         tiles += stage_tiles(problems_host[i].N, problem_split(problems_host[i].K, S));
       chosen = S;
-      if (tiles <= cus) break;
+      if (tiles <= resident) break;
     }
-    int64_t tiles = 0;
     for (int i = first; i < last; ++i) {
       const int Si = problem_split(problems_host[i].K, chosen);
       tab.split[i] = (uint8_t)Si;
-      tiles += stage_tiles(problems_host[i].N, Si);
       total += stage_tiles(problems_host[i].N, Si);
       if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
       tab.blk_end[i] = (uint32_t)total;
     }
-    tab.stage_tile[s + 1] = (uint32_t)total;
-    widest = std::max(widest, tiles);
     first = last;
   }
-  const unsigned grid = (unsigned)std::min<int64_t>(
-      std::min<int64_t>((int64_t)per_cu * cus, widest), kMaxStageGrid);
-  // Bound each wait between stages at 200 ms of the wall clock.
+  tab.ntiles = (uint32_t)total;
+  // As many workgroups as can be resident: a workgroup that finishes early
+  // starts its next tile's weight loads while that tile's inputs are made.
+  const unsigned grid = (unsigned)std::min<int64_t>(resident, total);
+  // Bound each wait at 200 ms of the wall clock.
   uint64_t timeout = (uint64_t)std::max(clock_khz, 1) * 200u;
-  zero_words_kernel<<<1, kThreads, 0, stream>>>(sync, kStageFlag0 + (int)grid);
-  void *args[] = {(void *)&problems_dev, (void *)&tab, (void *)&sync, (void *)&timeout};
+  stage_epoch_kernel<<<1, 64, 0, stream>>>(reinterpret_cast<uint32_t *>(ws));
+  void *args[] = {(void *)&problems_dev, (void *)&tab, (void *)&ws, (void *)&timeout};
   return hipLaunchCooperativeKernel((const void *)stages_kernel, dim3(grid), dim3(kThreads), args,
                                     0, stream);
 }
