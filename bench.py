@@ -53,9 +53,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--layers", type=int, default=28)
-    ap.add_argument("--only", choices=("all", "decode", "prefill", "copy", "vendor"), default="all",
+    ap.add_argument("--only", choices=("all", "decode", "prefill", "chain", "copy", "vendor"),
+                    default="all",
                     help="decode: headline only; prefill: one prefill step size (--prefill-m) "
-                         "only; copy: 1 GiB copy probe used to calibrate the byte counters; "
+                         "only; chain: the dependent per-token chain only (graph of grouped "
+                         "launches, and the staged call); copy: 1 GiB copy probe used to calibrate the byte counters; "
                          "vendor: the vendor int8 GEMM (torch._int_mm) on the prefill shapes, "
                          "a reference point for the int8 MFMA rate these shapes allow")
     ap.add_argument("--prefill-m", type=int, default=256)
@@ -212,6 +214,13 @@ def main():
                                 [p.N for p in probs], [p.K for p in probs]) for c in copies]
         return plans, xs, ys
 
+    if args.only == "chain":
+        log("[bench] dependent per-token chain only")
+        res = chain_configs(torch, tb, synth, timer, problems, packed, w_scales, alg_bytes,
+                            decode_plans, dev)
+        print(json.dumps(res), flush=True)
+        return
+
     if args.only == "prefill":
         M = args.prefill_m
         log(f"[bench] prefill M={M} only")
@@ -353,41 +362,11 @@ def prefill_config(torch, tb, timer, problems, packed, w_scales, M, dev):
     return res
 
 
-def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, alg_bytes,
-                  decode_plans, dev):
+def chain_configs(torch, tb, synth, timer, problems, packed, w_scales, alg_bytes, decode_plans,
+                  dev):
+    """One decode token with the layer dependencies kept, two ways."""
     out = {}
-    # Single 1536x1536 GEMV at M=1 (weights seed 0), 600 packed copies rotated
-    # (354 MB) so each launch reads from HBM; this size is launch-latency bound.
-    W, x = synth.single_gemv(seed=0)
-    pk, sc = tb.bitnet_ternarize_pack(torch.from_numpy(W).to(dev))
-    copies = [pk.clone() for _ in range(600)]
-    xd = torch.from_numpy(x).to(dev)
-    y = torch.empty((1, 1536), device=dev)
-    ws = torch.empty(tb.bitnet_matmul_workspace_bytes(1, 1536), dtype=torch.uint8, device=dev)
-    ms = timer.time(lambda i=0: tb.bitnet_ternary_matmul_into(1, 1536, 1536, xd, copies[i % 600],
-                                                              sc, y, ws), 600)
-    out["single_gemv_1536x1536_m1"] = {
-        "us_per_call": round(ms * 1e3, 2),
-        "weight_GBps": round(1536 * 1536 / 4 / (ms * 1e-3) / 1e9, 1),
-        "note": "one 590 KB matrix per launch: launch and latency bound"}
-    del copies
-
-    # One decoder layer (7 projections, M=1) per grouped launch; steps walk the 28
-    # layers so each launch reads fresh weights.
     layers = len(problems) // 7
-    layer_plans = []
-    for l in range(layers):
-        probs = problems[7 * l:7 * l + 7]
-        plans, _, _ = decode_plans(1, probs, copies=(packed,))
-        layer_plans.append(plans[0])
-    ms = timer.time(lambda i=0: layer_plans[i % layers].run(), 4 * layers)
-    lb = sum(p.N * p.K // 4 for p in problems[:7])
-    out["one_layer_m1"] = {"us_per_layer": round(ms * 1e3, 2),
-                           "weight_GBps": round(lb / (ms * 1e-3) / 1e9, 1),
-                           "frac_of_hbm_peak": round(alg_bytes(1, problems[:7]) /
-                                                     (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
-    del layer_plans
-
     # One token through the decoder with the data dependencies of a layer kept:
     # per layer four grouped launches in order (q,k,v | o | gate,up | down), 112
     # launches per token, captured once in a HIP graph and replayed.  Graph
@@ -469,6 +448,47 @@ def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, a
         "matches_grouped_launches": bool(staged_ok), "wait_timed_out": bool(timed_out),
         "note": "one token, 28 layers x 4 dependent stages, one cooperative launch"}
     del staged, launches, stages, flow_ys, ref
+
+    return out
+
+
+def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, alg_bytes,
+                  decode_plans, dev):
+    out = {}
+    # Single 1536x1536 GEMV at M=1 (weights seed 0), 600 packed copies rotated
+    # (354 MB) so each launch reads from HBM; this size is launch-latency bound.
+    W, x = synth.single_gemv(seed=0)
+    pk, sc = tb.bitnet_ternarize_pack(torch.from_numpy(W).to(dev))
+    copies = [pk.clone() for _ in range(600)]
+    xd = torch.from_numpy(x).to(dev)
+    y = torch.empty((1, 1536), device=dev)
+    ws = torch.empty(tb.bitnet_matmul_workspace_bytes(1, 1536), dtype=torch.uint8, device=dev)
+    ms = timer.time(lambda i=0: tb.bitnet_ternary_matmul_into(1, 1536, 1536, xd, copies[i % 600],
+                                                              sc, y, ws), 600)
+    out["single_gemv_1536x1536_m1"] = {
+        "us_per_call": round(ms * 1e3, 2),
+        "weight_GBps": round(1536 * 1536 / 4 / (ms * 1e-3) / 1e9, 1),
+        "note": "one 590 KB matrix per launch: launch and latency bound"}
+    del copies
+
+    # One decoder layer (7 projections, M=1) per grouped launch; steps walk the 28
+    # layers so each launch reads fresh weights.
+    layers = len(problems) // 7
+    layer_plans = []
+    for l in range(layers):
+        probs = problems[7 * l:7 * l + 7]
+        plans, _, _ = decode_plans(1, probs, copies=(packed,))
+        layer_plans.append(plans[0])
+    ms = timer.time(lambda i=0: layer_plans[i % layers].run(), 4 * layers)
+    lb = sum(p.N * p.K // 4 for p in problems[:7])
+    out["one_layer_m1"] = {"us_per_layer": round(ms * 1e3, 2),
+                           "weight_GBps": round(lb / (ms * 1e-3) / 1e9, 1),
+                           "frac_of_hbm_peak": round(alg_bytes(1, problems[:7]) /
+                                                     (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    del layer_plans
+
+    out.update(chain_configs(torch, tb, synth, timer, problems, packed, w_scales, alg_bytes,
+                             decode_plans, dev))
 
     pbytes = sum(p.N * p.K // 4 for p in problems)
     for M in (4, 16):
