@@ -53,11 +53,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--layers", type=int, default=28)
-    ap.add_argument("--only", choices=("all", "decode", "prefill", "chain", "copy", "vendor"),
+    ap.add_argument("--only",
+                    choices=("all", "decode", "prefill", "chain", "lut", "copy", "vendor"),
                     default="all",
                     help="decode: headline only; prefill: one prefill step size (--prefill-m) "
                          "only; chain: the dependent per-token chain only (graph of grouped "
-                         "launches, and the staged call); copy: 1 GiB copy probe used to calibrate the byte counters; "
+                         "launches, and the staged call); lut: the lookup-table variant of "
+                         "the M=1 sweep only; copy: 1 GiB copy probe used to calibrate the byte counters; "
                          "vendor: the vendor int8 GEMM (torch._int_mm) on the prefill shapes, "
                          "a reference point for the int8 MFMA rate these shapes allow")
     ap.add_argument("--prefill-m", type=int, default=256)
@@ -218,6 +220,13 @@ def main():
         log("[bench] dependent per-token chain only")
         res = chain_configs(torch, tb, synth, timer, problems, packed, w_scales, alg_bytes,
                             decode_plans, dev)
+        print(json.dumps(res), flush=True)
+        return
+
+    if args.only == "lut":
+        log("[bench] lookup-table decode sweep only")
+        res = lut_config(torch, tb, synth, timer, problems, packed, copy_b, w_scales, alg_bytes,
+                         decode_plans, dev, steps=args.steps)
         print(json.dumps(res), flush=True)
         return
 
@@ -452,6 +461,31 @@ def chain_configs(torch, tb, synth, timer, problems, packed, w_scales, alg_bytes
     return out
 
 
+def lut_config(torch, tb, synth, timer, problems, packed, copy_b, w_scales, alg_bytes,
+               decode_plans, dev, steps=200):
+    """The lookup-table variant over the M=1 decode sweep, timed like the headline
+    (two packed copies alternate), with its outputs compared to the grouped
+    call's on the same inputs."""
+    xs_host = [synth.problem_activations(p, 1) for p in problems]
+    xs = [torch.from_numpy(x).to(dev) for x in xs_host]
+    ys = [torch.empty((1, p.N), dtype=torch.float32, device=dev) for p in problems]
+    Ns, Ks = [p.N for p in problems], [p.K for p in problems]
+    plans = [tb.LutPlan(xs, c, w_scales, ys, Ns, Ks) for c in (packed, copy_b)]
+    ms = timer.time(lambda i=0: plans[i % 2].run(), steps, warmup=20)
+    ref_plans, _, ref_ys = decode_plans(1, xs_host=xs_host, copies=(packed,))
+    plans[0].run()
+    ref_plans[0].run()
+    torch.cuda.synchronize()
+    same = all(torch.equal(a, b) for a, b in zip(ys, ref_ys))
+    pbytes = sum(p.N * p.K // 4 for p in problems)
+    return {"us_per_step": round(ms * 1e3, 2),
+            "weight_GBps": round(pbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(alg_bytes(1, problems) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                      4),
+            "outputs_equal_grouped_call": bool(same),
+            "kernel": "lut_gemv_grouped_kernel (16-entry tables per pair of codes in LDS)"}
+
+
 def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, alg_bytes,
                   decode_plans, dev):
     out = {}
@@ -491,6 +525,8 @@ def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, a
                              decode_plans, dev))
 
     pbytes = sum(p.N * p.K // 4 for p in problems)
+    out["decode_sweep_m1_lut"] = lut_config(torch, tb, synth, timer, problems, packed, copy_b,
+                                            w_scales, alg_bytes, decode_plans, dev)
     for M in (4, 16):
         plans, _, _ = decode_plans(M)
         ms = timer.time(lambda i=0: plans[i % 2].run(), 100)

@@ -186,6 +186,25 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
                                             void *stream);
 
 /* ------------------------------------------------------------------------
+ * Lookup-table variant of the single-row decode, for comparison with the
+ * unpack + matrix-core path.  bitnet.cpp's kernels use the lookup-table method
+ * of T-MAC (thetesserapress, "Microsoft's BitNet Adds 1-Bit Embeddings...",
+ * the paragraphs on the repo's dependencies and on platform support): each
+ * workgroup quantizes the activation row, tabulates the 16 signed sums that a
+ * 4-bit pair of packed codes can select, and adds one table entry per pair.
+ * The int32 sums, and so the outputs, equal the grouped call's at M = 1
+ * (exactly rounded).
+ *
+ * problems      as for the grouped call, with M = 1 (x is [1, K]);
+ *               1 <= K <= 16384, K % 128 == 0.
+ * No workspace; one launch.  Same status codes as the grouped call.
+ * ------------------------------------------------------------------------ */
+bitnet_status bitnet_ternary_matmul_lut_grouped(const bitnet_problem *problems_dev,
+                                                int32_t count,
+                                                const bitnet_problem *problems_host,
+                                                void *stream);
+
+/* ------------------------------------------------------------------------
  * Dependent decode stages in one launch.  The decoder reads all of its
  * weights for every token (blog "The Paper Says ARM Support...", section
  * "What the model is trying to do"), and its projections depend on each

@@ -43,7 +43,7 @@ EXPORTS = (
     "bitnet_ternarize_pack", "bitnet_quant_act", "bitnet_matmul_workspace_bytes",
     "bitnet_ternary_matmul", "bitnet_ternary_matmul_q8", "bitnet_grouped_workspace_bytes",
     "bitnet_ternary_matmul_grouped", "bitnet_stages_workspace_bytes",
-    "bitnet_ternary_matmul_stages",
+    "bitnet_ternary_matmul_stages", "bitnet_ternary_matmul_lut_grouped",
 )
 
 _lib = None
@@ -84,6 +84,8 @@ def lib():
         L.bitnet_stages_workspace_bytes.restype = _sz
         L.bitnet_ternary_matmul_stages.argtypes = [_i64, _p, _i32, _p, _i32, _p, _p, _sz, _p]
         L.bitnet_ternary_matmul_stages.restype = _i32
+        L.bitnet_ternary_matmul_lut_grouped.argtypes = [_p, _i32, _p, _p]
+        L.bitnet_ternary_matmul_lut_grouped.restype = _i32
         _lib = L
     return _lib
 
@@ -262,6 +264,34 @@ def bitnet_ternary_matmul_grouped(M, problems_dev, count, problems_host, workspa
                                                _c.byref(problems_host), _ptr(workspace),
                                                ws_bytes, _stream(stream)),
            "bitnet_ternary_matmul_grouped")
+
+
+def bitnet_ternary_matmul_lut_grouped(problems_dev, count, problems_host, stream=None) -> None:
+    _check(lib().bitnet_ternary_matmul_lut_grouped(_ptr(problems_dev), count,
+                                                   _c.byref(problems_host), _stream(stream)),
+           "bitnet_ternary_matmul_lut_grouped")
+
+
+class LutPlan:
+    """Independent single-row projections run by the lookup-table kernel in one
+    launch (the comparison variant of the grouped decode call at M = 1)."""
+
+    def __init__(self, xs, packeds, w_scales, ys, Ns, Ks, device=None):
+        count = len(xs)
+        if not 1 <= count <= BITNET_MAX_GROUP:
+            raise ValueError(f"group size must be 1..{BITNET_MAX_GROUP}")
+        arr = (bitnet_problem * count)()
+        for i in range(count):
+            arr[i] = bitnet_problem(xs[i].data_ptr(), packeds[i].data_ptr(),
+                                    w_scales[i].data_ptr(), ys[i].data_ptr(), int(Ns[i]),
+                                    int(Ks[i]))
+        self._keep = (list(xs), list(packeds), list(w_scales), list(ys))
+        self.host, self.count = arr, count
+        dev = device if device is not None else xs[0].device
+        self.dev = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8).to(dev)
+
+    def run(self, stream=None) -> None:
+        bitnet_ternary_matmul_lut_grouped(self.dev, self.count, self.host, stream)
 
 
 def bitnet_stages_workspace_bytes(M: int, problems_host, count: int) -> int:

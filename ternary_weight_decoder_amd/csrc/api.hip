@@ -275,6 +275,40 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
   return from_hip(launch_gemm_grouped(problems_dev, tab, ws, hs));
 }
 
+bitnet_status bitnet_ternary_matmul_lut_grouped(const bitnet_problem *problems_dev,
+                                                int32_t count,
+                                                const bitnet_problem *problems_host,
+                                                void *stream) {
+  if (!problems_dev || !problems_host) return BITNET_ERR_NULL;
+  if (count < 1 || count > kMaxGroup) return BITNET_ERR_SHAPE;
+  if (!aligned(problems_dev, 8)) return BITNET_ERR_ALIGN;
+  for (int32_t i = 0; i < count; ++i) {
+    bitnet_status st = check_problem(1, problems_host[i]);
+    if (st != BITNET_OK) return st;
+    if (problems_host[i].K > kLutMaxK) return BITNET_ERR_SHAPE;
+  }
+  bitnet_status st = device_check();
+  if (st != BITNET_OK) return st;
+  // Longest K first, as in the grouped call.
+  int32_t idx[kMaxGroup];
+  for (int32_t i = 0; i < count; ++i) idx[i] = i;
+  std::stable_sort(idx, idx + count, [&](int32_t a, int32_t b) {
+    return problems_host[a].K > problems_host[b].K;
+  });
+  GroupTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  tab.count = count;
+  tab.M = 1;
+  uint64_t total = 0;
+  for (int32_t s = 0; s < count; ++s) {
+    total += (uint64_t)lut_blocks(problems_host[idx[s]].N);
+    if (total >= ((uint64_t)1 << 31)) return BITNET_ERR_SHAPE;
+    tab.blk_end[s] = (uint32_t)total;
+    tab.order[s] = (uint16_t)idx[s];
+  }
+  return from_hip(launch_lut_grouped(problems_dev, tab, as_stream(stream)));
+}
+
 size_t bitnet_stages_workspace_bytes(int64_t M, const bitnet_problem *problems_host,
                                      int32_t count) {
   if (!problems_host || count < 1 || count > kMaxGroup || M < 1 || M > kGemvMaxM) return 0;

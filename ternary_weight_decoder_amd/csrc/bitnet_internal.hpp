@@ -154,6 +154,12 @@ hipError_t launch_stages(const bitnet_problem *problems_dev, const bitnet_proble
                          int count, const int32_t *stage_end, int nstages, int M,
                          const int16_t *src, uint8_t *ws, hipStream_t stream);
 
+// lut.hip: lookup-table variant of the single-row decode (M = 1, K <= kLutMaxK).
+constexpr int kLutMaxK = 16384;
+int lut_blocks(int64_t N);
+hipError_t launch_lut_grouped(const bitnet_problem *problems, const GroupTable &tab,
+                              hipStream_t stream);
+
 // gemm.hip  (M > 16)
 hipError_t launch_gemm(int M, int N, int K, const int8_t *xq_perm, const float *x_scale,
                        const int32_t *rowsum, const uint8_t *packed, const float *w_scale,

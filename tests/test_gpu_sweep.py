@@ -65,7 +65,7 @@ def gpu_activations(M, K, seed):
     return x
 
 
-def run_and_check(sweep, M, subset, host_x):
+def run_and_check(sweep, M, subset, host_x, lut=False):
     import torch
     tb = sweep["tb"]
     idx = [i for i, p in enumerate(sweep["problems"]) if subset(p)]
@@ -75,9 +75,9 @@ def run_and_check(sweep, M, subset, host_x):
     else:
         xs = [gpu_activations(M, p.K, 70000 + 7 * p.layer + p.proj) for p in probs]
     ys = [torch.full((M, p.N), float("nan"), device="cuda:0") for p in probs]
-    plan = tb.GroupedPlan(M, xs, [sweep["packed"][i] for i in idx],
-                          [sweep["scales"][i] for i in idx], ys, [p.N for p in probs],
-                          [p.K for p in probs])
+    args = (xs, [sweep["packed"][i] for i in idx], [sweep["scales"][i] for i in idx], ys,
+            [p.N for p in probs], [p.K for p in probs])
+    plan = tb.LutPlan(*args) if lut else tb.GroupedPlan(M, *args)
     plan.run()
     torch.cuda.synchronize()
     rng = np.random.default_rng(M)
@@ -111,6 +111,12 @@ def test_decode_sweep_sampled(sweep, M):
     """The 196-matrix decode sweep (one grouped launch) at M = 1, 4, 16."""
     say(f"[sweep] decode M={M}")
     run_and_check(sweep, M, lambda p: True, host_x=True)
+
+
+def test_lut_decode_sweep_sampled(sweep):
+    """The lookup-table variant over the same 196-matrix sweep at M = 1."""
+    say("[sweep] lookup-table decode M=1")
+    run_and_check(sweep, 1, lambda p: True, host_x=True, lut=True)
 
 
 @pytest.mark.parametrize("M", [32, 64])
