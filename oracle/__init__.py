@@ -62,6 +62,11 @@ def lib():
         L.oracle_dequant.argtypes = [p, f32, p, i64, i64, p]
         L.oracle_ternary_matmul.argtypes = [i64, i64, i64, p, p, f32, p, p, p, p]
         L.oracle_matmul_sampled.argtypes = [i64, i64, p, p, p, f32, p, p, i64, p, p]
+        L.oracle_i8_quant_weights.argtypes = [p, i64, i64, p, p]
+        L.oracle_i8_matmul.argtypes = [p, p, i64, i64, i64, p]
+        L.oracle_i8_linear.argtypes = [i64, i64, i64, p, p, f32, p, ctypes.c_int, p, p, p, p]
+        L.oracle_i8_linear_sampled.argtypes = [i64, i64, p, p, p, f32, p, ctypes.c_int, p, p,
+                                               i64, p, p, p]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -194,3 +199,61 @@ def matmul_sampled(xq: np.ndarray, x_scale: np.ndarray, packed: np.ndarray, w_sc
                                 float(np.float32(w_scale)), _ptr(ms), _ptr(ns), cnt,
                                 _ptr(acc), _ptr(y))
     return acc, y
+
+
+# ---- I8_S: int8 weights x int8 activations --------------------------------
+
+def i8_quant_weights(W: np.ndarray):
+    """fp32 [N,K] -> (q int8 [N,K], w_scale float32): one absmax scale per tensor."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    q = np.empty((N, K), np.int8)
+    s = np.zeros(1, np.float32)
+    lib().oracle_i8_quant_weights(_ptr(W), N, K, _ptr(q), _ptr(s))
+    return q, np.float32(s[0])
+
+
+def i8_matmul(xq: np.ndarray, q: np.ndarray) -> np.ndarray:
+    xq = _c(xq, np.int8)
+    q = _c(q, np.int8)
+    M, K = xq.shape
+    N, K2 = q.shape
+    assert K == K2
+    acc = np.empty((M, N), np.int32)
+    lib().oracle_i8_matmul(_ptr(xq), _ptr(q), M, N, K, _ptr(acc))
+    return acc
+
+
+def i8_linear(x: np.ndarray, q: np.ndarray, w_scale, bias=None, relu: bool = False):
+    """Whole I8_S layer -> dict(y, xq, x_scale, acc)."""
+    x = _c(x, np.float32)
+    q = _c(q, np.int8)
+    M, K = x.shape
+    N = q.shape[0]
+    b = None if bias is None else _c(bias, np.float32)
+    y = np.empty((M, N), np.float32)
+    xq = np.empty((M, K), np.int8)
+    xs = np.empty(M, np.float32)
+    acc = np.empty((M, N), np.int32)
+    lib().oracle_i8_linear(M, N, K, _ptr(x), _ptr(q), float(np.float32(w_scale)),
+                           None if b is None else _ptr(b), int(bool(relu)), _ptr(y), _ptr(xq),
+                           _ptr(xs), _ptr(acc))
+    return {"y": y, "xq": xq, "x_scale": xs, "acc": acc}
+
+
+def i8_linear_sampled(xq, x_scale, q, w_scale, bias, relu, ms, ns):
+    """acc, d = acc * w_scale / x_scale (fp64) and y at the selected (m, n) pairs."""
+    xq = _c(xq, np.int8)
+    xs = _c(x_scale, np.float32)
+    q = _c(q, np.int8)
+    N, K = q.shape
+    ms = _c(ms, np.int64)
+    ns = _c(ns, np.int64)
+    b = None if bias is None else _c(bias, np.float32)
+    acc = np.empty(ms.size, np.int32)
+    d = np.empty(ms.size, np.float64)
+    y = np.empty(ms.size, np.float32)
+    lib().oracle_i8_linear_sampled(N, K, _ptr(xq), _ptr(xs), _ptr(q), float(np.float32(w_scale)),
+                                   None if b is None else _ptr(b), int(bool(relu)), _ptr(ms),
+                                   _ptr(ns), ms.size, _ptr(acc), _ptr(d), _ptr(y))
+    return acc, d, y

@@ -258,3 +258,97 @@ void oracle_matmul_sampled(int64_t N, int64_t K, const int8_t *xq, const float *
         y[i] = (float)((double)acc[i] * (double)w_scale / (double)x_scale[m]);
     }
 }
+
+/* ---------------------------------------------------------------------- */
+/* I8_S: int8 weights x int8 activations (the audio encoders' path)         */
+/* ---------------------------------------------------------------------- */
+/*
+ * The audio tokenizer's encoders run as I8_S: int8 weights and int8
+ * activations, with ReLU in place of GELU (ONNX model card
+ * "multimodalart/VibeVoice-ASR-BitNet-ONNX", Quantization table, row "VAE
+ * encoders"), in fused conv / depthwise conv / matmul+bias+ReLU routines
+ * (aitrends.kr summary, technical-features section).  The pages give no scale
+ * granularity or formula.  Readings used here:
+ *  - one scale per weight tensor, as in I2_S: a = max|W|, s = fl32(a / 127)
+ *    (the dequant multiplier), q = clamp(rint(fl32(W / s)), -127, 127); a
+ *    zero tensor gives s = 0 and q = 0;
+ *  - activations per row exactly as oracle_quant_act;
+ *  - y = relu?(acc * s / x_scale + bias) with acc = sum_k xq * q in int32,
+ *    computed in fp64 and rounded once to fp32; relu(v) = v > 0 ? v : 0.
+ */
+
+void oracle_i8_quant_weights(const float *W, int64_t N, int64_t K, int8_t *q, float *w_scale) {
+    float a = 0.0f;
+    for (int64_t i = 0; i < N * K; ++i) {
+        float v = fabsf(W[i]);
+        if (v > a) a = v;
+    }
+    if (a == 0.0f) {
+        memset(q, 0, (size_t)(N * K));
+        *w_scale = 0.0f;
+        return;
+    }
+    float s = a / 127.0f;                 /* fp32, correctly rounded */
+    *w_scale = s;
+    for (int64_t i = 0; i < N * K; ++i) {
+        float t = rintf(W[i] / s);        /* fp32 quotient, half to even */
+        if (t > 127.0f) t = 127.0f;
+        if (t < -127.0f) t = -127.0f;
+        q[i] = (int8_t)t;
+    }
+}
+
+/* acc[m,n] = sum_k xq[m,k] * q[n,k], exactly (int64, stored as int32). */
+void oracle_i8_matmul(const int8_t *xq, const int8_t *q, int64_t M, int64_t N, int64_t K,
+                      int32_t *acc) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t s = 0;
+            for (int64_t k = 0; k < K; ++k) s += (int64_t)xq[m * K + k] * (int64_t)q[n * K + k];
+            acc[m * N + n] = (int32_t)s;
+        }
+}
+
+/* The whole I8_S linear layer.  bias may be NULL (no bias); relu != 0 applies
+ * ReLU.  xq_out / x_scale_out / acc_out may be NULL. */
+void oracle_i8_linear(int64_t M, int64_t N, int64_t K, const float *x, const int8_t *q,
+                      float w_scale, const float *bias, int relu, float *y, int8_t *xq_out,
+                      float *x_scale_out, int32_t *acc_out) {
+    int8_t *xq = (int8_t *)malloc((size_t)(M * K));
+    float *xs = (float *)malloc(sizeof(float) * (size_t)M);
+    int32_t *acc = (int32_t *)malloc(sizeof(int32_t) * (size_t)(M * N));
+    oracle_quant_act(x, M, K, xq, xs);
+    oracle_i8_matmul(xq, q, M, N, K, acc);
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double v = (double)acc[m * N + n] * (double)w_scale / (double)xs[m];
+            if (bias) v += (double)bias[n];
+            if (relu && !(v > 0.0)) v = 0.0;
+            y[m * N + n] = (float)v;
+        }
+    if (xq_out) memcpy(xq_out, xq, (size_t)(M * K));
+    if (x_scale_out) memcpy(x_scale_out, xs, sizeof(float) * (size_t)M);
+    if (acc_out) memcpy(acc_out, acc, sizeof(int32_t) * (size_t)(M * N));
+    free(xq); free(xs); free(acc);
+}
+
+/* Selected outputs of the I8_S linear layer from the oracle's own quantized
+ * rows: for each pair (ms[i], ns[i]), acc[i] and the fp64 value before ReLU
+ * and bias (d[i] = acc * w_scale / x_scale) and the output y[i]. */
+void oracle_i8_linear_sampled(int64_t N, int64_t K, const int8_t *xq, const float *x_scale,
+                              const int8_t *q, float w_scale, const float *bias, int relu,
+                              const int64_t *ms, const int64_t *ns, int64_t count,
+                              int32_t *acc, double *d, float *y) {
+    (void)N;   /* q is [N, K]; only the selected rows are read */
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t m = ms[i], n = ns[i], s = 0;
+        for (int64_t k = 0; k < K; ++k) s += (int64_t)xq[m * K + k] * (int64_t)q[n * K + k];
+        acc[i] = (int32_t)s;
+        d[i] = (double)acc[i] * (double)w_scale / (double)x_scale[m];
+        double v = d[i] + (bias ? (double)bias[n] : 0.0);
+        if (relu && !(v > 0.0)) v = 0.0;
+        y[i] = (float)v;
+    }
+}
