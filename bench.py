@@ -54,12 +54,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--layers", type=int, default=28)
     ap.add_argument("--only",
-                    choices=("all", "decode", "prefill", "chain", "lut", "copy", "vendor"),
+                    choices=("all", "decode", "prefill", "chain", "lut", "i8", "copy", "vendor"),
                     default="all",
                     help="decode: headline only; prefill: one prefill step size (--prefill-m) "
                          "only; chain: the dependent per-token chain only (graph of grouped "
                          "launches, and the staged call); lut: the lookup-table variant of "
-                         "the M=1 sweep only; copy: 1 GiB copy probe used to calibrate the byte counters; "
+                         "the M=1 sweep only; i8: the int8 x int8 encoder layers only; copy: 1 GiB copy probe used to calibrate the byte counters; "
                          "vendor: the vendor int8 GEMM (torch._int_mm) on the prefill shapes, "
                          "a reference point for the int8 MFMA rate these shapes allow")
     ap.add_argument("--prefill-m", type=int, default=256)
@@ -172,6 +172,10 @@ def main():
     tb.lib()
     stream = torch.cuda.current_stream()
     timer = Timer(torch, stream)
+    if args.only == "i8":
+        log("[bench] I8_S encoder layers only")
+        print(json.dumps(i8_configs(torch, tb, synth, timer, dev, steps=args.steps)), flush=True)
+        return
 
     problems = synth.sweep_problems(args.layers)
     n_mat = len(problems)
@@ -461,6 +465,36 @@ def chain_configs(torch, tb, synth, timer, problems, packed, w_scales, alg_bytes
     return out
 
 
+def i8_configs(torch, tb, synth, timer, dev, steps=100):
+    """The I8_S encoder layers (int8 weights x int8 activations, fused bias and
+    ReLU): one call = the row quantization launch + the int8 GEMM launch.  Four
+    (x, y) buffer sets rotate so each call reads and writes HBM, not the MALL."""
+    out = {}
+    for name in sorted(synth.I8_LAYERS):
+        M, K, N, relu = synth.I8_LAYERS[name]
+        x, W, b = synth.i8_layer_inputs(name)
+        q, s = tb.bitnet_i8_quant_weights(torch.from_numpy(W).to(dev))
+        bd = torch.from_numpy(b).to(dev)
+        x0 = torch.from_numpy(x).to(dev)
+        xs = [x0] + [x0.clone() for _ in range(3)]
+        ys = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(4)]
+        ws = torch.empty(tb.bitnet_i8_linear_workspace_bytes(M, K), dtype=torch.uint8,
+                         device=dev)
+        ms = timer.time(lambda i=0: tb.bitnet_i8_linear_into(M, N, K, xs[i % 4], q, s, bd, relu,
+                                                             ys[i % 4], ws), steps, warmup=10)
+        moved = M * K * 4 + N * K + N * 4 + M * N * 4
+        out[f"i8_linear_{name}"] = {
+            "shape": {"M": M, "K": K, "N": N, "bias": True, "relu": relu},
+            "us_per_call": round(ms * 1e3, 2),
+            "GBps_moved": round(moved / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "int8_TOPS": round(2 * M * N * K / (ms * 1e-3) / 1e12, 1),
+            "bytes_moved": moved,
+            "step": "row quantization launch + int8 MFMA GEMM launch (bias, ReLU in epilogue)"}
+        del xs, ys, ws
+    return out
+
+
 def lut_config(torch, tb, synth, timer, problems, packed, copy_b, w_scales, alg_bytes,
                decode_plans, dev, steps=200):
     """The lookup-table variant over the M=1 decode sweep, timed like the headline
@@ -525,6 +559,7 @@ def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, a
                              decode_plans, dev))
 
     pbytes = sum(p.N * p.K // 4 for p in problems)
+    out.update(i8_configs(torch, tb, synth, timer, dev))
     out["decode_sweep_m1_lut"] = lut_config(torch, tb, synth, timer, problems, packed, copy_b,
                                             w_scales, alg_bytes, decode_plans, dev)
     for M in (4, 16):

@@ -186,6 +186,46 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
                                             void *stream);
 
 /* ------------------------------------------------------------------------
+ * I8_S: int8 weights x int8 activations, the audio encoders' linear layers.
+ * The encoders run with int8 weights and activations and ReLU in place of
+ * GELU (ONNX model card "multimodalart/VibeVoice-ASR-BitNet-ONNX",
+ * Quantization table, row "VAE encoders"), in fused matmul + bias + ReLU
+ * routines (aitrends.kr summary, technical-features section).  The pages give
+ * no scale granularity; this library uses one absmax scale per weight tensor
+ * (as I2_S has one scale per tensor) and the per-row activation quantization
+ * of bitnet_quant_act.
+ *
+ * bitnet_i8_quant_weights: W fp32 [N,K] row-major -> q int8 [N,K] and the
+ *   device scalar w_scale = fl32(max|W| / 127); q = clamp(rint(fl32(W /
+ *   w_scale)), -127, 127), half to even; a zero tensor gives w_scale 0 and
+ *   q 0.  Bit-exact.  K >= 64, K % 64 == 0; W, q 16-byte aligned; workspace
+ *   bitnet_i8_quant_workspace_bytes() bytes, 256-byte aligned (scratch).
+ *   Three small launches.
+ *
+ * bitnet_i8_linear: y[m,n] = relu?(acc[m,n] * w_scale / x_scale[m] + bias[n])
+ *   with xq, x_scale the per-row quantization of x (as bitnet_quant_act) and
+ *   acc = sum_k xq[m,k] * q[n,k] in int32 (bit-exact).  The epilogue is fp32:
+ *   fl32(fl32(acc) * fl32(w_scale / x_scale)) + bias, then max(., 0) when
+ *   relu != 0; its error is below 4 * 2^-24 * (|acc * w_scale / x_scale| +
+ *   |bias|).  x fp32 [M,K], q int8 [N,K] (16-byte aligned), bias fp32 [N] or
+ *   NULL, y fp32 [M,N]; acc_out int32 [M,N] or NULL.  K >= 64, K % 64 == 0.
+ *   workspace: bitnet_i8_linear_workspace_bytes(M, K) bytes, 256-byte
+ *   aligned (the int8 rows and their scales).  Two launches.
+ * ------------------------------------------------------------------------ */
+size_t bitnet_i8_quant_workspace_bytes(void);
+
+bitnet_status bitnet_i8_quant_weights(const float *W, int64_t N, int64_t K, int8_t *q,
+                                      float *w_scale, void *workspace, size_t workspace_bytes,
+                                      void *stream);
+
+size_t bitnet_i8_linear_workspace_bytes(int64_t M, int64_t K);
+
+bitnet_status bitnet_i8_linear(int64_t M, int64_t N, int64_t K, const float *x, const int8_t *q,
+                               const float *w_scale, const float *bias, int32_t relu, float *y,
+                               void *workspace, size_t workspace_bytes, int32_t *acc_out,
+                               void *stream);
+
+/* ------------------------------------------------------------------------
  * Lookup-table variant of the single-row decode, for comparison with the
  * unpack + matrix-core path.  bitnet.cpp's kernels use the lookup-table method
  * of T-MAC (thetesserapress, "Microsoft's BitNet Adds 1-Bit Embeddings...",

@@ -44,6 +44,8 @@ EXPORTS = (
     "bitnet_ternary_matmul", "bitnet_ternary_matmul_q8", "bitnet_grouped_workspace_bytes",
     "bitnet_ternary_matmul_grouped", "bitnet_stages_workspace_bytes",
     "bitnet_ternary_matmul_stages", "bitnet_ternary_matmul_lut_grouped",
+    "bitnet_i8_quant_workspace_bytes", "bitnet_i8_quant_weights",
+    "bitnet_i8_linear_workspace_bytes", "bitnet_i8_linear",
 )
 
 _lib = None
@@ -86,6 +88,15 @@ def lib():
         L.bitnet_ternary_matmul_stages.restype = _i32
         L.bitnet_ternary_matmul_lut_grouped.argtypes = [_p, _i32, _p, _p]
         L.bitnet_ternary_matmul_lut_grouped.restype = _i32
+        L.bitnet_i8_quant_workspace_bytes.argtypes = []
+        L.bitnet_i8_quant_workspace_bytes.restype = _sz
+        L.bitnet_i8_quant_weights.argtypes = [_p, _i64, _i64, _p, _p, _p, _sz, _p]
+        L.bitnet_i8_quant_weights.restype = _i32
+        L.bitnet_i8_linear_workspace_bytes.argtypes = [_i64, _i64]
+        L.bitnet_i8_linear_workspace_bytes.restype = _sz
+        L.bitnet_i8_linear.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p, _sz, _p,
+                                       _p]
+        L.bitnet_i8_linear.restype = _i32
         _lib = L
     return _lib
 
@@ -264,6 +275,52 @@ def bitnet_ternary_matmul_grouped(M, problems_dev, count, problems_host, workspa
                                                _c.byref(problems_host), _ptr(workspace),
                                                ws_bytes, _stream(stream)),
            "bitnet_ternary_matmul_grouped")
+
+
+def bitnet_i8_quant_weights_into(W, N, K, q, w_scale, workspace, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().bitnet_i8_quant_weights(_ptr(W), N, K, _ptr(q), _ptr(w_scale), _ptr(workspace),
+                                         ws_bytes, _stream(stream)),
+           "bitnet_i8_quant_weights")
+
+
+def bitnet_i8_quant_weights(W: torch.Tensor, stream=None):
+    """fp32 W [N,K] -> (q int8 [N,K], w_scale fp32 [1]) on W's device (I8_S)."""
+    _dev(W, torch.float32, "W")
+    N, K = W.shape
+    q = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    w_scale = torch.empty(1, dtype=torch.float32, device=W.device)
+    ws = torch.empty(int(lib().bitnet_i8_quant_workspace_bytes()), dtype=torch.uint8,
+                     device=W.device)
+    bitnet_i8_quant_weights_into(W, N, K, q, w_scale, ws, stream)
+    return q, w_scale
+
+
+def bitnet_i8_linear_workspace_bytes(M: int, K: int) -> int:
+    return int(lib().bitnet_i8_linear_workspace_bytes(M, K))
+
+
+def bitnet_i8_linear_into(M, N, K, x, q, w_scale, bias, relu, y, workspace, acc_out=None,
+                          stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().bitnet_i8_linear(M, N, K, _ptr(x), _ptr(q), _ptr(w_scale), _ptr(bias),
+                                  int(bool(relu)), _ptr(y), _ptr(workspace), ws_bytes,
+                                  _ptr(acc_out), _stream(stream)),
+           "bitnet_i8_linear")
+
+
+def bitnet_i8_linear(x: torch.Tensor, q: torch.Tensor, w_scale: torch.Tensor, bias=None,
+                     relu: bool = False, return_acc: bool = False, stream=None):
+    """I8_S layer: fp32 x [M,K], int8 q [N,K] -> fp32 y [M,N] (and int32 acc)."""
+    _dev(x, torch.float32, "x")
+    _dev(q, torch.int8, "q")
+    M, K = x.shape
+    N = q.shape[0]
+    y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    ws = torch.empty(bitnet_i8_linear_workspace_bytes(M, K), dtype=torch.uint8, device=x.device)
+    acc = torch.empty((M, N), dtype=torch.int32, device=x.device) if return_acc else None
+    bitnet_i8_linear_into(M, N, K, x, q, w_scale, bias, relu, y, ws, acc, stream)
+    return (y, acc) if return_acc else y
 
 
 def bitnet_ternary_matmul_lut_grouped(problems_dev, count, problems_host, stream=None) -> None:

@@ -275,6 +275,63 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
   return from_hip(launch_gemm_grouped(problems_dev, tab, ws, hs));
 }
 
+// I8_S shapes: K a multiple of 64 (one GEMM step), the same size limits as the
+// ternary path.
+static bool i8_shape_ok(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 64 || K % 64 != 0) return false;
+  if (M >= kLimit || N >= kLimit || K >= kLimit) return false;
+  if (M * K >= kLimit || N * K >= kLimit || M * N >= kLimit) return false;
+  if ((M + 128) * N * 4 >= kLimit) return false;
+  return true;
+}
+
+size_t bitnet_i8_quant_workspace_bytes(void) { return 256; }
+
+bitnet_status bitnet_i8_quant_weights(const float *W, int64_t N, int64_t K, int8_t *q,
+                                      float *w_scale, void *workspace, size_t workspace_bytes,
+                                      void *stream) {
+  if (!W || !q || !w_scale) return BITNET_ERR_NULL;
+  if (!i8_shape_ok(1, N, K)) return BITNET_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(q, 16) || !aligned(w_scale, 4)) return BITNET_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bitnet_i8_quant_workspace_bytes())
+    return BITNET_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BITNET_ERR_ALIGN;
+  bitnet_status st = device_check();
+  if (st != BITNET_OK) return st;
+  return from_hip(launch_i8_quant_weights(W, N, K, q, w_scale,
+                                          reinterpret_cast<uint32_t *>(workspace),
+                                          as_stream(stream)));
+}
+
+size_t bitnet_i8_linear_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 1 || K < 1) return 0;
+  return align256((size_t)(M * K)) + align256((size_t)M * 4);
+}
+
+bitnet_status bitnet_i8_linear(int64_t M, int64_t N, int64_t K, const float *x, const int8_t *q,
+                               const float *w_scale, const float *bias, int32_t relu, float *y,
+                               void *workspace, size_t workspace_bytes, int32_t *acc_out,
+                               void *stream) {
+  if (!x || !q || !w_scale || !y) return BITNET_ERR_NULL;
+  if (!i8_shape_ok(M, N, K)) return BITNET_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(w_scale, 4) || !aligned(y, 4) ||
+      (bias && !aligned(bias, 4)) || (acc_out && !aligned(acc_out, 4)))
+    return BITNET_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bitnet_i8_linear_workspace_bytes(M, K))
+    return BITNET_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BITNET_ERR_ALIGN;
+  bitnet_status st = device_check();
+  if (st != BITNET_OK) return st;
+  hipStream_t s = as_stream(stream);
+  uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
+  int8_t *xq = reinterpret_cast<int8_t *>(ws);
+  float *xs = reinterpret_cast<float *>(ws + align256((size_t)(M * K)));
+  st = from_hip(launch_quant_rows(x, (int)M, (int)K, xq, nullptr, xs, nullptr, nullptr, s));
+  if (st != BITNET_OK) return st;
+  return from_hip(launch_i8_gemm((int)M, (int)N, (int)K, xq, xs, q, w_scale, bias,
+                                 relu != 0 ? 1 : 0, y, acc_out, s));
+}
+
 bitnet_status bitnet_ternary_matmul_lut_grouped(const bitnet_problem *problems_dev,
                                                 int32_t count,
                                                 const bitnet_problem *problems_host,

@@ -1,0 +1,314 @@
+// I8_S: int8 weights x int8 activations, the audio encoders' linear layers.
+//
+// The audio tokenizer's encoders run with int8 weights and int8 activations
+// and ReLU in place of GELU (ONNX model card "multimodalart/VibeVoice-ASR-
+// BitNet-ONNX", Quantization table, row "VAE encoders"), in fused routines
+// that combine the matmul with its bias and ReLU (aitrends.kr summary,
+// technical-features section).  Here that is one library call:
+//   - the activation rows are quantized (per-row absmax int8, the same
+//     quantization kernel as the ternary path) into the workspace;
+//   - one GEMM launch contracts them with the int8 weights on
+//     v_mfma_i32_32x32x32_i8 and applies the per-row dequantization factor,
+//     the bias and the ReLU in its epilogue.
+// Weights are quantized once, offline, with one absmax scale per tensor.
+//
+// GEMM.  Workgroup tile 64 (or 128) x 128, 4 waves in a 2 x 2 arrangement,
+// each wave 32 (64) x 64 as blocks of 32 x 32.  K advances 64 inputs per step:
+// the activation tile (BM rows x 64 int8) and the weight tile (128 rows x 64
+// int8) go straight from memory into LDS (buffer_load ... lds), into a ring of
+// three stages issued two steps ahead; rows past M or N load as zeros.  Inside
+// a stage, 16-byte chunk c of tile row r sits at position c ^ ((r / 4) % 4), so
+// the operand reads of 16 consecutive rows hit 16 different bank groups.  Lane
+// (i = lane % 32, h = lane / 32) feeds k-step s of a stage with chunk 2s + h of
+// its A row and of its B row, so the k positions of both operands agree.
+// Tiles are dealt to the eight XCDs by row block (block b runs on XCD b % 8),
+// so the workgroups that read one block of activation rows share one L2.
+#include <algorithm>
+
+#include "bitnet_device.hpp"
+#include "bitnet_internal.hpp"
+
+namespace bitnet {
+namespace {
+
+#ifndef BITNET_I8_RING
+#define BITNET_I8_RING 3
+#endif
+constexpr int kThreads = 256;
+constexpr int kBN = 128;
+constexpr int kKB = 64;                 // inputs per K step
+constexpr int kRing = BITNET_I8_RING;   // LDS stages
+constexpr int kStoreAux = 2;            // outputs are not read again here: non-temporal
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// Tile height BM = 128 or 64: the 4 waves sit 2 x 2, each owning BM/2 rows
+// (BM/64 blocks of 32) and 64 columns (2 blocks of 32).
+template <int BM>
+struct I8Shared {
+  __attribute__((aligned(16))) int8_t a[kRing][BM * kKB];
+  __attribute__((aligned(16))) int8_t b[kRing][kBN * kKB];
+  float factor[BM];
+};
+
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+
+// s_waitcnt immediate: at most n vector-memory operations outstanding and no
+// LDS operation (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8).
+constexpr int vmcnt_lgkm0_wait(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4); }
+
+struct I8Params {
+  const int8_t *xq;        // [M][K] natural order
+  const float *x_scale;    // [M]
+  const int8_t *q;         // [N][K]
+  const float *w_scale;    // device scalar
+  const float *bias;       // [N] or null
+  float *y;                // [M][N]
+  int32_t *acc_out;        // [M][N] or null
+  int M, N, K, relu, MB, NB;
+};
+
+template <int BM>
+__global__ void __launch_bounds__(kThreads) i8_gemm_kernel(I8Params p) {
+  constexpr int RB = BM / 64;            // 32-row blocks per wave
+  constexpr int kDmaA = BM / 64;         // 1 KB activation loads per wave and step
+  constexpr int kDmaPerWave = kDmaA + 2;
+  __shared__ I8Shared<BM> sh;
+  // Block b runs on XCD b % 8: XCD x takes row blocks x, x + 8, ... and every
+  // column block of each.
+  const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
+  const int mb = (j / p.NB) * 8 + xcd, nb = j % p.NB;
+  if (mb >= p.MB) return;
+  const int m0 = mb * BM, n0 = nb * kBN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 31, lh = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int steps = p.K / kKB;
+
+  // DMA: wave w fills activation rows [BM/4 w, BM/4 (w + 1)) and weight rows
+  // [32w, 32w + 32) with 1 KB loads; lane L of a load lands at position L % 4
+  // of tile row r = (first row of the load) + L / 4 and so fetches chunk
+  // (L % 4) ^ swz(r).
+  const uint32_t a_bytes = (uint32_t)((size_t)p.M * p.K);
+  const uint32_t b_bytes = (uint32_t)((size_t)p.N * p.K);
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.xq, a_bytes);
+  const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(p.q, b_bytes);
+  uint32_t a_off[kDmaA], b_off[2];
+#pragma unroll
+  for (int q = 0; q < kDmaA; ++q) {
+    const int r = (BM / 4) * wave + 16 * q + (lane >> 2);
+    const int chunk = (lane & 3) ^ swz(r);
+    a_off[q] = m0 + r < p.M ? (uint32_t)(m0 + r) * p.K + 16 * chunk : a_bytes;
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = 32 * wave + 16 * q + (lane >> 2);
+    const int chunk = (lane & 3) ^ swz(r);
+    b_off[q] = n0 + r < p.N ? (uint32_t)(n0 + r) * p.K + 16 * chunk : b_bytes;
+  }
+  auto issue = [&](int u, int slot) {
+    const bool live = u < steps;
+#pragma unroll
+    for (int q = 0; q < kDmaA; ++q) {
+      const uint32_t ao = live && a_off[q] < a_bytes ? a_off[q] + (uint32_t)u * kKB : a_bytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          a_rsrc, (lds_ptr_t)(&sh.a[slot][((BM / 4) * wave + 16 * q) * kKB]), 16, ao, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t bo = live && b_off[q] < b_bytes ? b_off[q] + (uint32_t)u * kKB : b_bytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          b_rsrc, (lds_ptr_t)(&sh.b[slot][(32 * wave + 16 * q) * kKB]), 16, bo, 0, 0, 0);
+    }
+  };
+
+  // Operand reads: row (32 rb + li) of the wave's half, chunk 2s + lh.
+  uint32_t rd[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) rd[s] = li * kKB + (((2 * s + lh) ^ swz(li)) * 16);
+
+  // Per-row dequantization factors of the tile (rows past M: any finite value).
+  if (tid < BM) {
+    const int row = min(m0 + tid, p.M - 1);
+    sh.factor[tid] = ld_global<float>(p.w_scale) / ld_global<float>(p.x_scale + row);
+  }
+
+#pragma unroll
+  for (int u = 0; u < kRing - 1; ++u) issue(u, u);
+
+  v16i acc[RB][2];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[rb][cb][e] = 0;
+
+  for (int base = 0; base < steps; base += kRing) {
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) {
+      const int u = base + s;
+      // This wave's loads of step u are its oldest outstanding ones (those of
+      // step u + 1 may stay in flight); after the barrier every wave's part of
+      // stage s is in LDS and every wave is done reading the stage that the
+      // next loads overwrite.  Steps past K load zeros and add nothing.
+      // The wait also drains this wave's LDS reads: the loads issued after
+      // the barrier overwrite the stage read one step earlier, and a read
+      // still queued behind the barrier would see the new data.  Nothing is
+      // scheduled across this point, so those reads and the MFMAs that use
+      // them stay on this side.
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_wait((kRing - 2) * kDmaPerWave));
+      __builtin_amdgcn_s_barrier();
+      issue(u + kRing - 1, (s + kRing - 1) % kRing);
+      __builtin_amdgcn_sched_barrier(0);
+      const int8_t *as = sh.a[s] + (wm * (BM / 2)) * kKB;
+      const int8_t *bs = sh.b[s] + (wn * 64) * kKB;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        v4i av[RB], bv[2];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) av[r] = *reinterpret_cast<const v4i *>(as + r * 32 * kKB + rd[ks]);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) bv[r] = *reinterpret_cast<const v4i *>(bs + r * 32 * kKB + rd[ks]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+            acc[rb][cb] =
+                __builtin_amdgcn_mfma_i32_32x32x32_i8(av[rb], bv[cb], acc[rb][cb], 0, 0, 0);
+      }
+    }
+  }
+  // The last ring slots loaded zeros into LDS; let them land before the
+  // workgroup can end and its LDS be handed to another one.
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+
+  // Epilogue: element e of a 32x32 block sits at row 8(e/4) + 4lh + e%4,
+  // column li.  y = relu?(fl32(fl32(acc) * factor) + bias).  Rows past M and
+  // columns past N are aimed beyond the buffers and dropped.
+  const uint32_t y_bytes = (uint32_t)((size_t)p.M * p.N * 4);
+  const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(p.y, y_bytes);
+  const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(p.acc_out, p.acc_out ? y_bytes : 0);
+  float bias[2];
+  uint32_t col_off[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int n = n0 + wn * 64 + cb * 32 + li;
+    bias[cb] = (p.bias && n < p.N) ? ld_global<float>(p.bias + n) : 0.0f;
+    col_off[cb] = n < p.N ? (uint32_t)n * 4u : 0x80000000u;
+  }
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int lrow = wm * (BM / 2) + rb * 32 + 8 * g + 4 * lh + k;
+        const int row = m0 + lrow;
+        const uint32_t row_off = row < p.M ? (uint32_t)row * (uint32_t)p.N * 4u : 0x80000000u;
+        const float f = sh.factor[lrow];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          const int a = acc[rb][cb][4 * g + k];
+          float v = (float)a * f + bias[cb];
+          if (p.relu) v = v > 0.0f ? v : 0.0f;
+          const uint32_t off = (row_off | col_off[cb]) >= 0x80000000u ? y_bytes
+                                                                      : row_off + col_off[cb];
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), y_rsrc, off, 0,
+                                                kStoreAux);
+          if (p.acc_out) __builtin_amdgcn_raw_buffer_store_b32(a, c_rsrc, off, 0, 0);
+        }
+      }
+}
+
+// Weight quantization, one scale per tensor.  Pass 1: max |W| (non-negative
+// floats order like their bit patterns, so an integer atomic max is exact and
+// order-independent).  Pass 2: s = fl32(max / 127), q = clamp(rint(W / s)).
+__global__ void i8_zero_kernel(uint32_t *w) {
+  if (threadIdx.x == 0) w[0] = 0u;
+}
+
+__global__ void __launch_bounds__(kThreads) i8_absmax_kernel(const float *W, int64_t n4,
+                                                             uint32_t *amax) {
+  __shared__ float red[kThreads / 64];
+  const f32x4 *w4 = reinterpret_cast<const f32x4 *>(W);
+  float a = 0.0f;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * kThreads) {
+    const f32x4 v = ld_global<f32x4>(w4 + i);
+    a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+  a = wave_max(a);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    atomicMax(amax, __builtin_bit_cast(uint32_t, m));
+  }
+}
+
+__device__ __forceinline__ int quant_w(float w, float s) {
+  float t = __builtin_rintf(w / s);
+  t = fminf(fmaxf(t, -127.0f), 127.0f);
+  return (int)t;
+}
+
+__global__ void __launch_bounds__(kThreads) i8_quant_weights_kernel(const float *W, int64_t n4,
+                                                                    const uint32_t *amax,
+                                                                    int8_t *q, float *w_scale) {
+  const float a = __builtin_bit_cast(float, ld_global<uint32_t>(amax));
+  const float s = a / 127.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) st_global<float>(w_scale, a == 0.0f ? 0.0f : s);
+  const f32x4 *w4 = reinterpret_cast<const f32x4 *>(W);
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * kThreads) {
+    uint32_t packed = 0;
+    if (a != 0.0f) {
+      const f32x4 v = ld_global<f32x4>(w4 + i);
+      packed = pack4_i8(quant_w(v.x, s), quant_w(v.y, s), quant_w(v.z, s), quant_w(v.w, s));
+    }
+    st_global<uint32_t>(q + 4 * i, packed);
+  }
+}
+
+// 64-row tiles unless 128-row tiles are plentiful: on the encoder layers
+// (1024 and 256 tiles of 128 rows) the shorter tiles, with twice the
+// workgroups and four resident per compute unit, measured faster.
+#ifndef BITNET_I8_TALL_MIN_TILES
+#define BITNET_I8_TALL_MIN_TILES 4096
+#endif
+bool i8_tall_tiles(int M, int N) {
+  const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + kBN - 1) / kBN);
+  return tiles >= BITNET_I8_TALL_MIN_TILES;
+}
+
+}  // namespace
+
+hipError_t launch_i8_quant_weights(const float *W, int64_t N, int64_t K, int8_t *q,
+                                   float *w_scale, uint32_t *amax, hipStream_t stream) {
+  const int64_t n4 = N * K / 4;
+  const int blocks = (int)std::min<int64_t>((n4 + kThreads - 1) / kThreads, 4096);
+  i8_zero_kernel<<<1, 64, 0, stream>>>(amax);
+  i8_absmax_kernel<<<blocks, kThreads, 0, stream>>>(W, n4, amax);
+  i8_quant_weights_kernel<<<blocks, kThreads, 0, stream>>>(W, n4, amax, q, w_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_i8_gemm(int M, int N, int K, const int8_t *xq, const float *x_scale,
+                          const int8_t *q, const float *w_scale, const float *bias, int relu,
+                          float *y, int32_t *acc_out, hipStream_t stream) {
+  I8Params p{xq, x_scale, q, w_scale, bias, y, acc_out, M, N, K, relu ? 1 : 0, 0, 0};
+  p.NB = (N + kBN - 1) / kBN;
+  const bool tall = i8_tall_tiles(M, N);
+  p.MB = (M + (tall ? 127 : 63)) / (tall ? 128 : 64);
+  const int64_t grid = (int64_t)8 * ((p.MB + 7) / 8) * p.NB;
+  if (grid >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if (tall)
+    i8_gemm_kernel<128><<<(unsigned)grid, kThreads, 0, stream>>>(p);
+  else
+    i8_gemm_kernel<64><<<(unsigned)grid, kThreads, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace bitnet

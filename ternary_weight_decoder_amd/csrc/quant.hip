@@ -60,7 +60,8 @@ __device__ __forceinline__ void store_row_meta(const RowOut &o, float s, int sum
   if (o.rowsum) st_global<int>(o.rowsum, sum);
 }
 
-// One wave, one row of K <= kWaveMaxK values (K % 128 == 0).
+// One wave, one row of K <= kWaveMaxK values (K % 4 == 0; the permuted row
+// needs K % 128 == 0).
 __device__ __forceinline__ void quant_row_wave(const float *__restrict__ xr, int K,
                                                const RowOut &o) {
   const int lane = threadIdx.x & 63;
@@ -102,7 +103,8 @@ __device__ __forceinline__ void block_finish(int sum, float s, const RowOut &o, 
   if (threadIdx.x == 0) store_row_meta(o, s, sh.ired[0] + sh.ired[1] + sh.ired[2] + sh.ired[3]);
 }
 
-// One workgroup, one row of any K (K % 128 == 0).  Whole workgroup, uniform.
+// One workgroup, one row of any K (K % 4 == 0; the permuted row needs
+// K % 128 == 0).  Whole workgroup, uniform.
 __device__ __forceinline__ void quant_row_block(const float *__restrict__ xr, int K,
                                                 const RowOut &o, QuantShared &sh) {
   const int tid = threadIdx.x;

@@ -153,3 +153,29 @@ def random_int8(M: int, K: int, seed: int, lo: int = -127, hi: int = 127) -> np.
     """Uniform int8 values in [lo, hi], for tests of the integer contraction."""
     rng = np.random.default_rng(seed)
     return rng.integers(lo, hi + 1, size=(M, K), dtype=np.int16).astype(np.int8)
+
+
+# ---- I8_S audio-encoder layers ----------------------------------------------
+# The pages name the encoders' format (int8 weights and activations, ReLU for
+# GELU, fused matmul + bias + ReLU) and describe a ConvNeXt-style tokenizer
+# whose activations outweigh its weights, but give no layer sizes.  The two
+# layers below are the pointwise pair of one such block over 8192 frames:
+# 512 -> 2048 channels with bias and ReLU, then 2048 -> 512 with bias.  In the
+# first, the fp32 activations (16 MB) outweigh the int8 weights (1 MB) 16:1.
+I8_FRAMES = 8192
+I8_LAYERS = {
+    # name: (M, K, N, relu)
+    "pw1": (I8_FRAMES, 512, 2048, True),
+    "pw2": (I8_FRAMES, 2048, 512, False),
+}
+
+
+def i8_layer_inputs(name: str, seed: int = 70000):
+    """(x [M,K], W [N,K], bias [N]) for one I8_S layer: x as `activations`
+    (N(0,1), 1% of channels x20), W ~ N(0, 0.02^2), bias ~ N(0, 0.1^2)."""
+    M, K, N, _ = I8_LAYERS[name]
+    off = sorted(I8_LAYERS).index(name)
+    x = activations(M, K, seed + 10 * off)
+    W = normal_weights(N, K, seed + 10 * off + 1)
+    bias = np.random.default_rng(seed + 10 * off + 2).standard_normal(N, dtype=np.float32)
+    return x, W, (bias * np.float32(0.1)).astype(np.float32)
