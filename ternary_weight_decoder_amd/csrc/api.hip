@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "bitnet_internal.hpp"
+#include "bitnet_variants.hpp"
 #include "bitnet_tm.h"
 
 using namespace bitnet;

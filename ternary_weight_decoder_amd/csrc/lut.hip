@@ -32,6 +32,7 @@
 
 #include "bitnet_device.hpp"
 #include "bitnet_internal.hpp"
+#include "bitnet_variants.hpp"
 
 namespace bitnet {
 namespace {
