@@ -48,7 +48,9 @@ def build(jobs: int = 8) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    # -z defs: a symbol left undefined (a kernel launch stub that the host
+    # pass did not emit, say) fails the link here instead of the first load.
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

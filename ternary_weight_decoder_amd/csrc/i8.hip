@@ -48,7 +48,7 @@ template <int BM>
 struct I8Shared {
   __attribute__((aligned(16))) int8_t a[kRing][BM * kKB];
   __attribute__((aligned(16))) int8_t b[kRing][kBN * kKB];
-  float factor[BM];
+  __attribute__((aligned(16))) float factor[BM];
 };
 
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
@@ -69,7 +69,27 @@ struct I8Params {
   int M, N, K, relu, MB, NB;
 };
 
-template <int BM>
+// s_waitcnt for step u of the K loop: the loads of the `later` steps issued
+// after it (at most kRing - 2) may stay in flight, no LDS operation may.
+template <int kDmaPerWave>
+__device__ __forceinline__ void wait_for_step(int later) {
+  if (kRing >= 4 && later >= 2)
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_wait(2 * kDmaPerWave));
+  else if (kRing >= 3 && later >= 1)
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_wait(kDmaPerWave));
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_wait(0));
+}
+
+// Output value: relu?(fl32(fl32(acc) * factor) + bias).
+template <bool RELU>
+__device__ __forceinline__ float i8_out(float a, float f, float b) {
+  float v = a * f + b;
+  if (RELU) v = v > 0.0f ? v : 0.0f;
+  return v;
+}
+
+template <int BM, bool RELU>
 __global__ void __launch_bounds__(kThreads) i8_gemm_kernel(I8Params p) {
   constexpr int RB = BM / 64;            // 32-row blocks per wave
   constexpr int kDmaA = BM / 64;         // 1 KB activation loads per wave and step
@@ -107,19 +127,24 @@ __global__ void __launch_bounds__(kThreads) i8_gemm_kernel(I8Params p) {
     const int chunk = (lane & 3) ^ swz(r);
     b_off[q] = n0 + r < p.N ? (uint32_t)(n0 + r) * p.K + 16 * chunk : b_bytes;
   }
+  // The step's K offset goes in the scalar offset; rows past M or N carry a
+  // vector offset at the buffer's end, so they load zeros without a memory
+  // access whatever the step.  Steps past K are never issued.
   auto issue = [&](int u, int slot) {
-    const bool live = u < steps;
+    const uint32_t soff = (uint32_t)u * kKB;
 #pragma unroll
     for (int q = 0; q < kDmaA; ++q) {
-      const uint32_t ao = live && a_off[q] < a_bytes ? a_off[q] + (uint32_t)u * kKB : a_bytes;
+      // (Through a local: a captured array element passed straight to the
+      // builtin keeps this compiler's host pass from emitting the launch stub.)
+      const uint32_t ao = a_off[q];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          a_rsrc, (lds_ptr_t)(&sh.a[slot][((BM / 4) * wave + 16 * q) * kKB]), 16, ao, 0, 0, 0);
+          a_rsrc, (lds_ptr_t)(&sh.a[slot][((BM / 4) * wave + 16 * q) * kKB]), 16, ao, soff, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const uint32_t bo = live && b_off[q] < b_bytes ? b_off[q] + (uint32_t)u * kKB : b_bytes;
+      const uint32_t bo = b_off[q];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          b_rsrc, (lds_ptr_t)(&sh.b[slot][(32 * wave + 16 * q) * kKB]), 16, bo, 0, 0, 0);
+          b_rsrc, (lds_ptr_t)(&sh.b[slot][(32 * wave + 16 * q) * kKB]), 16, bo, soff, 0, 0);
     }
   };
 
@@ -134,8 +159,18 @@ __global__ void __launch_bounds__(kThreads) i8_gemm_kernel(I8Params p) {
     sh.factor[tid] = ld_global<float>(p.w_scale) / ld_global<float>(p.x_scale + row);
   }
 
+  // The bias of the lane's columns, fetched now so that its latency hides
+  // behind the K loop.
+  float bias[2];
 #pragma unroll
-  for (int u = 0; u < kRing - 1; ++u) issue(u, u);
+  for (int cb = 0; cb < 2; ++cb) {
+    const int n = n0 + wn * 64 + cb * 32 + li;
+    bias[cb] = (p.bias && n < p.N) ? ld_global<float>(p.bias + n) : 0.0f;
+  }
+
+#pragma unroll
+  for (int u = 0; u < kRing - 1; ++u)
+    if (u < steps) issue(u, u);
 
   v16i acc[RB][2];
 #pragma unroll
@@ -145,58 +180,77 @@ __global__ void __launch_bounds__(kThreads) i8_gemm_kernel(I8Params p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[rb][cb][e] = 0;
 
-  for (int base = 0; base < steps; base += kRing) {
+  for (int u = 0; u < steps; ++u) {
+    const int s = u % kRing;
+    // Step u's loads are this wave's oldest outstanding ones; after the
+    // barrier every wave's part of stage s is in LDS and every wave is done
+    // reading the stage that the next loads overwrite.  The wait also drains
+    // this wave's LDS reads: the loads issued after the barrier overwrite the
+    // stage read one step earlier, and a read still queued behind the barrier
+    // would see the new data.  Nothing is scheduled across this point, so
+    // those reads and the MFMAs that use them stay on this side.
+    __builtin_amdgcn_sched_barrier(0);
+    wait_for_step<kDmaPerWave>(min(kRing - 2, steps - 1 - u));
+    __builtin_amdgcn_s_barrier();
+    if (u + kRing - 1 < steps) issue(u + kRing - 1, (u + kRing - 1) % kRing);
+    __builtin_amdgcn_sched_barrier(0);
+    const int8_t *as = sh.a[s] + (wm * (BM / 2)) * kKB;
+    const int8_t *bs = sh.b[s] + (wn * 64) * kKB;
 #pragma unroll
-    for (int s = 0; s < kRing; ++s) {
-      const int u = base + s;
-      // This wave's loads of step u are its oldest outstanding ones (those of
-      // step u + 1 may stay in flight); after the barrier every wave's part of
-      // stage s is in LDS and every wave is done reading the stage that the
-      // next loads overwrite.  Steps past K load zeros and add nothing.
-      // The wait also drains this wave's LDS reads: the loads issued after
-      // the barrier overwrite the stage read one step earlier, and a read
-      // still queued behind the barrier would see the new data.  Nothing is
-      // scheduled across this point, so those reads and the MFMAs that use
-      // them stay on this side.
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_wait((kRing - 2) * kDmaPerWave));
-      __builtin_amdgcn_s_barrier();
-      issue(u + kRing - 1, (s + kRing - 1) % kRing);
-      __builtin_amdgcn_sched_barrier(0);
-      const int8_t *as = sh.a[s] + (wm * (BM / 2)) * kKB;
-      const int8_t *bs = sh.b[s] + (wn * 64) * kKB;
+    for (int ks = 0; ks < 2; ++ks) {
+      v4i av[RB], bv[2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        v4i av[RB], bv[2];
+      for (int r = 0; r < RB; ++r) av[r] = *reinterpret_cast<const v4i *>(as + r * 32 * kKB + rd[ks]);
 #pragma unroll
-        for (int r = 0; r < RB; ++r) av[r] = *reinterpret_cast<const v4i *>(as + r * 32 * kKB + rd[ks]);
+      for (int r = 0; r < 2; ++r) bv[r] = *reinterpret_cast<const v4i *>(bs + r * 32 * kKB + rd[ks]);
 #pragma unroll
-        for (int r = 0; r < 2; ++r) bv[r] = *reinterpret_cast<const v4i *>(bs + r * 32 * kKB + rd[ks]);
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb)
-            acc[rb][cb] =
-                __builtin_amdgcn_mfma_i32_32x32x32_i8(av[rb], bv[cb], acc[rb][cb], 0, 0, 0);
-      }
+        for (int cb = 0; cb < 2; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[rb], bv[cb], acc[rb][cb], 0, 0, 0);
     }
   }
-  // The last ring slots loaded zeros into LDS; let them land before the
-  // workgroup can end and its LDS be handed to another one.
-  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
 
   // Epilogue: element e of a 32x32 block sits at row 8(e/4) + 4lh + e%4,
-  // column li.  y = relu?(fl32(fl32(acc) * factor) + bias).  Rows past M and
-  // columns past N are aimed beyond the buffers and dropped.
+  // column li.  y = relu?(fl32(fl32(acc) * factor) + bias).
   const uint32_t y_bytes = (uint32_t)((size_t)p.M * p.N * 4);
   const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(p.y, y_bytes);
   const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(p.acc_out, p.acc_out ? y_bytes : 0);
-  float bias[2];
+  if (m0 + BM <= p.M && n0 + kBN <= p.N) {
+    // Whole tile inside: one vector offset per column block, the row step in
+    // the scalar offset.
+    const uint32_t rstride = (uint32_t)p.N * 4u;
+    uint32_t vo[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+      vo[cb] = (uint32_t)(m0 + wm * (BM / 2) + 4 * lh) * rstride +
+               (uint32_t)(n0 + wn * 64 + cb * 32 + li) * 4u;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 f4 =
+            *reinterpret_cast<const f32x4 *>(&sh.factor[wm * (BM / 2) + rb * 32 + 8 * g + 4 * lh]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t so = (uint32_t)(rb * 32 + 8 * g + k) * rstride;
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) {
+            const int a = acc[rb][cb][4 * g + k];
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, i8_out<RELU>((float)a, f4[k], bias[cb])),
+                                                  y_rsrc, vo[cb], so, kStoreAux);
+            if (p.acc_out) __builtin_amdgcn_raw_buffer_store_b32(a, c_rsrc, vo[cb], so, 0);
+          }
+        }
+      }
+    return;
+  }
+  // Edge tile: rows past M and columns past N are aimed beyond the buffers
+  // and dropped.
   uint32_t col_off[2];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const int n = n0 + wn * 64 + cb * 32 + li;
-    bias[cb] = (p.bias && n < p.N) ? ld_global<float>(p.bias + n) : 0.0f;
     col_off[cb] = n < p.N ? (uint32_t)n * 4u : 0x80000000u;
   }
 #pragma unroll
@@ -212,12 +266,10 @@ __global__ void __launch_bounds__(kThreads) i8_gemm_kernel(I8Params p) {
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
           const int a = acc[rb][cb][4 * g + k];
-          float v = (float)a * f + bias[cb];
-          if (p.relu) v = v > 0.0f ? v : 0.0f;
           const uint32_t off = (row_off | col_off[cb]) >= 0x80000000u ? y_bytes
                                                                       : row_off + col_off[cb];
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), y_rsrc, off, 0,
-                                                kStoreAux);
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, i8_out<RELU>((float)a, f, bias[cb])),
+                                                y_rsrc, off, 0, kStoreAux);
           if (p.acc_out) __builtin_amdgcn_raw_buffer_store_b32(a, c_rsrc, off, 0, 0);
         }
       }
@@ -305,10 +357,14 @@ hipError_t launch_i8_gemm(int M, int N, int K, const int8_t *xq, const float *x_
   p.MB = (M + (tall ? 127 : 63)) / (tall ? 128 : 64);
   const int64_t grid = (int64_t)8 * ((p.MB + 7) / 8) * p.NB;
   if (grid >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  if (tall)
-    i8_gemm_kernel<128><<<(unsigned)grid, kThreads, 0, stream>>>(p);
+  if (tall && relu)
+    i8_gemm_kernel<128, true><<<(unsigned)grid, kThreads, 0, stream>>>(p);
+  else if (tall)
+    i8_gemm_kernel<128, false><<<(unsigned)grid, kThreads, 0, stream>>>(p);
+  else if (relu)
+    i8_gemm_kernel<64, true><<<(unsigned)grid, kThreads, 0, stream>>>(p);
   else
-    i8_gemm_kernel<64><<<(unsigned)grid, kThreads, 0, stream>>>(p);
+    i8_gemm_kernel<64, false><<<(unsigned)grid, kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 
