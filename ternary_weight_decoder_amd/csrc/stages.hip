@@ -27,9 +27,11 @@
 // consumer reads those pairs with device-coherent loads, re-reading the ones
 // whose tag is not yet the current epoch.  A single atomic store carries value
 // and tag together, so no fence, flag or store acknowledgement sits between a
-// producer and its consumers.  A consumer first polls one probe pair (the last
-// one, written by the producer's last tile) so that waiting workgroups do not
-// flood the memory system, then reads everything.  Each workgroup runs its
+// producer and its consumers.  A consumer first polls one probe pair (the
+// first one, written by the producer's first tile) so that waiting workgroups
+// do not flood the memory system, then reads everything and re-reads what is
+// still pending; the producer's tiles finish close together, so the full read
+// mostly overlaps the last of them.  Each workgroup runs its
 // tiles in stage order and the grid is co-resident, so the lowest unfinished
 // tile never waits on an unfinished one.  Every wait is bounded by a
 // wall-clock timeout: a wait that runs out raises the flag in workspace word 1
@@ -126,8 +128,8 @@ __device__ __forceinline__ void stage_load_x(const float *x, const StageIo &io, 
   const uint64_t *xt = io.x_tagged;
   bool expired = ld_agent(&io.flags[1]) != 0;
   uint64_t t0 = wall_clock64();
-  // Probe: poll the last pair (written by the producer's last tile) first.
-  while (!expired && !pair_ok(ld_pair(xt, 4u * total - 1u), io.epoch)) {
+  // Probe: poll the first pair (written by the producer's first tile) first.
+  while (!expired && !pair_ok(ld_pair(xt, 0u), io.epoch)) {
     if (wall_clock64() - t0 > io.timeout) {
       atomicOr(&io.flags[1], 1u);
       expired = true;
