@@ -9,7 +9,11 @@ dequantization, all inside one kernel.  `value` is packed-weight GB/s.  The
 weights (seeded fp32 masters ~N(0, 0.02)) are ternarized and packed on the GPU
 once before timing, as the format ships pre-ternarized weights.  Two copies of
 the 327.5 MB packed set alternate between steps so the reads come from HBM
-rather than the 256 MB last-level cache.
+rather than the 256 MB last-level cache.  Before the warm-up and the timed
+steps the device is settled: a freshly started GPU runs its first seconds of
+work much slower, so untimed batches run until two in a row agree (`settle`).
+`step_stats` times the same launches one by one afterwards (median, minimum,
+interquartile range).
 
 `roofline` describes that decode kernel: algorithmic bytes per launch (packed
 codes + fp32 activations + fp32 outputs + scales) over the launch duration
@@ -17,9 +21,12 @@ timed with HIP events on the launch stream.  `traffic` comes from the counter
 summary in profiles/ when it was taken on the current kernel source.
 
 `configs` reports the other workloads (single 1536x1536 GEMV, one decoder
-layer, the sweep at M = 4 and 16, prefill at M = 256 and 1800, batched decode
-at M = 32 and 64); `cpu_baseline` times the CPU oracle on a bounded sample of
-the headline workload on this host.
+layer, each projection shape alone and grouped over its 28 layers, the launch
+floor, the sweep with all-zero codes against random ones, the dependent
+per-token chain, the I8_S encoder layers, the lookup-table sweep, the sweep at
+M = 4 and 16, prefill at M = 256 and 1800, batched decode at M = 32 and 64);
+`cpu_baseline` times the CPU oracle on a bounded sample of the headline
+workload on this host, and its ternarize + pack step on its own.
 """
 from __future__ import annotations
 
@@ -112,6 +119,46 @@ class Timer:
         e1.record(self.stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps   # ms per step
+
+    def settle(self, fn, batch=100, agree=0.02, min_s=3.0, max_s=30.0):
+        """Untimed work until the device reaches its steady state: batches of
+        `batch` steps until two in a row agree within `agree` (after at least
+        `min_s`, at most `max_s` seconds).  A freshly started GPU runs its
+        first seconds of work much slower (the same decode sweep measured
+        97.5 us per step in the first process on a box and 55.5 us in the
+        next).  Returns the seconds spent and the last two batch times."""
+        t0 = time.perf_counter()
+        prev = first = None
+        while True:
+            ms = self.time(fn, batch, warmup=0)
+            first = ms if first is None else first
+            el = time.perf_counter() - t0
+            if prev is not None and abs(ms - prev) <= agree * prev and el >= min_s:
+                break
+            if el >= max_s:
+                break
+            prev = ms
+        return {"seconds": round(el, 2), "first_batch_us_per_step": round(first * 1e3, 2),
+                "last_batches_us_per_step":
+                [round(prev * 1e3, 2) if prev else None, round(ms * 1e3, 2)]}
+
+    def per_step(self, fn, steps, warmup=3):
+        """Device time of each step on its own (an event pair around every
+        launch): median, minimum and interquartile range in microseconds."""
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(self.stream)
+        for i in range(steps):
+            fn(i)
+            ev[i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        us = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)])
+        q1, med, q3 = np.percentile(us, [25, 50, 75])
+        return {"steps": steps, "median_us": round(float(med), 2), "min_us": round(float(us.min()), 2),
+                "p25_us": round(float(q1), 2), "p75_us": round(float(q3), 2)}
 
 
 def copy_probe(torch):
@@ -251,14 +298,20 @@ def main():
     plans, xs, ys = decode_plans(M, probs=sweep, xs_host=xs_host)
     packed_bytes = sum(p.N * p.K // 4 for p in sweep)
     steps = args.steps
-    log(f"[bench] decode sweep M={M} over {len(sweep)} matrices: warmup {args.warmup}, "
-        f"timed {steps} steps")
+    log(f"[bench] decode sweep M={M} over {len(sweep)} matrices: settling the device, then "
+        f"warmup {args.warmup}, timed {steps} steps")
+    settle = timer.settle(lambda i=0: plans[i % 2].run())
+    log(f"[bench] settled after {settle['seconds']} s "
+        f"(first batch {settle['first_batch_us_per_step']}, last batches "
+        f"{settle['last_batches_us_per_step']} us/step)")
     ms_step = timer.time(lambda i=0: plans[i % 2].run(), steps, warmup=args.warmup)
     weight_gbps = packed_bytes / (ms_step * 1e-3) / 1e9
     bytes_launch = alg_bytes(M, sweep)
     achieved = bytes_launch / (ms_step * 1e-3) / 1e9
     log(f"[bench] decode {ms_step * 1e3:.1f} us/step, weight {weight_gbps:.0f} GB/s, "
         f"all bytes {achieved:.0f} GB/s")
+    # The same launches timed one by one (outside the timed block above).
+    step_stats = timer.per_step(lambda i=0: plans[i % 2].run(), 200)
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -278,12 +331,16 @@ def main():
         import oracle
         cores = oracle.num_threads()
         t_spent, bytes_done, mats, max_rel, packed_equal = 0.0, 0, 0, 0.0, 0
+        t_tern, tern_bytes = 0.0, 0
         plans[0].run()
         torch.cuda.synchronize()
         refs = []
         for i, p in enumerate(sweep):
             W = synth.problem_weights(p)
-            pk_ref, s_ref = oracle.ternarize_pack(W)      # offline step, not timed
+            t0 = time.perf_counter()
+            pk_ref, s_ref = oracle.ternarize_pack(W)      # offline step, timed on its own
+            t_tern += time.perf_counter() - t0
+            tern_bytes += W.nbytes
             refs.append((pk_ref, s_ref))
             t0 = time.perf_counter()
             ref = oracle.ternary_matmul(xs_host[i], pk_ref, s_ref, p.N)
@@ -313,6 +370,10 @@ def main():
                          f"{t_spent:.1f} s of oracle time on {cores} threads; GPU-packed codes "
                          f"equal to the oracle's in {packed_equal}/{mats} matrices; GPU outputs "
                          f"agree to max relative error {max_rel:.2e}",
+               "ternarize_pack": {"value": round(tern_bytes / t_tern / 1e9, 4),
+                                  "unit": "GB/s of fp32 masters", "matrices": mats,
+                                  "seconds": round(t_tern, 2),
+                                  "note": "offline step, outside the decode figure"},
                "single_thread": {"value": round(b1 / t1 / 1e9, 4), "unit": "GB/s",
                                  "sample": "layer 0's 7 projections, M=1, 1 thread"},
                "host_cpu": host_cpu()}
@@ -326,6 +387,8 @@ def main():
         "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 6),
+        "step_stats": step_stats,
+        "settle": settle,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -554,6 +617,58 @@ def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, a
                            "frac_of_hbm_peak": round(alg_bytes(1, problems[:7]) /
                                                      (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
     del layer_plans
+
+    # Each projection shape on its own: single launches walking the 28 layers'
+    # instances (two copies of each, so a launch rarely finds its matrix in
+    # the last-level cache; the small shapes still fit there), and one grouped
+    # launch over the 28 instances.
+    per_shape = {}
+    ws1 = torch.empty(tb.bitnet_matmul_workspace_bytes(1, synth.INTERMEDIATE), dtype=torch.uint8,
+                      device=dev)
+    for j, (name, K, N) in enumerate(synth.PROJECTIONS):
+        idx = [i for i, p in enumerate(problems) if p.proj == j]
+        inst = [(c[i], w_scales[i]) for c in (packed, copy_b) for i in idx]
+        xd = torch.from_numpy(synth.problem_activations(problems[idx[0]], 1)).to(dev)
+        yd = torch.empty((1, N), device=dev)
+        ms1 = timer.time(lambda i=0: tb.bitnet_ternary_matmul_into(
+            1, N, K, xd, inst[i % len(inst)][0], inst[i % len(inst)][1], yd, ws1), 4 * len(inst))
+        plans, _, _ = decode_plans(1, [problems[i] for i in idx])
+        msg = timer.time(lambda i=0: plans[i % 2].run(), 100)
+        b1 = N * K // 4
+        per_shape[name] = {
+            "K": K, "N": N,
+            "single_us_per_call": round(ms1 * 1e3, 2),
+            "single_weight_GBps": round(b1 / (ms1 * 1e-3) / 1e9, 1),
+            "grouped28_us_per_launch": round(msg * 1e3, 2),
+            "grouped28_weight_GBps": round(28 * b1 / (msg * 1e-3) / 1e9, 1)}
+        del plans
+    out["per_shape_m1"] = per_shape
+
+    # Launch floor: the smallest call (M=1, N=64, K=128).
+    pk0, sc0 = tb.bitnet_ternarize_pack(torch.ones((64, 128), device=dev))
+    x0 = torch.ones((1, 128), device=dev)
+    y0 = torch.empty((1, 64), device=dev)
+    ms0 = timer.time(lambda i=0: tb.bitnet_ternary_matmul_into(1, 64, 128, x0, pk0, sc0, y0, ws1),
+                     500)
+    out["launch_floor_m1_n64_k128"] = {"us_per_call": round(ms0 * 1e3, 2)}
+
+    # The decode time must not depend on the codes: the sweep again with every
+    # code 0 (field value 1 in all four positions of a byte).
+    zero_codes = [torch.full_like(t, 0x55) for t in packed]
+    zplans = [tb.GroupedPlan(1, xs_, zero_codes, w_scales, ys_, [p.N for p in problems],
+                             [p.K for p in problems])
+              for xs_, ys_ in [([torch.from_numpy(synth.problem_activations(p, 1)).to(dev)
+                                 for p in problems],
+                                [torch.empty((1, p.N), device=dev) for p in problems])]]
+    msz = timer.time(lambda i=0: zplans[0].run(), 200)
+    rplans, _, _ = decode_plans(1)
+    msr = timer.time(lambda i=0: rplans[0].run(), 200)
+    out["decode_sweep_m1_code_independence"] = {
+        "us_per_step_random_codes": round(msr * 1e3, 2),
+        "us_per_step_all_zero_codes": round(msz * 1e3, 2),
+        "note": "both from one copy of the weights (not rotated, so partly served by the "
+                "last-level cache); only the codes differ"}
+    del zero_codes, zplans, rplans
 
     out.update(chain_configs(torch, tb, synth, timer, problems, packed, w_scales, alg_bytes,
                              decode_plans, dev))
