@@ -75,6 +75,9 @@ def parse():
     ap.add_argument("--decode-subset", choices=("all", "gate_down"), default="all",
                     help="matrices of the decode sweep (gate_down: the 28 gate + 28 down)")
     ap.add_argument("--no-configs", action="store_true", help="skip the other workloads")
+    ap.add_argument("--settle-seconds", type=float, default=3.0,
+                    help="minimum untimed settling before the headline warm-up (0: none, for "
+                         "profiler runs that count every dispatch)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the timed CPU-oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -300,10 +303,12 @@ def main():
     steps = args.steps
     log(f"[bench] decode sweep M={M} over {len(sweep)} matrices: settling the device, then "
         f"warmup {args.warmup}, timed {steps} steps")
-    settle = timer.settle(lambda i=0: plans[i % 2].run())
-    log(f"[bench] settled after {settle['seconds']} s "
-        f"(first batch {settle['first_batch_us_per_step']}, last batches "
-        f"{settle['last_batches_us_per_step']} us/step)")
+    settle = (timer.settle(lambda i=0: plans[i % 2].run(), min_s=args.settle_seconds)
+              if args.settle_seconds > 0 else None)
+    if settle:
+        log(f"[bench] settled after {settle['seconds']} s "
+            f"(first batch {settle['first_batch_us_per_step']}, last batches "
+            f"{settle['last_batches_us_per_step']} us/step)")
     ms_step = timer.time(lambda i=0: plans[i % 2].run(), steps, warmup=args.warmup)
     weight_gbps = packed_bytes / (ms_step * 1e-3) / 1e9
     bytes_launch = alg_bytes(M, sweep)
@@ -677,9 +682,12 @@ def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, a
     out.update(i8_configs(torch, tb, synth, timer, dev))
     out["decode_sweep_m1_lut"] = lut_config(torch, tb, synth, timer, problems, packed, copy_b,
                                             w_scales, alg_bytes, decode_plans, dev)
+    # The first launches on freshly allocated buffers run slower (M=4: about 72
+    # us per step over 100 steps after 3 warm-up, 67.5 over 1000 after 200), so
+    # these sweeps take the headline's warm-up.
     for M in (4, 16):
         plans, _, _ = decode_plans(M)
-        ms = timer.time(lambda i=0: plans[i % 2].run(), 100)
+        ms = timer.time(lambda i=0: plans[i % 2].run(), 1000, warmup=200)
         out[f"decode_sweep_m{M}"] = {
             "us_per_step": round(ms * 1e3, 2), "weight_GBps": round(pbytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(alg_bytes(M, problems) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
@@ -700,7 +708,7 @@ def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, a
         ys = [torch.empty((M, p.N), device=dev) for p in sub]
         plans = [tb.GroupedPlan(M, xs, [c[i] for i in idx], [w_scales[i] for i in idx], ys,
                                 [p.N for p in sub], [p.K for p in sub]) for c in (packed, copy_b)]
-        ms = timer.time(lambda i=0: plans[i % 2].run(), 50)
+        ms = timer.time(lambda i=0: plans[i % 2].run(), 500, warmup=100)
         sb = sum(p.N * p.K // 4 for p in sub)
         ops = 2.0 * M * sum(p.N * p.K for p in sub)
         out[f"batched_decode_m{M}"] = {

@@ -256,7 +256,20 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
   }
   hipStream_t hs = as_stream(stream);
   uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
-  if (fused) return from_hip(launch_gemv_grouped(problems_dev, tab, ws, true, kmax, hs));
+  // Workgroups of each dispatch slot, for the XCD schedule of the main launch.
+  auto schedule = [&]() {
+    uint32_t tiles[kMaxGroup];
+    for (int32_t s = 0; s < count; ++s) {
+      const bitnet_problem &p = problems_host[tab.order[s]];
+      tiles[s] = gemv ? (uint32_t)gemv_blocks(p.N, p.K, tab.split != 0)
+                      : (uint32_t)gemm_blocks(M, p.N);
+    }
+    xcd_schedule(tab, problems_host, tiles);
+  };
+  if (fused) {
+    schedule();
+    return from_hip(launch_gemv_grouped(problems_dev, tab, ws, true, kmax, hs));
+  }
   QuantTable qt;
   std::memset(&qt, 0, sizeof(qt));
   qt.count = count;
@@ -271,8 +284,8 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
   std::memcpy(qt.ws_off, tab.ws_off, sizeof(qt.ws_off));
   st = from_hip(launch_quant_grouped(problems_dev, qt, ws, hs));
   if (st != BITNET_OK) return st;
+  schedule();
   if (gemv) return from_hip(launch_gemv_grouped(problems_dev, tab, ws, false, kmax, hs));
-  gemm_schedule(tab, problems_host);
   return from_hip(launch_gemm_grouped(problems_dev, tab, ws, hs));
 }
 

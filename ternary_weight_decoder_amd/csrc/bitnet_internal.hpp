@@ -37,9 +37,9 @@ struct GroupTable {
   uint32_t blk_end[kMaxGroup];   // inclusive prefix sum of workgroups, in dispatch order
   uint16_t order[kMaxGroup];     // problem index of each dispatch slot
   uint32_t ws_off[kMaxGroup];    // workspace offset of each problem, in 256-byte units
-  // Prefill only.  spread == 0: the tiles (workgroups) are one list in slot
-  // order, cut into kXcds contiguous ranges of about equal work; XCD x runs
-  // [xcd_first[x], xcd_first[x + 1]).  spread != 0: workgroup b runs tile b.
+  // spread == 0: the workgroups are one list in slot order, cut into kXcds
+  // contiguous ranges of whole projections of about equal work; XCD x runs
+  // [xcd_first[x], xcd_first[x + 1]).  spread != 0: workgroup b runs entry b.
   int32_t spread;
   uint32_t xcd_first[kXcds + 1];
 };
@@ -161,7 +161,11 @@ hipError_t launch_gemm(int M, int N, int K, const int8_t *xq_perm, const float *
 int gemm_blocks(int64_t M, int64_t N);
 // Prefill launch schedule: reorders the slots (tab.order, tab.blk_end) and
 // fills tab.spread / tab.xcd_first.
-void gemm_schedule(GroupTable &tab, const bitnet_problem *problems_host);
+// Deal whole projections to the XCDs (sets tab.order, blk_end, spread and
+// xcd_first); tiles[s] = workgroups of dispatch slot s in the current order.
+void xcd_schedule(GroupTable &tab, const bitnet_problem *problems_host, const uint32_t *tiles);
+// Grid of an XCD-scheduled launch: eight times the largest per-XCD range.
+unsigned xcd_grid(const uint32_t *first);
 hipError_t launch_gemm_grouped(const bitnet_problem *problems, const GroupTable &tab,
                                const uint8_t *workspace, hipStream_t stream);
 

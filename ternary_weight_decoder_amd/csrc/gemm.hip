@@ -444,20 +444,19 @@ int gemm_blocks(int64_t M, int64_t N) {
   return (int)(((M + bm - 1) / bm) * ((N + BN - 1) / BN));
 }
 
-void gemm_schedule(GroupTable &tab, const bitnet_problem *problems_host) {
-  // Each XCD gets a set of whole projections of about equal work (a tile's
-  // work is its number of K units), assigned longest K first to the least
-  // loaded XCD, so every XCD holds its share of the long-K tiles and starts
-  // them first.  When the projections are too few for that to balance, the
-  // tiles are dealt to the XCDs round-robin instead.
+void xcd_schedule(GroupTable &tab, const bitnet_problem *problems_host, const uint32_t *tiles) {
+  // Each XCD gets a set of whole projections of about equal work (a
+  // workgroup's work is its number of K units), assigned longest K first to
+  // the least loaded XCD, so every XCD holds its share of the long-K
+  // workgroups and starts them first, and a projection's activations and codes
+  // are fetched into one L2 only.  When the projections are too few for that
+  // to balance, the workgroups are dealt to the XCDs round-robin instead.
   const int count = tab.count;
   int slot[kMaxGroup];
-  uint32_t tiles[kMaxGroup];
   uint64_t work[kMaxGroup];
   for (int s = 0; s < count; ++s) {
     const int p = tab.order[s];
     slot[s] = s;
-    tiles[s] = (uint32_t)gemm_blocks(tab.M, problems_host[p].N);
     work[s] = (uint64_t)tiles[s] * (uint64_t)(problems_host[p].K / kUnit);
   }
   std::stable_sort(slot, slot + count, [&](int a, int b) {
@@ -496,7 +495,7 @@ void gemm_schedule(GroupTable &tab, const bitnet_problem *problems_host) {
   for (int i = 0; i < count; ++i) tab.order[i] = order[i];
 }
 
-static unsigned xcd_grid(const uint32_t *first) {
+unsigned xcd_grid(const uint32_t *first) {
   uint32_t most = 0;
   for (int x = 0; x < kXcds; ++x) most = std::max(most, first[x + 1] - first[x]);
   return most * kXcds;

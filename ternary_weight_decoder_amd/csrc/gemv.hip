@@ -313,7 +313,15 @@ __global__ void __launch_bounds__(kThreads)
                         const uint8_t *__restrict__ workspace) {
   __shared__ GemvShared sh;
   extern __shared__ __attribute__((aligned(16))) int8_t xq_lds[];
-  const uint32_t b = blockIdx.x;
+  // Block b runs on XCD b % 8; unless the table deals workgroups round-robin,
+  // XCD x runs its own range [xcd_first[x], xcd_first[x + 1]) of whole
+  // projections, so each projection's activations are fetched into one L2.
+  uint32_t b = blockIdx.x;
+  if (!tab.spread) {
+    const uint32_t x = b % kXcds;
+    b = tab.xcd_first[x] + b / kXcds;
+    if (b >= tab.xcd_first[x + 1]) return;
+  }
   const SlotInfo si = find_slot(tab, b);
   const uint32_t first = si.first;
   const int pi = si.problem;
@@ -385,7 +393,7 @@ hipError_t launch_gemv_fused(int M, int N, int K, const float *x, const uint8_t 
 hipError_t launch_gemv_grouped(const bitnet_problem *problems, const GroupTable &tab,
                                const uint8_t *workspace, bool fused, int64_t kmax,
                                hipStream_t stream) {
-  const unsigned blocks = tab.blk_end[tab.count - 1];
+  const unsigned blocks = tab.spread ? tab.blk_end[tab.count - 1] : xcd_grid(tab.xcd_first);
   if (fused)
     gemv_grouped_kernel<true><<<blocks, kThreads, fused_lds_bytes(tab.M, kmax, tab.split != 0),
                                 stream>>>(problems, tab, workspace);
