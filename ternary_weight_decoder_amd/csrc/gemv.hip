@@ -18,11 +18,14 @@
 // bytes per unit and 16-column block.  Field values u = code+1 enter the MFMA;
 // the epilogue subtracts the activation row sum.
 //
-// Weights are read with buffer loads kept D (tile, unit) items ahead in a
-// register ring that runs across tile boundaries.  Loads for columns past N or
-// items past the wave's range are aimed past the buffer's end: the hardware
-// returns zeros without touching memory, so every ring slot issues the same
-// instructions and the wait counts stay static.
+// Weights are read with buffer loads kept D units ahead in a register ring.
+// Loads for columns past N or units past the wave's range are aimed past the
+// buffer's end: the hardware returns zeros without touching memory, so every
+// ring slot issues the same instructions and the wait counts stay static.
+//
+// Grouped launches: the host deals whole projections to the eight XCDs (block
+// b runs on XCD b % 8, and XCD x runs its own range of the table), so each
+// projection's activation row, or staged int8 rows, is fetched into one L2.
 //
 // Activation quantization is fused when the M x K int8 rows fit in LDS: every
 // workgroup quantizes the rows itself (absmax, scale, round, row sum) into LDS
