@@ -371,12 +371,16 @@ bitnet_status bitnet_ternary_matmul_lut_grouped(const bitnet_problem *problems_d
   tab.count = count;
   tab.M = 1;
   uint64_t total = 0;
+  uint32_t tiles[kMaxGroup];
   for (int32_t s = 0; s < count; ++s) {
-    total += (uint64_t)lut_blocks(problems_host[idx[s]].N);
+    tiles[s] = (uint32_t)lut_blocks(problems_host[idx[s]].N);
+    total += tiles[s];
     if (total >= ((uint64_t)1 << 31)) return BITNET_ERR_SHAPE;
     tab.blk_end[s] = (uint32_t)total;
     tab.order[s] = (uint16_t)idx[s];
   }
+  // Whole projections to the XCDs, as in the grouped call.
+  xcd_schedule(tab, problems_host, tiles);
   return from_hip(launch_lut_grouped(problems_dev, tab, as_stream(stream)));
 }
 

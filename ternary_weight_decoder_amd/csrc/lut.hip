@@ -130,11 +130,20 @@ __device__ __forceinline__ int lut_unit(const u32x4 (&w)[2], uint32_t ubase,
 __global__ void __launch_bounds__(kLutThreads)
     lut_gemv_grouped_kernel(const bitnet_problem *__restrict__ problems, GroupTable tab) {
   __shared__ LutShared sh;
-  const SlotInfo si = find_slot(tab, blockIdx.x);
+  // Block b runs on XCD b % 8; unless the table deals workgroups round-robin,
+  // XCD x runs its own range [xcd_first[x], xcd_first[x + 1]) of whole
+  // projections.
+  uint32_t b = blockIdx.x;
+  if (!tab.spread) {
+    const uint32_t x = b % kXcds;
+    b = tab.xcd_first[x] + b / kXcds;
+    if (b >= tab.xcd_first[x + 1]) return;
+  }
+  const SlotInfo si = find_slot(tab, b);
   const bitnet_problem pr = problems[si.problem];
   const int N = (int)pr.N, K = (int)pr.K, U = K >> 7;
   // Column r of this thread: n0 + 256 r (each wave reads 64 adjacent columns).
-  const int n0 = (int)(blockIdx.x - si.first) * kLutTile + threadIdx.x;
+  const int n0 = (int)(b - si.first) * kLutTile + threadIdx.x;
 
   const uint32_t w_bytes = (uint32_t)((size_t)N * K / 4);
   const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(pr.packed, w_bytes);
@@ -191,7 +200,8 @@ int lut_blocks(int64_t N) { return (int)((N + kLutTile - 1) / kLutTile); }
 
 hipError_t launch_lut_grouped(const bitnet_problem *problems, const GroupTable &tab,
                               hipStream_t stream) {
-  lut_gemv_grouped_kernel<<<tab.blk_end[tab.count - 1], kLutThreads, 0, stream>>>(problems, tab);
+  const unsigned grid = tab.spread ? tab.blk_end[tab.count - 1] : xcd_grid(tab.xcd_first);
+  lut_gemv_grouped_kernel<<<grid, kLutThreads, 0, stream>>>(problems, tab);
   return hipGetLastError();
 }
 
