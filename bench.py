@@ -109,7 +109,7 @@ class Timer:
     def __init__(self, torch, stream):
         self.torch, self.stream = torch, stream
 
-    def time(self, fn, steps, warmup=3):
+    def time(self, fn, steps, warmup=50):
         torch = self.torch
         for _ in range(warmup):
             fn()
@@ -432,7 +432,7 @@ def prefill_config(torch, tb, timer, problems, packed, w_scales, M, dev):
     ys = [torch.empty((M, p.N), device=dev) for p in problems]
     plan = tb.GroupedPlan(M, xs, packed, w_scales, ys, [p.N for p in problems],
                           [p.K for p in problems])
-    ms = timer.time(lambda i=0: plan.run(), 5 if M > 1000 else 10, warmup=2)
+    ms = timer.time(lambda i=0: plan.run(), 5 if M > 1000 else 10, warmup=5)
     ops = 2.0 * M * sum(p.N * p.K for p in problems)
     res = {"ms_per_step": round(ms, 4), "int8_TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
            "frac_of_int8_peak": round(ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
@@ -549,7 +549,7 @@ def i8_configs(torch, tb, synth, timer, dev, steps=100):
         ws = torch.empty(tb.bitnet_i8_linear_workspace_bytes(M, K), dtype=torch.uint8,
                          device=dev)
         ms = timer.time(lambda i=0: tb.bitnet_i8_linear_into(M, N, K, xs[i % 4], q, s, bd, relu,
-                                                             ys[i % 4], ws), steps, warmup=10)
+                                                             ys[i % 4], ws), steps, warmup=100)
         moved = M * K * 4 + N * K + N * 4 + M * N * 4
         out[f"i8_linear_{name}"] = {
             "shape": {"M": M, "K": K, "N": N, "bias": True, "relu": relu},
@@ -564,7 +564,7 @@ def i8_configs(torch, tb, synth, timer, dev, steps=100):
 
 
 def lut_config(torch, tb, synth, timer, problems, packed, copy_b, w_scales, alg_bytes,
-               decode_plans, dev, steps=200):
+               decode_plans, dev, steps=1000):
     """The lookup-table variant over the M=1 decode sweep, timed like the headline
     (two packed copies alternate), with its outputs compared to the grouped
     call's on the same inputs."""
@@ -573,7 +573,7 @@ def lut_config(torch, tb, synth, timer, problems, packed, copy_b, w_scales, alg_
     ys = [torch.empty((1, p.N), dtype=torch.float32, device=dev) for p in problems]
     Ns, Ks = [p.N for p in problems], [p.K for p in problems]
     plans = [tb.LutPlan(xs, c, w_scales, ys, Ns, Ks) for c in (packed, copy_b)]
-    ms = timer.time(lambda i=0: plans[i % 2].run(), steps, warmup=20)
+    ms = timer.time(lambda i=0: plans[i % 2].run(), steps, warmup=200)
     ref_plans, _, ref_ys = decode_plans(1, xs_host=xs_host, copies=(packed,))
     plans[0].run()
     ref_plans[0].run()
