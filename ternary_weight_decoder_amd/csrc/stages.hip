@@ -53,7 +53,6 @@ constexpr int kStageWaves = kWaves;
 constexpr int kStageItems = 18;    // K units per wave: ceil(70 / 4) for K <= 8960
 constexpr int kStageXVec = (int)((kGemvFusedLdsBytes / 4 + kThreads - 1) / kThreads);
 constexpr int kWeightAux = 2;      // weights are read once: non-temporal
-constexpr int kCoherentAux = 16;   // sc1: device-coherent load
 
 struct StageShared {
   __attribute__((aligned(16))) int8_t xq[kGemvFusedLdsBytes];   // permuted rows [M][K]
