@@ -87,8 +87,9 @@ struct GemvShared {
   int rowsum[kGemvMaxM];
 };
 
-// Quantize the M rows of x into LDS (permuted order) with the scales and row sums.
-__device__ __forceinline__ void quant_rows_to_lds(const GemvProblem &p, GemvShared &sh,
+// Quantize the M rows of x into LDS (permuted order) with the scales and row sums,
+// one grid-stride loop per pass (the form for launches that fill the chip).
+__device__ __forceinline__ void quant_rows_serial(const GemvProblem &p, GemvShared &sh,
                                                   int8_t *xq_lds, bool write_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n4 = p.K >> 2;
@@ -131,13 +132,95 @@ __device__ __forceinline__ void quant_rows_to_lds(const GemvProblem &p, GemvShar
   __syncthreads();
 }
 
+// The same for small launches (K-split).  // A pass over a row issues all of a thread's loads at once (up to kQuantBatch
+// 16-byte buffer loads; positions past the row are aimed beyond it and return
+// zeros without a memory access), so a row costs one memory round trip per
+// pass instead of one per loop iteration: on a long row (K = 8960) that is the
+// difference between 2 and 18 round trips, which a small launch cannot hide
+// behind other workgroups.  A single row that fits one batch stays in
+// registers from the absmax pass to the quantizing pass.
+constexpr int kQuantBatch = 9;   // 9 x 256 threads x 4 = 9216 inputs per batch
+
+__device__ __forceinline__ void load_row_batch(__amdgpu_buffer_rsrc_t rsrc, int n4, int base,
+                                               f32x4 (&v)[kQuantBatch]) {
+#pragma unroll
+  for (int j = 0; j < kQuantBatch; ++j) {
+    const int i = base + j * kThreads + (int)threadIdx.x;
+    const uint32_t off = (uint32_t)(i < n4 ? i : n4) * 16u;
+    v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0));
+  }
+}
+
+__device__ __forceinline__ void quant_rows_batched(const GemvProblem &p, GemvShared &sh,
+                                                  int8_t *xq_lds, bool write_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n4 = p.K >> 2;
+  constexpr int kBatch4 = kQuantBatch * kThreads;   // f32x4 elements per batch
+  const bool resident = p.M == 1 && n4 <= kBatch4;
+  f32x4 v[kQuantBatch];
+  for (int m = 0; m < p.M; ++m) {
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(p.x + (size_t)m * p.K, (uint32_t)p.K * 4u);
+    float a = 0.0f;
+    for (int base = 0; base < n4; base += kBatch4) {
+      load_row_batch(rsrc, n4, base, v);
+#pragma unroll
+      for (int j = 0; j < kQuantBatch; ++j)
+        a = fmaxf(a, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+    }
+    a = wave_max(a);
+    if (lane == 0) sh.red[m][wave] = a;
+  }
+  __syncthreads();
+  for (int m = 0; m < p.M; ++m) {
+    const float a = fmaxf(fmaxf(sh.red[m][0], sh.red[m][1]), fmaxf(sh.red[m][2], sh.red[m][3]));
+    const float s = (a == 0.0f) ? 1.0f : 127.0f / a;
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(p.x + (size_t)m * p.K, (uint32_t)p.K * 4u);
+    int8_t *dst = xq_lds + (size_t)m * p.K;
+    int sum = 0;
+    for (int base = 0; base < n4; base += kBatch4) {
+      if (!resident) load_row_batch(rsrc, n4, base, v);
+#pragma unroll
+      for (int j = 0; j < kQuantBatch; ++j) {
+        const int i = base + j * kThreads + tid;
+        if (i < n4) {
+          const int q0 = quant_one(v[j].x, s), q1 = quant_one(v[j].y, s);
+          const int q2 = quant_one(v[j].z, s), q3 = quant_one(v[j].w, s);
+          sum += q0 + q1 + q2 + q3;
+          const uint32_t w = pack4_i8(q0, q1, q2, q3);
+          *reinterpret_cast<uint32_t *>(dst + perm_offset(4 * i)) = w;
+          if (write_out) st_global<uint32_t>(p.xq_out + (size_t)m * p.K + 4 * i, w);
+        }
+      }
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) sh.ired[m][wave] = sum;
+    if (tid == 0) {
+      sh.scale[m] = s;
+      if (write_out) st_global<float>(p.x_scale_out + m, s);
+    }
+  }
+  __syncthreads();
+  if (tid < p.M)
+    sh.rowsum[tid] = sh.ired[tid][0] + sh.ired[tid][1] + sh.ired[tid][2] + sh.ired[tid][3];
+  __syncthreads();
+}
+
+template <bool BATCHED>
+__device__ __forceinline__ void quant_rows_to_lds(const GemvProblem &p, GemvShared &sh,
+                                                  int8_t *xq_lds, bool write_out) {
+  if (BATCHED)
+    quant_rows_batched(p, sh, xq_lds, write_out);
+  else
+    quant_rows_serial(p, sh, xq_lds, write_out);
+}
+
 // Workgroup blk of a problem: with S = 1, wave w owns columns
 // [(4 blk + w) * 64, +64) over all K units; with a K-split S (single-row fused
 // launches only), wave w owns the 64 columns of group g = w % (4/S) starting at
 // (blk * 4/S + g) * 64, over K units [q * units / S, (q + 1) * units / S) with
 // q = w / (4/S).  FUSED: the rows are quantized into LDS here; otherwise they
 // are staged into LDS from the workspace chunk by chunk.
-template <bool FUSED>
+template <bool FUSED, bool SMALL>
 __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, bool split,
                                            GemvShared &sh, int8_t *lds) {
   constexpr int C = kGemvC;
@@ -202,7 +285,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, bool s
 #pragma unroll
   for (int j = 0; j < D; ++j) load_item(wr[j]);
 
-  if (FUSED) quant_rows_to_lds(p, sh, lds, p.xq_out != nullptr && blk == 0);
+  if (FUSED) quant_rows_to_lds<SMALL>(p, sh, lds, p.xq_out != nullptr && blk == 0);
 
   // Dequantization inputs of accumulator element r of this lane (row 4h + r).
   const float ws = ld_global<float>(p.w_scale);
@@ -302,16 +385,19 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, bool s
   }
 }
 
-template <bool FUSED>
-__global__ void __launch_bounds__(kThreads) gemv_kernel(GemvProblem p, int split) {
+// SMALL: a launch too small to fill the chip (the K-split form), whose
+// workgroups quantize their row with batched loads; four workgroups (waves per
+// SIMD) stay resident, which holds the batch's registers to that budget.
+template <bool FUSED, bool SMALL>
+__global__ void __launch_bounds__(kThreads, SMALL ? 4 : 1) gemv_kernel(GemvProblem p, int split) {
   __shared__ GemvShared sh;
   extern __shared__ __attribute__((aligned(16))) int8_t xq_lds[];
-  gemv_block<FUSED>(p, blockIdx.x, split != 0, sh, xq_lds);
+  gemv_block<FUSED, SMALL>(p, blockIdx.x, split != 0, sh, xq_lds);
 }
 
 // Grouped: dispatch slot s of the table owns workgroups [blk_end[s-1], blk_end[s]).
-template <bool FUSED>
-__global__ void __launch_bounds__(kThreads)
+template <bool FUSED, bool SMALL>
+__global__ void __launch_bounds__(kThreads, SMALL ? 4 : 1)
     gemv_grouped_kernel(const bitnet_problem *__restrict__ problems, GroupTable tab,
                         const uint8_t *__restrict__ workspace) {
   __shared__ GemvShared sh;
@@ -352,7 +438,7 @@ __global__ void __launch_bounds__(kThreads)
   p.N = (int)pr.N;
   p.K = (int)pr.K;
   p.M = M;
-  gemv_block<FUSED>(p, (int)(b - first), tab.split != 0, sh, xq_lds);
+  gemv_block<FUSED, SMALL>(p, (int)(b - first), tab.split != 0, sh, xq_lds);
 }
 
 }  // namespace
@@ -378,7 +464,7 @@ hipError_t launch_gemv(int M, int N, int K, const int8_t *xq_perm, const float *
                        float *y, int32_t *acc_out, hipStream_t stream) {
   GemvProblem p{packed, nullptr, xq_perm, x_scale, rowsum, w_scale, y, acc_out,
                 nullptr, nullptr, N, K, M};
-  gemv_kernel<false><<<gemv_blocks(N, K, false), kThreads, 2 * kChunkBytes, stream>>>(p, 0);
+  gemv_kernel<false, false><<<gemv_blocks(N, K, false), kThreads, 2 * kChunkBytes, stream>>>(p, 0);
   return hipGetLastError();
 }
 
@@ -388,8 +474,12 @@ hipError_t launch_gemv_fused(int M, int N, int K, const float *x, const uint8_t 
   GemvProblem p{packed, x, nullptr, nullptr, nullptr, w_scale, y, acc_out,
                 xq_out, x_scale_out, N, K, M};
   const bool split = gemv_blocks(N, K, false) < kGemvSplitBelow;
-  gemv_kernel<true><<<gemv_blocks(N, K, split), kThreads, fused_lds_bytes(M, K, split),
-                      stream>>>(p, split ? 1 : 0);
+  if (split)
+    gemv_kernel<true, true><<<gemv_blocks(N, K, true), kThreads, fused_lds_bytes(M, K, true),
+                              stream>>>(p, 1);
+  else
+    gemv_kernel<true, false><<<gemv_blocks(N, K, false), kThreads,
+                               fused_lds_bytes(M, K, false), stream>>>(p, 0);
   return hipGetLastError();
 }
 
@@ -397,12 +487,15 @@ hipError_t launch_gemv_grouped(const bitnet_problem *problems, const GroupTable 
                                const uint8_t *workspace, bool fused, int64_t kmax,
                                hipStream_t stream) {
   const unsigned blocks = tab.spread ? tab.blk_end[tab.count - 1] : xcd_grid(tab.xcd_first);
-  if (fused)
-    gemv_grouped_kernel<true><<<blocks, kThreads, fused_lds_bytes(tab.M, kmax, tab.split != 0),
-                                stream>>>(problems, tab, workspace);
+  if (fused && tab.split)
+    gemv_grouped_kernel<true, true><<<blocks, kThreads, fused_lds_bytes(tab.M, kmax, true),
+                                      stream>>>(problems, tab, workspace);
+  else if (fused)
+    gemv_grouped_kernel<true, false><<<blocks, kThreads, fused_lds_bytes(tab.M, kmax, false),
+                                       stream>>>(problems, tab, workspace);
   else
-    gemv_grouped_kernel<false><<<blocks, kThreads, 2 * kChunkBytes, stream>>>(problems, tab,
-                                                                              workspace);
+    gemv_grouped_kernel<false, false><<<blocks, kThreads, 2 * kChunkBytes, stream>>>(
+        problems, tab, workspace);
   return hipGetLastError();
 }
 
