@@ -386,10 +386,11 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, bool s
 }
 
 // SMALL: a launch too small to fill the chip (the K-split form), whose
-// workgroups quantize their row with batched loads; four workgroups (waves per
-// SIMD) stay resident, which holds the batch's registers to that budget.
+// workgroups quantize their row with batched loads.  Such a launch has fewer
+// than two workgroups per CU, so the register budget is that of two waves per
+// SIMD (measured faster than holding it to four).
 template <bool FUSED, bool SMALL>
-__global__ void __launch_bounds__(kThreads, SMALL ? 4 : 1) gemv_kernel(GemvProblem p, int split) {
+__global__ void __launch_bounds__(kThreads, SMALL ? 2 : 1) gemv_kernel(GemvProblem p, int split) {
   __shared__ GemvShared sh;
   extern __shared__ __attribute__((aligned(16))) int8_t xq_lds[];
   gemv_block<FUSED, SMALL>(p, blockIdx.x, split != 0, sh, xq_lds);
@@ -397,7 +398,7 @@ __global__ void __launch_bounds__(kThreads, SMALL ? 4 : 1) gemv_kernel(GemvProbl
 
 // Grouped: dispatch slot s of the table owns workgroups [blk_end[s-1], blk_end[s]).
 template <bool FUSED, bool SMALL>
-__global__ void __launch_bounds__(kThreads, SMALL ? 4 : 1)
+__global__ void __launch_bounds__(kThreads, SMALL ? 2 : 1)
     gemv_grouped_kernel(const bitnet_problem *__restrict__ problems, GroupTable tab,
                         const uint8_t *__restrict__ workspace) {
   __shared__ GemvShared sh;
