@@ -123,11 +123,14 @@ __device__ __forceinline__ int swz(int r) { return (r >> BITNET_GEMM_SWZ_SHIFT) 
 // One output tile over K units [ub, ub + nunits).  SPLIT: the tile is one of
 // several K slices; its raw int32 sums (field values times activations, no
 // row-sum correction) are added atomically into the output buffer, which
-// holds int32 partial sums until the finishing pass.
-template <int BM, bool SPLIT>
+// holds int32 partial sums until the finishing pass.  RB: the 32-row blocks
+// the tile multiplies and stores, fewer than BM / 32 for the last row block of
+// a ragged M (its activation loads still cover BM rows, those past M as zeros,
+// so the ring and its wait counts are the same for every tile).
+template <int BM, bool SPLIT, int RB>
 __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0, int ub,
                                            int nunits, GemmShared<BM> &sh) {
-  constexpr int RB = TileCfg<BM>::RB;
+  static_assert(RB >= 1 && RB <= TileCfg<BM>::RB, "row blocks per tile");
   constexpr int kDma = TileCfg<BM>::kDma;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -340,6 +343,20 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
   }
 }
 
+// A tile starting at row m0: as many 32-row blocks as the rows left below M
+// need, so the last row block of a ragged M does not multiply padding rows.
+template <int BM, bool SPLIT, int RB = TileCfg<BM>::RB>
+__device__ __forceinline__ void gemm_tile(const GemmProblem &p, int m0, int n0, int ub,
+                                          int nunits, GemmShared<BM> &sh) {
+  if constexpr (RB > 1) {
+    if (p.M - m0 <= 32 * (RB - 1)) {
+      gemm_tile<BM, SPLIT, RB - 1>(p, m0, n0, ub, nunits, sh);
+      return;
+    }
+  }
+  gemm_block<BM, SPLIT, RB>(p, m0, n0, ub, nunits, sh);
+}
+
 template <int BM>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(TileCfg<BM>::kWavesPerEu, TileCfg<BM>::kWavesPerEu)))
@@ -353,7 +370,7 @@ __global__ void __launch_bounds__(kThreads)
   if (t >= (x + 1) * tiles / kXcds) return;
   int rb, ct;
   band_tile((int)t, mt, nt, rb, ct);
-  gemm_block<BM, false>(p, rb * BM, ct * BN, 0, p.K >> 7, sh);
+  gemm_tile<BM, false>(p, rb * BM, ct * BN, 0, p.K >> 7, sh);
 }
 
 // K-split form for launches with few tiles: block b runs K slice b % S of tile
@@ -371,7 +388,7 @@ __global__ void __launch_bounds__(kThreads)
   const int ub = q * units / S;
   int rb, ct;
   band_tile(t, mt, nt, rb, ct);
-  gemm_block<BM, true>(p, rb * BM, ct * BN, ub, (q + 1) * units / S - ub, sh);
+  gemm_tile<BM, true>(p, rb * BM, ct * BN, ub, (q + 1) * units / S - ub, sh);
 }
 
 // Zero the output before the K slices add into it (a fill kernel, so that the
@@ -426,7 +443,7 @@ __global__ void __launch_bounds__(kThreads)
   p.K = (int)pr.K;
   int rb, ct;
   band_tile((int)(g - si.first), (M + BM - 1) / BM, (p.N + BN - 1) / BN, rb, ct);
-  gemm_block<BM, false>(p, rb * BM, ct * BN, 0, p.K >> 7, sh);
+  gemm_tile<BM, false>(p, rb * BM, ct * BN, 0, p.K >> 7, sh);
 }
 
 }  // namespace

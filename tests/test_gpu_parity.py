@@ -210,6 +210,8 @@ MATMUL_CASES = [(m, 200, 384) for m in range(1, 21)] + [
     (1, 1536, 1536), (1, 256, 1536), (1, 8960, 1536), (1, 1536, 8960), (4, 1536, 8960),
     (16, 1536, 8960), (16, 65, 128), (32, 300, 512), (64, 8960, 1536), (256, 1536, 1536),
     (257, 520, 256), (1800, 300, 1536), (129, 257, 1280), (20, 136, 10368), (40, 72, 2176),
+    # 128-row tiles whose last row block holds 1..4 blocks of 32 rows
+    (90, 300, 384), (200, 520, 640), (161, 264, 512), (236, 72, 1152),
     # decode rows staged through LDS in 8-unit chunks: partial chunks, ragged N
     (5, 200, 2048), (3, 72, 8960), (16, 300, 1280), (2, 520, 4608), (13, 1000, 768),
     # single-row launches with K split 2 or 4 ways across the waves of a workgroup
@@ -356,13 +358,14 @@ def test_grouped_layer_parity(tb, M):
         assert_y_matches(ys[i].cpu().numpy(), ref["y"], M)
 
 
-@pytest.mark.parametrize("M", [1, 3, 16, 40])
+@pytest.mark.parametrize("M", [1, 3, 16, 40, 200])
 def test_grouped_many_ragged_parity(tb, M):
     """64 independent projections of mixed ragged shapes in one grouped call,
     every output checked against the oracle.  With these sizes the host deals
     whole projections to the XCDs in every regime: M = 1 (fused quantization,
     K split across waves), M = 3 (fused, several rows), M = 16 (rows staged
-    through LDS) and M = 40 (the prefill GEMM)."""
+    through LDS), M = 40 (the prefill GEMM, 64-row tiles) and M = 200 (128-row
+    tiles, the last row block three 32-row blocks deep)."""
     import torch
     say(f"[grouped] 64 ragged projections M={M}")
     rng = np.random.default_rng(900)
