@@ -24,9 +24,12 @@ summary in profiles/ when it was taken on the current kernel source.
 layer, each projection shape alone and grouped over its 28 layers, the launch
 floor, the sweep with all-zero codes against random ones, the dependent
 per-token chain, the I8_S encoder layers, the lookup-table sweep, the sweep at
-M = 4 and 16, prefill at M = 256 and 1800, batched decode at M = 32 and 64);
+M = 4 and 16, prefill at M = 256 and 1800 over the 196 matrices and at M = 256
+over one layer, prefill on each projection shape alone (its 28 matrices
+grouped, and one matrix per call), batched decode at M = 32 and 64);
 `cpu_baseline` times the CPU oracle on a bounded sample of the headline
-workload on this host, and its ternarize + pack step on its own.
+workload on this host, its ternarize + pack step on its own, and (in
+`other_rows`) its prefill and I8_S contractions on row samples.
 """
 from __future__ import annotations
 
@@ -288,6 +291,8 @@ def main():
         M = args.prefill_m
         log(f"[bench] prefill M={M} only")
         res = prefill_config(torch, tb, timer, problems, packed, w_scales, M, dev)
+        res["per_shape"] = prefill_shapes_config(torch, tb, timer, problems, packed, w_scales,
+                                                      M, dev)
         print(json.dumps({"workload": f"prefill M={M} over {n_mat} matrices", **res}), flush=True)
         return
 
@@ -367,6 +372,29 @@ def main():
             t1 += time.perf_counter() - t0
             b1 += p.N * p.K // 4
         oracle.set_num_threads(cores)
+        # The oracle on the other contraction rows, each on a bounded row sample.
+        other = {}
+        t_pf, ops_pf = 0.0, 0.0
+        for i, p in enumerate(sweep[:min(7, mats)]):
+            xp = synth.activations(32, p.K, seed=33000 + i)
+            t0 = time.perf_counter()
+            oracle.ternary_matmul(xp, refs[i][0], refs[i][1], p.N)
+            t_pf += time.perf_counter() - t0
+            ops_pf += 2.0 * 32 * p.N * p.K
+        if t_pf > 0:
+            other["prefill"] = {"value": round(ops_pf / t_pf / 1e12, 5), "unit": "int8 TOPS",
+                                "sample": "layer 0's 7 projections, 32 rows each"}
+        t_i8, ops_i8 = 0.0, 0.0
+        for name in sorted(synth.I8_LAYERS):
+            _, K8, N8, relu8 = synth.I8_LAYERS[name]
+            x8, W8, b8 = synth.i8_layer_inputs(name)
+            q8, s8 = oracle.i8_quant_weights(W8)
+            t0 = time.perf_counter()
+            oracle.i8_linear(x8[:1024], q8, s8, b8, relu8)
+            t_i8 += time.perf_counter() - t0
+            ops_i8 += 2.0 * 1024 * N8 * K8
+        other["i8_linear"] = {"value": round(ops_i8 / t_i8 / 1e12, 5), "unit": "int8 TOPS",
+                              "sample": "first 1024 rows of each I8_S encoder layer"}
         cpu = {"value": round(bytes_done / t_spent / 1e9, 4), "unit": "GB/s", "cores": cores,
                "kind": "oracle",
                "sample": f"first {mats} of {len(sweep)} decode projections (layers in order, "
@@ -381,6 +409,7 @@ def main():
                                   "note": "offline step, outside the decode figure"},
                "single_thread": {"value": round(b1 / t1 / 1e9, 4), "unit": "GB/s",
                                  "sample": "layer 0's 7 projections, M=1, 1 thread"},
+               "other_rows": other,
                "host_cpu": host_cpu()}
         log(f"[bench] cpu oracle {cpu['value']} GB/s on {cores} threads ({mats} matrices)")
 
@@ -441,6 +470,62 @@ def prefill_config(torch, tb, timer, problems, packed, w_scales, M, dev):
     del xs, ys, plan
     torch.cuda.empty_cache()
     return res
+
+
+def prefill_layer_config(torch, tb, timer, problems, packed, w_scales, M, dev):
+    """One layer's 7 projections at prefill in one grouped call (quantization +
+    GEMM); step i runs layer i % 28, so every step reads its codes from HBM."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(31000 + M)
+    layer = problems[:7]
+    xs = [gpu_activations(torch, g, M, p.K, dev) for p in layer]
+    ys = [torch.empty((M, p.N), device=dev) for p in layer]
+    layers = len(problems) // 7
+    plans = [tb.GroupedPlan(M, xs, packed[7 * l:7 * l + 7], w_scales[7 * l:7 * l + 7], ys,
+                            [p.N for p in layer], [p.K for p in layer]) for l in range(layers)]
+    ms = timer.time(lambda i=0: plans[i % layers].run(), 280, warmup=56)
+    ops = 2.0 * M * sum(p.N * p.K for p in layer)
+    return {"us_per_layer": round(ms * 1e3, 2), "int8_TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
+            "frac_of_int8_peak": round(ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+            "step": "one grouped call (quantization + GEMM launch) over q,k,v,o,gate,up,down "
+                    "of one layer, layers rotated"}
+
+
+def prefill_shapes_config(torch, tb, timer, problems, packed, w_scales, M, dev):
+    """Each projection shape alone: its 28 matrices (one per layer) in one
+    grouped call per step (quantization + GEMM launch), and one matrix per call
+    through bitnet_ternary_matmul_q8 from pre-quantized rows (a row-sum pass and
+    the GEMM launch; K-split launches add a zero fill and a finishing pass), the
+    28 layers' matrices in turn."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(32000 + M)
+    out = {}
+    for proj, name in ((0, "q_o_1536x1536"), (1, "k_v_256x1536"), (4, "gate_up_8960x1536"),
+                       (6, "down_1536x8960")):
+        idx = [i for i, p in enumerate(problems) if p.proj == proj]
+        n = len(idx)
+        N, K = problems[idx[0]].N, problems[idx[0]].K
+        ops = 2.0 * M * N * K
+        xs = [gpu_activations(torch, g, M, K, dev) for _ in idx]
+        ys = [torch.empty((M, N), device=dev) for _ in idx]
+        plan = tb.GroupedPlan(M, xs, [packed[i] for i in idx], [w_scales[i] for i in idx], ys,
+                              [N] * n, [K] * n)
+        ms_g = timer.time(lambda i=0: plan.run(), 10 if M > 1000 else 40, warmup=5)
+        xq, xsc = tb.bitnet_quant_act(xs[0])
+        ws = torch.empty(tb.bitnet_matmul_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+        ms_1 = timer.time(lambda i=0: tb.bitnet_ternary_matmul_q8_into(
+            M, N, K, xq, xsc, packed[idx[i % n]], w_scales[idx[i % n]], ys[0], ws), 5 * n,
+            warmup=2 * n)
+        out[name] = {"grouped_28_us": round(ms_g * 1e3, 2),
+                     "grouped_28_int8_TOPS": round(n * ops / (ms_g * 1e-3) / 1e12, 1),
+                     "grouped_28_frac_of_int8_peak": round(
+                         n * ops / (ms_g * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                     "single_call_q8_us": round(ms_1 * 1e3, 2),
+                     "single_call_q8_frac_of_int8_peak": round(
+                         ops / (ms_1 * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)}
+        del xs, ys, plan, xq, xsc, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def chain_configs(torch, tb, synth, timer, problems, packed, w_scales, alg_bytes, decode_plans,
@@ -697,6 +782,11 @@ def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, a
     # the same 196 matrices.
     for M in (synth.PREFILL_M_30S, synth.PREFILL_M_LONG):
         out[f"prefill_m{M}"] = prefill_config(torch, tb, timer, problems, packed, w_scales, M, dev)
+    out[f"prefill_one_layer_m{synth.PREFILL_M_30S}"] = prefill_layer_config(
+        torch, tb, timer, problems, packed, w_scales, synth.PREFILL_M_30S, dev)
+    for M in (synth.PREFILL_M_30S, synth.PREFILL_M_LONG):
+        out[f"prefill_per_shape_m{M}"] = prefill_shapes_config(
+            torch, tb, timer, problems, packed, w_scales, M, dev)
 
     # Batched decode: M=32 and 64 on the 28 gate and 28 down matrices.
     sub = [p for p in problems if p.proj in (4, 6)]
