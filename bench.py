@@ -73,6 +73,8 @@ def parse():
                          "vendor: the vendor int8 GEMM (torch._int_mm) on the prefill shapes, "
                          "a reference point for the int8 MFMA rate these shapes allow")
     ap.add_argument("--prefill-m", type=int, default=256)
+    ap.add_argument("--prefill-shapes", action="store_true",
+                    help="with --only prefill: also each projection shape alone")
     ap.add_argument("--decode-m", type=int, default=1,
                     help="rows of the headline decode sweep (1 unless profiling other sizes)")
     ap.add_argument("--decode-subset", choices=("all", "gate_down"), default="all",
@@ -291,8 +293,9 @@ def main():
         M = args.prefill_m
         log(f"[bench] prefill M={M} only")
         res = prefill_config(torch, tb, timer, problems, packed, w_scales, M, dev)
-        res["per_shape"] = prefill_shapes_config(torch, tb, timer, problems, packed, w_scales,
-                                                      M, dev)
+        if args.prefill_shapes:
+            res["per_shape"] = prefill_shapes_config(torch, tb, timer, problems, packed,
+                                                      w_scales, M, dev)
         print(json.dumps({"workload": f"prefill M={M} over {n_mat} matrices", **res}), flush=True)
         return
 
