@@ -24,7 +24,9 @@ summary in profiles/ when it was taken on the current kernel source.
 layer, each projection shape alone and grouped over its 28 layers, the launch
 floor, the sweep with all-zero codes against random ones, the dependent
 per-token chain, the I8_S encoder layers, the lookup-table sweep, the sweep at
-M = 4 and 16, prefill at M = 256 and 1800 over the 196 matrices and at M = 256
+M = 4 and 16 (each projection with its own input, and with the inputs a decoder
+shares: q, k, v one, gate and up another), prefill at M = 256 and 1800 over the
+196 matrices and at M = 256
 over one layer, prefill on each projection shape alone (its 28 matrices
 grouped, and one matrix per call), batched decode at M = 32 and 64);
 `cpu_baseline` times the CPU oracle on a bounded sample of the headline
@@ -780,6 +782,29 @@ def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, a
             "us_per_step": round(ms * 1e3, 2), "weight_GBps": round(pbytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(alg_bytes(M, problems) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
         del plans
+
+    # The same sweeps with the inputs a decoder shares: a layer's q, k and v
+    # read one buffer and its gate and up another, so the grouped call
+    # quantizes each such input once (112 inputs instead of 196).
+    for M in (4, 16):
+        shared = {}
+        xs_sh = []
+        for p in problems:
+            key = (p.layer, (0, 0, 0, 1, 2, 2, 3)[p.proj])
+            if key not in shared:
+                shared[key] = torch.from_numpy(synth.problem_activations(p, M)).to(dev)
+            xs_sh.append(shared[key])
+        ys = [torch.empty((M, p.N), dtype=torch.float32, device=dev) for p in problems]
+        plans = [tb.GroupedPlan(M, xs_sh, c, w_scales, ys, [p.N for p in problems],
+                                [p.K for p in problems]) for c in (packed, copy_b)]
+        ms = timer.time(lambda i=0: plans[i % 2].run(), 1000, warmup=200)
+        sb = (pbytes + sum(x.numel() * 4 for x in shared.values()) +
+              sum(M * p.N * 4 for p in problems) + 4 * len(problems))
+        out[f"decode_sweep_m{M}_shared_inputs"] = {
+            "us_per_step": round(ms * 1e3, 2), "weight_GBps": round(pbytes / (ms * 1e-3) / 1e9, 1),
+            "distinct_inputs": len(shared),
+            "frac_of_hbm_peak": round(sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        del plans, ys, xs_sh, shared
 
     # Prefill: M=256 (30 s of audio + prompt) and M=1800 (4 min of audio) over
     # the same 196 matrices.

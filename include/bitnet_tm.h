@@ -164,9 +164,13 @@ bitnet_status bitnet_ternary_matmul_q8(int64_t M, int64_t N, int64_t K, const in
  * problems_host host copy of the same array (read by the host to check shapes
  *               and size the launch); both must hold identical values.
  * workspace     at least bitnet_grouped_workspace_bytes(M, problems_host, count)
- *               bytes, 256-byte aligned.
+ *               bytes, 256-byte aligned (that function returns 0 for M < 1,
+ *               a NULL array or count outside 1..BITNET_MAX_GROUP).
  * count         1..BITNET_MAX_GROUP.
- * Every problem obeys the single-problem rules above.
+ * Every problem obeys the single-problem rules above.  Problems with the same
+ * x pointer and the same K (a decoder's q, k and v, or its gate and up) share
+ * one quantized copy of their rows: it is made once per call and takes
+ * workspace once.  The outputs are the same as with separate copies.
  * ------------------------------------------------------------------------ */
 typedef struct bitnet_problem {
     const float *x;          /* [M,K] fp32 activations                     */

@@ -60,12 +60,30 @@ bitnet_status check_problem(int64_t M, const bitnet_problem &p) {
   return BITNET_OK;
 }
 
-// Workspace offsets (256-byte units) of each problem of a group.
+// Index of the first problem of a group with the same x and K as problem i
+// (i itself when there is none).  Such problems read the same rows, so they
+// share one quantized copy: a decoder's q, k and v read one input, as do its
+// gate and up.
+int32_t input_owner(const bitnet_problem *ph, int32_t i) {
+  int32_t j = 0;
+  while (j < i && !(ph[j].x == ph[i].x && ph[j].K == ph[i].K)) ++j;
+  return j;
+}
+
+// Workspace offsets (256-byte units) of each problem of a group; problems that
+// share their input share its region.  count <= kMaxGroup.
 size_t group_ws(int64_t M, const bitnet_problem *ph, int32_t count, uint32_t *off) {
+  uint32_t own[kMaxGroup];
   size_t total = 0;
   for (int32_t i = 0; i < count; ++i) {
-    if (off) off[i] = (uint32_t)(total / 256);
-    total += align256(ws_layout(M, ph[i].K).total);
+    const int32_t j = input_owner(ph, i);
+    if (j == i) {
+      own[i] = (uint32_t)(total / 256);
+      total += align256(ws_layout(M, ph[i].K).total);
+    } else {
+      own[i] = own[j];
+    }
+    if (off) off[i] = own[i];
   }
   return total;
 }
@@ -201,7 +219,7 @@ bitnet_status bitnet_ternary_matmul_q8(int64_t M, int64_t N, int64_t K, const in
 
 size_t bitnet_grouped_workspace_bytes(int64_t M, const bitnet_problem *problems_host,
                                       int32_t count) {
-  if (M < 1 || !problems_host || count < 1) return 0;
+  if (M < 1 || !problems_host || count < 1 || count > kMaxGroup) return 0;
   return group_ws(M, problems_host, count, nullptr);
 }
 
@@ -272,14 +290,17 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
   }
   QuantTable qt;
   std::memset(&qt, 0, sizeof(qt));
-  qt.count = count;
+  qt.count = 0;
   qt.M = (int32_t)M;
+  // One quantization per distinct input.
   uint64_t qtotal = 0;
   for (int32_t s = 0; s < count; ++s) {
+    if (input_owner(problems_host, idx[s]) != idx[s]) continue;
     qtotal += (uint64_t)quant_grouped_blocks(M, problems_host[idx[s]].K);
     if (qtotal >= ((uint64_t)1 << 31)) return BITNET_ERR_SHAPE;
-    qt.wg_end[s] = (uint32_t)qtotal;
-    qt.order[s] = tab.order[s];
+    qt.wg_end[qt.count] = (uint32_t)qtotal;
+    qt.order[qt.count] = (uint16_t)idx[s];
+    ++qt.count;
   }
   std::memcpy(qt.ws_off, tab.ws_off, sizeof(qt.ws_off));
   st = from_hip(launch_quant_grouped(problems_dev, qt, ws, hs));

@@ -133,6 +133,30 @@ def test_grouped_validation(L):
     assert g(1, A, 2, ref, A, 16, NULL) == ERR["WORKSPACE"]
 
 
+def test_grouped_workspace_shares_inputs(L):
+    """Problems with the same x pointer and K take one workspace region; the
+    same pointer with another K (other rows) takes its own."""
+    from ternary_weight_decoder_amd.binding import BITNET_MAX_GROUP, bitnet_problem
+    f = L.bitnet_grouped_workspace_bytes
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32]
+    X1, X2 = A, A + (1 << 30)
+
+    def ws(probs, M=40, count=None):
+        arr = (bitnet_problem * len(probs))(*[bitnet_problem(x, A, A, A, n, k)
+                                              for x, n, k in probs])
+        return f(M, ctypes.addressof(arr), len(probs) if count is None else count)
+
+    one = ws([(X1, 1536, 1536)])
+    assert one > 0
+    assert ws([(X1, 1536, 1536), (X1, 256, 1536), (X1, 256, 1536)]) == one   # q, k, v
+    assert ws([(X1, 1536, 1536), (X2, 256, 1536)]) == 2 * one
+    assert ws([(X1, 1536, 1536), (X1, 1536, 128)]) == one + ws([(X1, 1536, 128)])
+    assert ws([(X1, 1536, 1536), (X2, 1536, 1536), (X1, 8960, 1536), (X2, 72, 1536)]) == 2 * one
+    assert ws([(X1, 1536, 1536)], count=BITNET_MAX_GROUP + 1) == 0
+    assert ws([(X1, 1536, 1536)], count=0) == 0
+
+
 def test_stages_validation(L):
     """Argument checks of the staged call; every case fails before any device
     work (the addresses are never dereferenced)."""

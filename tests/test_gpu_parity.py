@@ -384,3 +384,40 @@ def test_grouped_many_ragged_parity(tb, M):
     for i, (N, K) in enumerate(shapes):
         ref = oracle.ternary_matmul(xs[i], packs[i][0], packs[i][1], N)
         assert_y_matches(ys[i].cpu().numpy(), ref["y"], M)
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 40, 200])
+def test_grouped_shared_inputs_parity(tb, M):
+    """One layer called the way a decoder calls it: q, k and v read one input
+    buffer, gate and up another, and an extra problem reads the q input's buffer
+    with K = 128 (other rows, so a quantized copy of its own).  Each shared input
+    is quantized once; every output is checked against the oracle."""
+    import torch
+    say(f"[grouped] shared inputs M={M}")
+    x_attn = synth.activations(M, 1536, seed=5100)
+    x_o = synth.activations(M, 1536, seed=5101)
+    x_mlp = synth.activations(M, 1536, seed=5102)
+    x_down = synth.activations(M, 8960, seed=5103)
+    d_attn, d_o, d_mlp, d_down = (dev_tensor(x) for x in (x_attn, x_o, x_mlp, x_down))
+    reads = [(x_attn, d_attn), (x_attn, d_attn), (x_attn, d_attn), (x_o, d_o), (x_mlp, d_mlp),
+             (x_mlp, d_mlp), (x_down, d_down)]
+    shapes = [(N, K) for _, K, N in synth.PROJECTIONS]
+    xs = [h for h, _ in reads]
+    dxs = [d for _, d in reads]
+    shapes.append((200, 128))
+    xs.append(np.ascontiguousarray(x_attn.reshape(-1)[:M * 128].reshape(M, 128)))
+    dxs.append(d_attn)
+    Ws = [synth.normal_weights(N, K, seed=5200 + i) for i, (N, K) in enumerate(shapes)]
+    packs = [oracle.ternarize_pack(W) for W in Ws]
+    dp = [dev_tensor(p) for p, _ in packs]
+    ds = [dev_tensor(np.array([s], np.float32)) for _, s in packs]
+    ys = [torch.full((M, N), float("nan"), device="cuda:0") for N, _ in shapes]
+    plan = tb.GroupedPlan(M, dxs, dp, ds, ys, [N for N, _ in shapes], [K for _, K in shapes])
+    for _ in range(2):
+        plan.run()
+        torch.cuda.synchronize()
+        for i, (N, K) in enumerate(shapes):
+            ref = oracle.ternary_matmul(xs[i], packs[i][0], packs[i][1], N)
+            assert_y_matches(ys[i].cpu().numpy(), ref["y"], M)
+        for y in ys:
+            y.fill_(float("nan"))
