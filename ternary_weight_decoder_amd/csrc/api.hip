@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <utility>
 
 #include "bitnet_internal.hpp"
 #include "bitnet_variants.hpp"
@@ -60,28 +61,41 @@ bitnet_status check_problem(int64_t M, const bitnet_problem &p) {
   return BITNET_OK;
 }
 
-// Index of the first problem of a group with the same x and K as problem i
-// (i itself when there is none).  Such problems read the same rows, so they
-// share one quantized copy: a decoder's q, k and v read one input, as do its
-// gate and up.
-int32_t input_owner(const bitnet_problem *ph, int32_t i) {
-  int32_t j = 0;
-  while (j < i && !(ph[j].x == ph[i].x && ph[j].K == ph[i].K)) ++j;
-  return j;
+// owner[i]: the lowest index of the problems with the same x and K as
+// problem i (i itself when there is none).  Such problems read the same rows,
+// so they share one quantized copy: a decoder's q, k and v read one input, as
+// do its gate and up.  count <= kMaxGroup.
+void input_owners(const bitnet_problem *ph, int32_t count, int32_t *owner) {
+  int32_t ix[kMaxGroup];
+  for (int32_t i = 0; i < count; ++i) ix[i] = i;
+  const auto key = [&](int32_t i) {
+    return std::make_pair(reinterpret_cast<uintptr_t>(ph[i].x), ph[i].K);
+  };
+  std::sort(ix, ix + count, [&](int32_t a, int32_t b) {
+    return key(a) != key(b) ? key(a) < key(b) : a < b;
+  });
+  for (int32_t r = 0; r < count;) {
+    int32_t e = r;
+    while (e < count && key(ix[e]) == key(ix[r])) owner[ix[e++]] = ix[r];
+    r = e;
+  }
 }
 
 // Workspace offsets (256-byte units) of each problem of a group; problems that
 // share their input share its region.  count <= kMaxGroup.
-size_t group_ws(int64_t M, const bitnet_problem *ph, int32_t count, uint32_t *off) {
+size_t group_ws(int64_t M, const bitnet_problem *ph, int32_t count, uint32_t *off,
+                int32_t *owner_out = nullptr) {
+  int32_t owner_buf[kMaxGroup];
+  int32_t *owner = owner_out ? owner_out : owner_buf;
+  input_owners(ph, count, owner);
   uint32_t own[kMaxGroup];
   size_t total = 0;
   for (int32_t i = 0; i < count; ++i) {
-    const int32_t j = input_owner(ph, i);
-    if (j == i) {
+    if (owner[i] == i) {
       own[i] = (uint32_t)(total / 256);
       total += align256(ws_layout(M, ph[i].K).total);
     } else {
-      own[i] = own[j];
+      own[i] = own[owner[i]];
     }
     if (off) off[i] = own[i];
   }
@@ -238,7 +252,8 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
   std::memset(&tab, 0, sizeof(tab));
   tab.count = count;
   tab.M = (int32_t)M;
-  const size_t need = group_ws(M, problems_host, count, tab.ws_off);
+  int32_t owner[kMaxGroup];
+  const size_t need = group_ws(M, problems_host, count, tab.ws_off, owner);
   if (!workspace || workspace_bytes < need) return BITNET_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return BITNET_ERR_ALIGN;
   bitnet_status st = device_check();
@@ -295,7 +310,7 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
   // One quantization per distinct input.
   uint64_t qtotal = 0;
   for (int32_t s = 0; s < count; ++s) {
-    if (input_owner(problems_host, idx[s]) != idx[s]) continue;
+    if (owner[idx[s]] != idx[s]) continue;
     qtotal += (uint64_t)quant_grouped_blocks(M, problems_host[idx[s]].K);
     if (qtotal >= ((uint64_t)1 << 31)) return BITNET_ERR_SHAPE;
     qt.wg_end[qt.count] = (uint32_t)qtotal;
