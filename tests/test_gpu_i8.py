@@ -67,6 +67,26 @@ def test_i8_weight_quant_zero_and_ties(tb):
     np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
 
 
+def test_i8_weight_quant_golden_quotient(tb):
+    # hand-worked example C of i8_linear_worked.txt: W/s and W*fl32(1/s) round
+    # to different codes; the kernel must give the quotient's (9, not 10)
+    import torch
+    from conftest import read_golden
+    say("[i8] weight quantization golden quotient")
+    C = {}
+    for row in read_golden("i8_linear_worked.txt"):
+        if row[0] == "C":
+            C[row[1]] = row[2:]
+    W = np.zeros((1, 64), np.float32)
+    vals = [float.fromhex(h) for h in C["w_hex"]]
+    W[0, :len(vals)] = vals
+    q, s = tb.bitnet_i8_quant_weights(torch.from_numpy(W).to("cuda:0"))
+    assert s.item() == float(C["scale"][0])
+    qh = q.cpu().numpy()
+    np.testing.assert_array_equal(qh[0, :2], np.array([int(v) for v in C["q"]], np.int8))
+    assert not qh[0, 2:].any()
+
+
 def run_linear(tb, M, N, K, bias_on, relu, seed, zero_row=False):
     import torch
     dev = "cuda:0"

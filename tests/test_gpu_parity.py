@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from ternary_weight_decoder_amd import synth
-from conftest import read_golden
+from conftest import read_golden, ternarize_rounding_cases
 
 pytestmark = pytest.mark.gpu
 
@@ -151,6 +151,19 @@ def test_ternarize_golden_ties(tb):
     q, _ = oracle.unpack(packed, N, K)
     np.testing.assert_array_equal(q, np.stack([sign[0], 0 * sign[1], 0 * sign[2]]).astype(np.int8))
     assert any(r[0] == "example" for r in rows)
+
+
+@pytest.mark.parametrize("ex", ternarize_rounding_cases(), ids=lambda e: e["name"])
+def test_ternarize_golden_rounding_readings(tb, ex):
+    # the hand-worked cases that fix the mean's single rounding and the IEEE
+    # quotient W/m: the kernel must give the golden scale and codes
+    say(f"[ternarize_pack] golden rounding {ex['name']}")
+    N, K = ex["W"].shape
+    packed, s = gpu_ternarize_pack(tb, ex["W"])
+    assert float(s) == ex["scale"], (float(s).hex(), float(ex["scale"]).hex())
+    q, bad = oracle.unpack(packed, N, K)
+    assert bad == 0
+    np.testing.assert_array_equal(q, ex["codes"])
 
 
 # ---------------------------------------------------------------------------

@@ -130,3 +130,18 @@ def test_sampled_matches_full():
     acc, d, y = oracle.i8_linear_sampled(full["xq"], full["x_scale"], q, s, b, True, ms, ns)
     np.testing.assert_array_equal(acc, full["acc"][ms, ns])
     np.testing.assert_array_equal(y, full["y"][ms, ns])
+
+
+def test_weight_code_is_the_ieee_quotient():
+    # golden example C: the quotient W/s and the product W*fl32(1/s) fall on
+    # opposite sides of 9.5; the reading is the quotient.
+    C = golden()["C"]
+    W = np.zeros((1, 64), np.float32)
+    vals = [float.fromhex(h) for h in C["w_hex"][0]]
+    W[0, :len(vals)] = vals
+    q, s = oracle.i8_quant_weights(W)
+    assert s == np.float32(C["scale"][0][0])
+    np.testing.assert_array_equal(q[0, :2], np.array(C["q"][0], np.int8))
+    assert not q[0, 2:].any()
+    # the example discriminates: the reciprocal form rounds the other way
+    assert np.rint(np.float32(W[0, 1]) * (np.float32(1) / s)) == 10

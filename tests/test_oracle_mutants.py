@@ -34,11 +34,18 @@ MUTANTS = {
     "act_round": ("float t = rintf(p);          /* half to even */", "float t = roundf(p);"),
     # transposed operand: row n of codes read with the activation row index
     "transposed": ("int8_t c = q[n * K + k];", "int8_t c = q[(m % N) * K + k];"),
+    # code from W times the rounded reciprocal of m instead of the quotient W/m
+    "code_by_reciprocal": ("float r = w / m;", "float r = w * (1.0f / m);"),
+    # mean rounded twice: fp64 sum rounded to fp32, then an fp32 division
+    "mean_rounded_twice": ("return (float)(total / (double)(N * K));",
+                           "return (float)total / (float)(N * K);"),
 }
 
 # Slips in the I8_S functions, caught by the I8_S pins.
 I8_MUTANTS = {
     "i8_round_half_away": ("float t = rintf(W[i] / s);", "float t = roundf(W[i] / s);"),
+    # weight code from W times the rounded reciprocal of s instead of W/s
+    "i8_code_by_reciprocal": ("float t = rintf(W[i] / s);", "float t = rintf(W[i] * (1.0f / s));"),
     "i8_scale_128": ("float s = a / 127.0f;                 /* fp32, correctly rounded */",
                      "float s = a / 128.0f;"),
     "i8_transposed": ("s += (int64_t)xq[m * K + k] * (int64_t)q[n * K + k];",

@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from ternary_weight_decoder_amd import synth
-from conftest import read_golden
+from conftest import read_golden, ternarize_rounding_cases
 
 
 def _facts():
@@ -440,3 +440,42 @@ def test_sampled_matches_full():
     acc, y = oracle.matmul_sampled(full["xq"], full["x_scale"], packed, s, N, ms, ns)
     np.testing.assert_array_equal(acc, full["acc"][ms, ns])
     np.testing.assert_array_equal(y, full["y"][ms, ns])
+
+
+# ---------------------------------------------------------------------------
+# Readings C2 (mean rounded once) and C3 (IEEE quotient W/m): hand-worked cases
+# ---------------------------------------------------------------------------
+
+def _rn32(x: Fraction) -> Fraction:
+    """Round an exact rational to the nearest fp32 (ties to even), by search on
+    the fp32 grid around it; normal range only."""
+    lo = np.float32(float(x))
+    cands = [np.nextafter(lo, np.float32(-np.inf)), lo, np.nextafter(lo, np.float32(np.inf))]
+    def key(v):
+        return (abs(Fraction(float(v)) - x), int(np.array([v], np.float32).view(np.uint32)[0]) & 1)
+    return Fraction(float(min(cands, key=key)))
+
+
+@pytest.mark.parametrize("ex", ternarize_rounding_cases(), ids=lambda e: e["name"])
+def test_ternarize_golden_rounding_readings(ex):
+    q, s = oracle.ternarize(ex["W"])
+    assert float(s) == ex["scale"], (float(s).hex(), ex["scale"])
+    np.testing.assert_array_equal(q, ex["codes"])
+
+
+def test_rounding_goldens_discriminate():
+    # The worked cases only pin C2/C3 if the rejected forms really give other
+    # results on them; check that with exact rational arithmetic.
+    ex = {e["name"]: e for e in ternarize_rounding_cases()}
+    W = ex["div_vs_recip"]["W"]
+    m = Fraction(ex["div_vs_recip"]["scale"])
+    assert sum(Fraction(float(v)) for v in W.ravel()) == m * W.size
+    w = Fraction(float(W[0, 0]))
+    half = Fraction(1, 2)
+    assert _rn32(w / m) > half                       # quotient: code 1
+    assert _rn32(w * _rn32(1 / m)) == half           # reciprocal: tie to even, code 0
+    W = ex["single_rounding"]["W"]
+    T = sum(Fraction(float(v)) for v in W.ravel())
+    once = _rn32(T / W.size)
+    twice = _rn32(_rn32(T) / W.size)
+    assert once == Fraction(ex["single_rounding"]["scale"]) and twice != once
