@@ -67,6 +67,10 @@ def lib():
         L.oracle_i8_linear.argtypes = [i64, i64, i64, p, p, f32, p, ctypes.c_int, p, p, p, p]
         L.oracle_i8_linear_sampled.argtypes = [i64, i64, p, p, p, f32, p, ctypes.c_int, p, p,
                                                i64, p, p, p]
+        L.oracle_rowq_quant_weights.argtypes = [p, i64, i64, p, p]
+        L.oracle_rowq_embed.argtypes = [p, i64, p, p, i64, i64, p]
+        L.oracle_rowq_linear.argtypes = [i64, i64, i64, p, p, p, p, p, p, p]
+        L.oracle_rowq_linear_sampled.argtypes = [i64, p, p, p, p, p, p, i64, p, p]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -257,3 +261,58 @@ def i8_linear_sampled(xq, x_scale, q, w_scale, bias, relu, ms, ns):
                                    None if b is None else _ptr(b), int(bool(relu)), _ptr(ms),
                                    _ptr(ns), ms.size, _ptr(acc), _ptr(d), _ptr(y))
     return acc, d, y
+
+
+# ---- 8-bit weights, one scale per row: embeddings and lm_head ---------------
+
+def rowq_quant_weights(W: np.ndarray):
+    """fp32 [N,K] -> (q int8 [N,K], w_scale float32 [N]): one absmax scale per row."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    q = np.empty((N, K), np.int8)
+    s = np.empty(N, np.float32)
+    lib().oracle_rowq_quant_weights(_ptr(W), N, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def rowq_embed(ids: np.ndarray, q: np.ndarray, w_scale: np.ndarray) -> np.ndarray:
+    """Embedding rows of the int8 table for the token ids -> fp32 [T, K]."""
+    ids = _c(ids, np.int32)
+    q = _c(q, np.int8)
+    s = _c(w_scale, np.float32)
+    N, K = q.shape
+    out = np.empty((ids.size, K), np.float32)
+    lib().oracle_rowq_embed(_ptr(ids), ids.size, _ptr(q), _ptr(s), N, K, _ptr(out))
+    return out
+
+
+def rowq_linear(x: np.ndarray, q: np.ndarray, w_scale: np.ndarray):
+    """lm_head over the int8 table -> dict(y, xq, x_scale, acc)."""
+    x = _c(x, np.float32)
+    q = _c(q, np.int8)
+    s = _c(w_scale, np.float32)
+    M, K = x.shape
+    N = q.shape[0]
+    y = np.empty((M, N), np.float32)
+    xq = np.empty((M, K), np.int8)
+    xs = np.empty(M, np.float32)
+    acc = np.empty((M, N), np.int32)
+    lib().oracle_rowq_linear(M, N, K, _ptr(x), _ptr(q), _ptr(s), _ptr(y), _ptr(xq), _ptr(xs),
+                             _ptr(acc))
+    return {"y": y, "xq": xq, "x_scale": xs, "acc": acc}
+
+
+def rowq_linear_sampled(xq, x_scale, q, w_scale, ms, ns):
+    """acc and y of the lm_head at the selected (m, n) pairs only."""
+    xq = _c(xq, np.int8)
+    xs = _c(x_scale, np.float32)
+    q = _c(q, np.int8)
+    s = _c(w_scale, np.float32)
+    ms = _c(ms, np.int64)
+    ns = _c(ns, np.int64)
+    K = q.shape[1]
+    acc = np.empty(ms.size, np.int32)
+    y = np.empty(ms.size, np.float32)
+    lib().oracle_rowq_linear_sampled(K, _ptr(xq), _ptr(xs), _ptr(q), _ptr(s), _ptr(ms),
+                                     _ptr(ns), ms.size, _ptr(acc), _ptr(y))
+    return acc, y

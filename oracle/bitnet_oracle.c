@@ -42,9 +42,14 @@
  *    once to fp32 (the pages are silent on the epilogue; this is the plain
  *    reading of "dequantize both factors").
  *
+ *  - Embeddings and lm_head: an 8-bit table with one scale per row (ONNX
+ *    card, Quantization table, row "Embeddings / lm_head"); see the section
+ *    of that name below.
+ *
  * Parity pins for every function live in the CPU tests; none is "parity
  * unpinned" except the correspondence of the packed bit layout to the original
- * GGUF I2_S files, which are not available (the layout here is our own spec).
+ * GGUF I2_S files, and of the 8-bit table to the GGUF build's Q6_K blocks,
+ * neither of which is available (the layouts here are our own spec).
  */
 #include <math.h>
 #include <stdint.h>
@@ -350,5 +355,95 @@ void oracle_i8_linear_sampled(int64_t N, int64_t K, const int8_t *xq, const floa
         double v = d[i] + (bias ? (double)bias[n] : 0.0);
         if (relu && !(v > 0.0)) v = 0.0;
         y[i] = (float)v;
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* 8-bit weights with one scale per row: embeddings and lm_head             */
+/* ---------------------------------------------------------------------- */
+/*
+ * The decoder's token embeddings and its lm_head are stored at 8 bits with
+ * one scale per row (per vocabulary entry) in the ONNX build, Q6_K in the
+ * GGUF build (ONNX model card "multimodalart/VibeVoice-ASR-BitNet-ONNX",
+ * Quantization table, row "Embeddings / lm_head": "8-bit per-row /
+ * per-column"; xujun.org article, heterogeneous-quantization section: I2_S
+ * plus Q6_K embeddings).  The table is [V, K] (vocabulary x hidden); a row
+ * of it is one token's embedding, and, read as the lm_head weight, one output
+ * column's weights, so the same per-row scale serves both readings of the
+ * card's cell.  The card gives no formula.  Readings used here:
+ *  - per row n: a = max_k |W[n,k]|, s[n] = fl32(a / 127) (the dequant
+ *    multiplier), q = clamp(rint(fl32(W / s[n])), -127, 127); a zero row
+ *    gives s[n] = 0 and q = 0 (the same formula as the I8_S weights above,
+ *    applied to each row on its own);
+ *  - embedding lookup: e[t,k] = fl32(q[id_t,k] * s[id_t]); an id outside
+ *    [0, V) gives a zero row;
+ *  - lm_head: activations quantized per row exactly as oracle_quant_act,
+ *    acc = sum_k xq * q in int32, y[m,n] = acc * s[n] / x_scale[m] in fp64,
+ *    rounded once to fp32.
+ */
+
+void oracle_rowq_quant_weights(const float *W, int64_t N, int64_t K, int8_t *q,
+                               float *w_scale) {
+    for (int64_t n = 0; n < N; ++n) {
+        const float *row = W + n * K;
+        float a = 0.0f;                       /* max |W| over row n */
+        for (int64_t k = 0; k < K; ++k) a = fabsf(row[k]) > a ? fabsf(row[k]) : a;
+        if (a == 0.0f) {
+            memset(q + n * K, 0, (size_t)K);
+            w_scale[n] = 0.0f;
+            continue;
+        }
+        float s = a / 127.0f;                 /* row scale: fp32, correctly rounded */
+        w_scale[n] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            float t = rintf(row[k] / s);      /* fp32 quotient, half to even */
+            if (t > 127.0f) t = 127.0f;
+            if (t < -127.0f) t = -127.0f;
+            q[n * K + k] = (int8_t)t;
+        }
+    }
+}
+
+void oracle_rowq_embed(const int32_t *ids, int64_t T, const int8_t *q, const float *w_scale,
+                       int64_t N, int64_t K, float *out) {
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t id = ids[t];
+        for (int64_t k = 0; k < K; ++k)
+            out[t * K + k] = (id >= 0 && id < N)
+                                 ? (float)((double)q[id * K + k] * (double)w_scale[id])
+                                 : 0.0f;
+    }
+}
+
+/* The whole lm_head: y[m,n] = (sum_k xq[m,k] * q[n,k]) * s[n] / x_scale[m].
+ * xq_out / x_scale_out / acc_out may be NULL. */
+void oracle_rowq_linear(int64_t M, int64_t N, int64_t K, const float *x, const int8_t *q,
+                        const float *w_scale, float *y, int8_t *xq_out, float *x_scale_out,
+                        int32_t *acc_out) {
+    int8_t *xq = (int8_t *)malloc((size_t)(M * K));
+    float *xs = (float *)malloc(sizeof(float) * (size_t)M);
+    int32_t *acc = (int32_t *)malloc(sizeof(int32_t) * (size_t)(M * N));
+    oracle_quant_act(x, M, K, xq, xs);
+    oracle_i8_matmul(xq, q, M, N, K, acc);
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            y[m * N + n] = (float)((double)acc[m * N + n] * (double)w_scale[n] /
+                                   (double)xs[m]);
+    if (xq_out) memcpy(xq_out, xq, (size_t)(M * K));
+    if (x_scale_out) memcpy(x_scale_out, xs, sizeof(float) * (size_t)M);
+    if (acc_out) memcpy(acc_out, acc, sizeof(int32_t) * (size_t)(M * N));
+    free(xq); free(xs); free(acc);
+}
+
+/* Selected outputs of the lm_head from the oracle's own quantized rows. */
+void oracle_rowq_linear_sampled(int64_t K, const int8_t *xq, const float *x_scale,
+                                const int8_t *q, const float *w_scale, const int64_t *ms,
+                                const int64_t *ns, int64_t count, int32_t *acc, float *y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t m = ms[i], n = ns[i], dot = 0;
+        for (int64_t k = 0; k < K; ++k) dot += (int64_t)q[n * K + k] * (int64_t)xq[m * K + k];
+        acc[i] = (int32_t)dot;
+        y[i] = (float)((double)acc[i] * (double)w_scale[n] / (double)x_scale[m]);
     }
 }

@@ -57,6 +57,28 @@ I8_MUTANTS = {
 }
 
 
+# Slips in the 8-bit per-row table (embeddings and lm_head), caught by its pins.
+ROWQ_MUTANTS = {
+    # one scale for the whole table instead of one per row
+    "rowq_per_tensor": ("for (int64_t k = 0; k < K; ++k) a = fabsf(row[k]) > a ? fabsf(row[k]) : a;",
+                        "for (int64_t k = 0; k < N * K; ++k) a = fabsf(W[k]) > a ? fabsf(W[k]) : a;"),
+    "rowq_round_half_away": ("float t = rintf(row[k] / s);", "float t = roundf(row[k] / s);"),
+    "rowq_code_by_reciprocal": ("float t = rintf(row[k] / s);",
+                                "float t = rintf(row[k] * (1.0f / s));"),
+    "rowq_scale_127_5": ("float s = a / 127.0f;                 /* row scale: fp32, correctly rounded */",
+                         "float s = a / 127.5f;"),
+    # the lm_head output scaled by the activation row's index into the table scales
+    "rowq_scale_index": ("(double)acc[m * N + n] * (double)w_scale[n] /",
+                         "(double)acc[m * N + n] * (double)w_scale[m % N] /"),
+    # embedding scaled by the neighbouring row's scale
+    "rowq_embed_scale_row": ("(float)((double)q[id * K + k] * (double)w_scale[id])",
+                             "(float)((double)q[id * K + k] * (double)w_scale[(id + 1) % N])"),
+    # embedding rows read transposed
+    "rowq_embed_transposed": ("(float)((double)q[id * K + k] * (double)w_scale[id])",
+                              "(float)((double)q[(k % N) * K + id % K] * (double)w_scale[id])"),
+}
+
+
 def run_pins_on_mutant(tmp_path, old, new, pin_file):
     src = open(os.path.join(ROOT, "oracle", "bitnet_oracle.c")).read()
     assert old in src, "mutation site not found"
@@ -83,3 +105,10 @@ def test_i8_pins_reject_mutant(name, tmp_path):
     old, new = I8_MUTANTS[name]
     r = run_pins_on_mutant(tmp_path, old, new, "test_oracle_i8_pins.py")
     assert r.returncode != 0, f"I8_S pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(ROWQ_MUTANTS))
+def test_rowq_pins_reject_mutant(name, tmp_path):
+    old, new = ROWQ_MUTANTS[name]
+    r = run_pins_on_mutant(tmp_path, old, new, "test_oracle_rowq_pins.py")
+    assert r.returncode != 0, f"per-row table pins did not catch mutant {name}:\n{r.stdout[-2000:]}"

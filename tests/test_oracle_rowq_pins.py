@@ -1,0 +1,124 @@
+"""CPU pins of the oracle's 8-bit per-row table (the decoder's embeddings and
+lm_head) against values fixed by hand and by the mathematics, independent of
+the oracle itself: the worked example in tests/golden/rowq_worked.txt, the
+reduction of each row to the per-tensor int8 quantization (pinned on its own),
+power-of-two scale invariance per row, numpy's integer matmul, the exact
+rational dequantization bound, and exact fp32 products for the embedding.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from conftest import read_golden
+from ternary_weight_decoder_amd import synth
+
+
+def golden():
+    g = {}
+    for r in read_golden("rowq_worked.txt"):
+        g.setdefault(r[0], []).append(r[1:])
+    return g
+
+
+def u32(h):
+    return np.array([int(h, 16)], np.uint32).view(np.float32)[0]
+
+
+def test_worked_example():
+    g = golden()
+    W = np.array([[float.fromhex(v) for v in r[1:]] for r in g["w_hex"]], np.float32)
+    q, s = oracle.rowq_quant_weights(W)
+    np.testing.assert_array_equal(q, np.array([r[1:] for r in g["q"]], np.int8))
+    assert s.tobytes() == np.array([u32(h) for h in g["scale_bits"][0]], np.float32).tobytes()
+    x = np.array([r[1:] for r in g["x"]], np.float32)
+    out = oracle.rowq_linear(x, q, s)
+    np.testing.assert_array_equal(out["acc"], np.array([r[1:] for r in g["acc"]], np.int32))
+    want = np.array([[u32(h) for h in r[1:]] for r in g["y_bits"]], np.float32)
+    assert out["y"].tobytes() == want.tobytes()
+    e = oracle.rowq_embed(np.array(g["ids"][0], np.int32), q, s)
+    want = np.array([[float.fromhex(v) for v in r[1:]] for r in g["emb_hex"]], np.float32)
+    assert e.tobytes() == want.tobytes()
+
+
+def test_rows_reduce_to_the_per_tensor_quantization():
+    # each row alone, through the (separately pinned) per-tensor int8
+    # quantization, must give that row's codes and scale
+    W = synth.student_t_weights(37, 320, 11)
+    W[5] = 0.0
+    W[9, 17] = np.float32(-0.5)          # a row whose maximum is a negative entry
+    q, s = oracle.rowq_quant_weights(W)
+    for n in range(W.shape[0]):
+        qn, sn = oracle.i8_quant_weights(W[n:n + 1])
+        np.testing.assert_array_equal(q[n], qn[0])
+        assert s[n] == sn
+
+
+def test_row_scale_invariance_and_bound():
+    rng = np.random.default_rng(3)
+    W = synth.normal_weights(64, 256, 4)
+    q, s = oracle.rowq_quant_weights(W)
+    f = np.float32(2.0) ** rng.integers(-6, 7, size=(64, 1)).astype(np.float32)
+    q2, s2 = oracle.rowq_quant_weights((W * f).astype(np.float32))
+    np.testing.assert_array_equal(q2, q)
+    np.testing.assert_array_equal(s2, (s * f[:, 0]).astype(np.float32))
+    assert (np.abs(q).max(axis=1) == 127).all()
+    r = W.astype(np.float64) / s[:, None].astype(np.float64)
+    assert np.abs(q - r).max() <= 0.5 + 1e-4
+    assert (np.sign(q) * np.sign(W) >= 0).all()
+
+
+def test_lm_head_matches_integer_product_and_exact_dequant():
+    W = synth.normal_weights(300, 384, 8)
+    x = synth.activations(5, 384, 9)
+    q, s = oracle.rowq_quant_weights(W)
+    out = oracle.rowq_linear(x, q, s)
+    xq, xs = oracle.quant_act(x)
+    np.testing.assert_array_equal(out["xq"], xq)
+    acc = xq.astype(np.int64) @ q.astype(np.int64).T
+    np.testing.assert_array_equal(out["acc"], acc.astype(np.int32))
+    for m, n in [(0, 0), (1, 17), (4, 299), (2, 150), (3, 64)]:
+        exact = Fraction(int(acc[m, n])) * Fraction(float(s[n])) / Fraction(float(xs[m]))
+        got = Fraction(float(out["y"][m, n]))
+        ulp = abs(float(np.spacing(out["y"][m, n])))
+        assert abs(got - exact) <= Fraction(ulp) / 2
+
+
+def test_lm_head_scale_follows_the_column():
+    # scaling one table row by 2 doubles that output column and no other
+    W = synth.normal_weights(16, 128, 12)
+    x = synth.activations(3, 128, 13)
+    q, s = oracle.rowq_quant_weights(W)
+    base = oracle.rowq_linear(x, q, s)["y"]
+    s2 = s.copy()
+    s2[7] *= np.float32(2.0)
+    y2 = oracle.rowq_linear(x, q, s2)["y"]
+    np.testing.assert_array_equal(y2[:, 7], base[:, 7] * np.float32(2.0))
+    np.testing.assert_array_equal(np.delete(y2, 7, axis=1), np.delete(base, 7, axis=1))
+
+
+def test_embedding_is_the_scaled_row():
+    W = synth.normal_weights(50, 256, 14)
+    q, s = oracle.rowq_quant_weights(W)
+    ids = np.array([0, 49, 7, 7, -1, 50, 23], np.int32)
+    e = oracle.rowq_embed(ids, q, s)
+    for t, i in enumerate(ids):
+        if 0 <= i < 50:
+            # one IEEE fp32 product of two exact inputs
+            np.testing.assert_array_equal(e[t], q[i].astype(np.float32) * s[i])
+        else:
+            assert not e[t].any()
+
+
+def test_sampled_matches_full():
+    W = synth.normal_weights(97, 256, 15)
+    x = synth.activations(4, 256, 16)
+    q, s = oracle.rowq_quant_weights(W)
+    full = oracle.rowq_linear(x, q, s)
+    rng = np.random.default_rng(0)
+    ms = rng.integers(0, 4, 40)
+    ns = rng.integers(0, 97, 40)
+    acc, y = oracle.rowq_linear_sampled(full["xq"], full["x_scale"], q, s, ms, ns)
+    np.testing.assert_array_equal(acc, full["acc"][ms, ns])
+    np.testing.assert_array_equal(y, full["y"][ms, ns])
