@@ -71,6 +71,9 @@ def lib():
         L.oracle_rowq_embed.argtypes = [p, i64, p, p, i64, i64, p]
         L.oracle_rowq_linear.argtypes = [i64, i64, i64, p, p, p, p, p, p, p]
         L.oracle_rowq_linear_sampled.argtypes = [i64, p, p, p, p, p, p, i64, p, p]
+        L.oracle_i8_linear_rows.argtypes = [i64, i64, i64, p, p, p, p, ctypes.c_int, p, p, p, p]
+        L.oracle_i8_linear_rows_sampled.argtypes = [i64, p, p, p, p, p, ctypes.c_int, p, p, i64,
+                                                    p, p, p]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -316,3 +319,44 @@ def rowq_linear_sampled(xq, x_scale, q, w_scale, ms, ns):
     lib().oracle_rowq_linear_sampled(K, _ptr(xq), _ptr(xs), _ptr(q), _ptr(s), _ptr(ms),
                                      _ptr(ns), ms.size, _ptr(acc), _ptr(y))
     return acc, y
+
+
+# ---- I8_S with one weight scale per output channel ---------------------------
+
+def i8_linear_rows(x: np.ndarray, q: np.ndarray, w_scale: np.ndarray, bias=None,
+                   relu: bool = False):
+    """I8_S layer with per-channel weight scales (q, w_scale from
+    rowq_quant_weights) -> dict(y, xq, x_scale, acc)."""
+    x = _c(x, np.float32)
+    q = _c(q, np.int8)
+    s = _c(w_scale, np.float32)
+    M, K = x.shape
+    N = q.shape[0]
+    b = None if bias is None else _c(bias, np.float32)
+    y = np.empty((M, N), np.float32)
+    xq = np.empty((M, K), np.int8)
+    xs = np.empty(M, np.float32)
+    acc = np.empty((M, N), np.int32)
+    lib().oracle_i8_linear_rows(M, N, K, _ptr(x), _ptr(q), _ptr(s),
+                                None if b is None else _ptr(b), int(bool(relu)), _ptr(y),
+                                _ptr(xq), _ptr(xs), _ptr(acc))
+    return {"y": y, "xq": xq, "x_scale": xs, "acc": acc}
+
+
+def i8_linear_rows_sampled(xq, x_scale, q, w_scale, bias, relu, ms, ns):
+    """acc, d = acc * w_scale[n] / x_scale[m] (fp64) and y at the (m, n) pairs."""
+    xq = _c(xq, np.int8)
+    xs = _c(x_scale, np.float32)
+    q = _c(q, np.int8)
+    s = _c(w_scale, np.float32)
+    K = q.shape[1]
+    ms = _c(ms, np.int64)
+    ns = _c(ns, np.int64)
+    b = None if bias is None else _c(bias, np.float32)
+    acc = np.empty(ms.size, np.int32)
+    d = np.empty(ms.size, np.float64)
+    y = np.empty(ms.size, np.float32)
+    lib().oracle_i8_linear_rows_sampled(K, _ptr(xq), _ptr(xs), _ptr(q), _ptr(s),
+                                        None if b is None else _ptr(b), int(bool(relu)),
+                                        _ptr(ms), _ptr(ns), ms.size, _ptr(acc), _ptr(d), _ptr(y))
+    return acc, d, y

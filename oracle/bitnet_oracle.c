@@ -447,3 +447,55 @@ void oracle_rowq_linear_sampled(int64_t K, const int8_t *xq, const float *x_scal
         y[i] = (float)((double)acc[i] * (double)w_scale[n] / (double)x_scale[m]);
     }
 }
+
+/* ---------------------------------------------------------------------- */
+/* I8_S with one weight scale per output channel                            */
+/* ---------------------------------------------------------------------- */
+/*
+ * The ONNX build of the audio encoders stores "int8 per-channel weights"
+ * (ONNX model card "multimodalart/VibeVoice-ASR-BitNet-ONNX", Quantization
+ * table, row "VAE encoders").  Per output channel n the weights are
+ * quantized exactly as a table row above (oracle_rowq_quant_weights), the
+ * activations per row as oracle_quant_act, and
+ *   y[m,n] = relu?(acc[m,n] * w_scale[n] / x_scale[m] + bias[n])
+ * in fp64, rounded once to fp32.
+ */
+void oracle_i8_linear_rows(int64_t M, int64_t N, int64_t K, const float *x, const int8_t *q,
+                           const float *w_scale, const float *bias, int relu, float *y,
+                           int8_t *xq_out, float *x_scale_out, int32_t *acc_out) {
+    int8_t *xq = (int8_t *)malloc((size_t)(M * K));
+    float *xs = (float *)malloc(sizeof(float) * (size_t)M);
+    int32_t *acc = (int32_t *)malloc(sizeof(int32_t) * (size_t)(M * N));
+    oracle_quant_act(x, M, K, xq, xs);
+    oracle_i8_matmul(xq, q, M, N, K, acc);
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double v = (double)acc[m * N + n] * (double)w_scale[n] / (double)xs[m];
+            if (bias) v += (double)bias[n];          /* channel bias */
+            if (relu && v <= 0.0) v = 0.0;
+            y[m * N + n] = (float)v;
+        }
+    if (xq_out) memcpy(xq_out, xq, (size_t)(M * K));
+    if (x_scale_out) memcpy(x_scale_out, xs, sizeof(float) * (size_t)M);
+    if (acc_out) memcpy(acc_out, acc, sizeof(int32_t) * (size_t)(M * N));
+    free(xq); free(xs); free(acc);
+}
+
+/* Selected outputs of the per-channel layer from the oracle's own quantized
+ * rows: acc[i], d[i] = acc * w_scale[n] / x_scale[m] (fp64, before bias and
+ * ReLU) and y[i]. */
+void oracle_i8_linear_rows_sampled(int64_t K, const int8_t *xq, const float *x_scale,
+                                   const int8_t *q, const float *w_scale, const float *bias,
+                                   int relu, const int64_t *ms, const int64_t *ns,
+                                   int64_t count, int32_t *acc, double *d, float *y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t m = ms[i], n = ns[i], dot = 0;
+        for (int64_t k = 0; k < K; ++k) dot += (int64_t)q[n * K + k] * (int64_t)xq[m * K + k];
+        acc[i] = (int32_t)dot;
+        d[i] = (double)acc[i] * (double)w_scale[n] / (double)x_scale[m];
+        double v = d[i] + (bias ? (double)bias[n] : 0.0);
+        if (relu && v <= 0.0) v = 0.0;
+        y[i] = (float)v;
+    }
+}

@@ -73,6 +73,15 @@ ROWQ_MUTANTS = {
     # embedding scaled by the neighbouring row's scale
     "rowq_embed_scale_row": ("(float)((double)q[id * K + k] * (double)w_scale[id])",
                              "(float)((double)q[id * K + k] * (double)w_scale[(id + 1) % N])"),
+    # per-channel layer: the bias of the activation row's index
+    "rows_bias_index": ("if (bias) v += (double)bias[n];          /* channel bias */",
+                        "if (bias) v += (double)bias[m % N];"),
+    # per-channel layer: ReLU keeps the negative part
+    "rows_relu_inverted": ("if (relu && v <= 0.0) v = 0.0;\n            y[m * N + n] = (float)v;",
+                           "if (relu && v > 0.0) v = 0.0;\n            y[m * N + n] = (float)v;"),
+    # per-channel layer: one channel's scale for all
+    "rows_scale_first": ("double v = (double)acc[m * N + n] * (double)w_scale[n] / (double)xs[m];",
+                         "double v = (double)acc[m * N + n] * (double)w_scale[0] / (double)xs[m];"),
     # embedding rows read transposed
     "rowq_embed_transposed": ("(float)((double)q[id * K + k] * (double)w_scale[id])",
                               "(float)((double)q[(k % N) * K + id % K] * (double)w_scale[id])"),

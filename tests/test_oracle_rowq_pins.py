@@ -122,3 +122,69 @@ def test_sampled_matches_full():
     acc, y = oracle.rowq_linear_sampled(full["xq"], full["x_scale"], q, s, ms, ns)
     np.testing.assert_array_equal(acc, full["acc"][ms, ns])
     np.testing.assert_array_equal(y, full["y"][ms, ns])
+
+
+# ---- I8_S with per-channel weight scales -------------------------------------
+
+def test_per_channel_layer_worked_example():
+    g = golden()
+    W = np.array([[float.fromhex(v) for v in r[1:]] for r in g["w_hex"]], np.float32)
+    q, s = oracle.rowq_quant_weights(W)
+    x = np.array([r[1:] for r in g["x"]], np.float32)
+    b = np.array(g["bias"][0], np.float32)
+    for relu, key in ((False, "yb_bits"), (True, "ybr_bits")):
+        out = oracle.i8_linear_rows(x, q, s, b, relu=relu)
+        np.testing.assert_array_equal(out["acc"], np.array([r[1:] for r in g["acc"]], np.int32))
+        want = np.array([[u32(h) for h in r[1:]] for r in g[key]], np.float32)
+        assert out["y"].tobytes() == want.tobytes(), key
+    # without bias or ReLU it is the lm_head's output
+    out = oracle.i8_linear_rows(x, q, s)
+    want = np.array([[u32(h) for h in r[1:]] for r in g["y_bits"]], np.float32)
+    assert out["y"].tobytes() == want.tobytes()
+
+
+@pytest.mark.parametrize("relu", [False, True])
+def test_per_channel_layer_with_equal_scales_is_the_per_tensor_layer(relu):
+    # every channel scale equal to the tensor scale: the separately pinned
+    # per-tensor I8_S layer, bit for bit
+    W = synth.normal_weights(70, 192, 20)
+    x = synth.activations(9, 192, 21)
+    b = synth.normal_weights(1, 70, 22, std=0.1)[0]
+    q, s = oracle.i8_quant_weights(W)
+    ref = oracle.i8_linear(x, q, s, b, relu=relu)
+    out = oracle.i8_linear_rows(x, q, np.full(70, s, np.float32), b, relu=relu)
+    assert out["y"].tobytes() == ref["y"].tobytes()
+    np.testing.assert_array_equal(out["acc"], ref["acc"])
+
+
+def test_per_channel_layer_bias_and_scale_follow_the_channel():
+    W = synth.normal_weights(12, 128, 23)
+    x = synth.activations(4, 128, 24)
+    q, s = oracle.rowq_quant_weights(W)
+    base = oracle.i8_linear_rows(x, q, s)["y"]
+    b = np.zeros(12, np.float32)
+    b[5] = np.float32(0.75)
+    y = oracle.i8_linear_rows(x, q, s, b)["y"]
+    np.testing.assert_array_equal(np.delete(y, 5, axis=1), np.delete(base, 5, axis=1))
+    exact = [Fraction(float(v)) + Fraction(3, 4) for v in base[:, 5]]
+    assert all(abs(Fraction(float(g)) - e) <= Fraction(abs(float(np.spacing(g)))) for g, e in
+               zip(y[:, 5], exact))
+    s2 = s.copy()
+    s2[3] *= np.float32(4.0)
+    y2 = oracle.i8_linear_rows(x, q, s2)["y"]
+    np.testing.assert_array_equal(y2[:, 3], base[:, 3] * np.float32(4.0))
+    r = oracle.i8_linear_rows(x, q, s, relu=True)["y"]
+    np.testing.assert_array_equal(r, np.maximum(base, 0))
+
+
+def test_per_channel_sampled_matches_full():
+    W = synth.normal_weights(40, 256, 25)
+    x = synth.activations(6, 256, 26)
+    b = synth.normal_weights(1, 40, 27, std=0.1)[0]
+    q, s = oracle.rowq_quant_weights(W)
+    full = oracle.i8_linear_rows(x, q, s, b, relu=True)
+    ms = np.arange(6).repeat(40)
+    ns = np.tile(np.arange(40), 6)
+    acc, d, y = oracle.i8_linear_rows_sampled(full["xq"], full["x_scale"], q, s, b, True, ms, ns)
+    np.testing.assert_array_equal(acc, full["acc"].ravel())
+    np.testing.assert_array_equal(y, full["y"].ravel())
