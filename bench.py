@@ -66,12 +66,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--layers", type=int, default=28)
     ap.add_argument("--only",
-                    choices=("all", "decode", "prefill", "chain", "lut", "i8", "copy", "vendor"),
+                    choices=("all", "decode", "prefill", "chain", "lut", "i8", "lmhead", "copy",
+                             "vendor"),
                     default="all",
                     help="decode: headline only; prefill: one prefill step size (--prefill-m) "
                          "only; chain: the dependent per-token chain only (graph of grouped "
                          "launches, and the staged call); lut: the lookup-table variant of "
-                         "the M=1 sweep only; i8: the int8 x int8 encoder layers only; copy: 1 GiB copy probe used to calibrate the byte counters; "
+                         "the M=1 sweep only; i8: the int8 x int8 encoder layers only; lmhead: the "
+                         "8-bit embedding / lm_head table only; copy: 1 GiB copy probe used to calibrate the byte counters; "
                          "vendor: the vendor int8 GEMM (torch._int_mm) on the prefill shapes, "
                          "a reference point for the int8 MFMA rate these shapes allow")
     ap.add_argument("--prefill-m", type=int, default=256)
@@ -232,6 +234,11 @@ def main():
     if args.only == "i8":
         log("[bench] I8_S encoder layers only")
         print(json.dumps(i8_configs(torch, tb, synth, timer, dev, steps=args.steps)), flush=True)
+        return
+    if args.only == "lmhead":
+        log("[bench] embedding / lm_head table only")
+        print(json.dumps(lmhead_configs(torch, tb, synth, timer, dev, steps=args.steps)),
+              flush=True)
         return
 
     problems = synth.sweep_problems(args.layers)
@@ -653,6 +660,42 @@ def i8_configs(torch, tb, synth, timer, dev, steps=100):
     return out
 
 
+def lmhead_configs(torch, tb, synth, timer, dev, steps=200):
+    """The decoder's 8-bit table (151,936 x 1536, one scale per row): the
+    lm_head at M = 1, 4 and 16 (one launch each: per-row activation
+    quantization fused, int8 MFMA, exact per-column dequantization), three
+    table copies rotated (702 MB) so each call reads HBM, not the MALL; and the
+    embedding lookup of a 256-token prompt."""
+    V, K = synth.VOCAB, synth.HIDDEN
+    W = torch.from_numpy(synth.table_weights()).to(dev)
+    q, s = tb.bitnet_i8_quant_weights_rows(W)
+    del W
+    qs = [q] + [q.clone() for _ in range(2)]
+    out = {}
+    for M in (1, 4, 16):
+        x = torch.from_numpy(synth.activations(M, K, synth.TABLE_SEED + 2)).to(dev)
+        y = torch.empty((M, V), dtype=torch.float32, device=dev)
+        ms = timer.time(lambda i=0: tb.bitnet_lm_head_into(M, V, K, x, qs[i % 3], s, y),
+                        steps, warmup=100)
+        alg = V * K + V * 4 + M * K * 4 + M * V * 4
+        out[f"lm_head_m{M}"] = {
+            "shape": {"M": M, "V": V, "K": K},
+            "us_per_call": round(ms * 1e3, 2),
+            "table_GBps": round(V * K / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "algorithmic_bytes": alg,
+            "kernel": "lm_head_kernel (one launch)"}
+    ids = torch.from_numpy(synth.token_ids(256)).to(dev)
+    e = torch.empty((256, K), dtype=torch.float32, device=dev)
+    ms = timer.time(lambda i=0: tb.bitnet_embed_lookup_into(ids, 256, qs[i % 3], s, V, K, e),
+                    steps, warmup=50)
+    out["embed_lookup_t256"] = {
+        "us_per_call": round(ms * 1e3, 2),
+        "note": "256 token rows gathered and dequantized (1.6 MB written): launch-bound"}
+    del qs, q, s
+    return out
+
+
 def lut_config(torch, tb, synth, timer, problems, packed, copy_b, w_scales, alg_bytes,
                decode_plans, dev, steps=1000):
     """The lookup-table variant over the M=1 decode sweep, timed like the headline
@@ -770,6 +813,7 @@ def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, a
 
     pbytes = sum(p.N * p.K // 4 for p in problems)
     out.update(i8_configs(torch, tb, synth, timer, dev))
+    out.update(lmhead_configs(torch, tb, synth, timer, dev))
     out["decode_sweep_m1_lut"] = lut_config(torch, tb, synth, timer, problems, packed, copy_b,
                                             w_scales, alg_bytes, decode_plans, dev)
     # The first launches on freshly allocated buffers run slower (M=4: about 72

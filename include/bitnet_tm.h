@@ -45,8 +45,9 @@
  *   - All data pointers are DEVICE pointers on the current HIP device, which
  *     must be a gfx950 (MI355X).  `stream` is a hipStream_t passed as void*
  *     (NULL = the default stream).  Every call is asynchronous on `stream`.
- *   - The library never allocates device memory and keeps no mutable global
- *     state; callers own every buffer.  Calls on different streams are
+ *   - The library never allocates device memory; callers own every buffer.
+ *     Its only mutable host state is a per-device cache of the architecture
+ *     check, filled on first use.  Calls on different streams are
  *     independent as long as their buffers do not overlap.
  *   - Arguments are checked on the host before anything is launched.  On any
  *     error nothing is launched and nothing is written.  Faults inside kernels
@@ -224,10 +225,70 @@ bitnet_status bitnet_i8_quant_weights(const float *W, int64_t N, int64_t K, int8
 
 size_t bitnet_i8_linear_workspace_bytes(int64_t M, int64_t K);
 
+/* bitnet_i8_linear_rows: the same layer with one weight scale per output
+ *   channel, as the ONNX build stores the encoders ("int8 per-channel
+ *   weights": ONNX model card, Quantization table, row "VAE encoders"):
+ *   q and w_scale [N] come from bitnet_i8_quant_weights_rows, and
+ *   y[m,n] = relu?(acc[m,n] * w_scale[n] / x_scale[m] + bias[n]).  The
+ *   epilogue is fp32: fl32(fl32(fl32(acc) * w_scale[n]) * fl32(1 / x_scale[m]))
+ *   + bias, then ReLU; its error is below 5 * 2^-24 * (|acc * w_scale[n] /
+ *   x_scale[m]| + |bias|).  Same arguments, workspace, limits and launches as
+ *   bitnet_i8_linear; w_scale 4-byte aligned. */
+bitnet_status bitnet_i8_linear_rows(int64_t M, int64_t N, int64_t K, const float *x,
+                                    const int8_t *q, const float *w_scale, const float *bias,
+                                    int32_t relu, float *y, void *workspace,
+                                    size_t workspace_bytes, int32_t *acc_out, void *stream);
+
 bitnet_status bitnet_i8_linear(int64_t M, int64_t N, int64_t K, const float *x, const int8_t *q,
                                const float *w_scale, const float *bias, int32_t relu, float *y,
                                void *workspace, size_t workspace_bytes, int32_t *acc_out,
                                void *stream);
+
+/* ------------------------------------------------------------------------
+ * The decoder's 8-bit table with one scale per row: token embeddings and the
+ * lm_head.  The ONNX build stores both at 8 bits, "per-row / per-column", where
+ * the GGUF build uses Q6_K (ONNX model card "multimodalart/VibeVoice-ASR-
+ * BitNet-ONNX", Quantization table, row "Embeddings / lm_head"; xujun.org
+ * article, heterogeneous-quantization section: I2_S plus Q6_K embeddings).
+ * One table [V, K] (vocabulary x hidden, row-major) serves both: row v is
+ * token v's embedding and, read as the lm_head weight, the weights of logit v,
+ * so its per-row scales are the lm_head's per-column scales.  The Q6_K block
+ * format is not on the pages; this 8-bit form is the card's ONNX one.
+ *
+ * bitnet_i8_quant_weights_rows: W fp32 [N,K] row-major -> q int8 [N,K] and
+ *   w_scale fp32 [N]: per row n, w_scale[n] = fl32(max_k |W[n,k]| / 127),
+ *   q = clamp(rint(fl32(W / w_scale[n])), -127, 127), half to even; a zero row
+ *   gives w_scale[n] = 0 and q = 0.  Bit-exact.  N >= 1, K >= 64, K % 64 == 0,
+ *   N*K < 2^31; W and q 16-byte aligned, w_scale 4-byte.  One launch, no
+ *   workspace.  The same scales serve as per-output-channel scales of an
+ *   I8_S layer (bitnet_i8_linear_rows).
+ *
+ * bitnet_embed_lookup: out[t,k] = fl32(q[ids[t],k] * w_scale[ids[t]]) for
+ *   t < T; an id outside [0, N) gives a zero row (ids are device data and are
+ *   not checked on the host).  ids int32 [T] (4-byte aligned), q int8 [N,K]
+ *   and out fp32 [T,K] 16-byte aligned.  T == 0 launches nothing and returns
+ *   BITNET_OK.  K >= 64, K % 64 == 0, T*K and N*K < 2^31.  Bit-exact.
+ *
+ * bitnet_lm_head: y[m,n] = acc[m,n] * w_scale[n] / x_scale[m], rounded once to
+ *   fp32 (the product in fp64, exact; the division in fp64, correctly rounded),
+ *   with xq, x_scale the per-row quantization of x (as bitnet_quant_act) and
+ *   acc = sum_k xq[m,k] * q[n,k] in int32.  Decode only: 1 <= M <= 16 and
+ *   M * (K + 16) <= 57344 (the quantized rows stay in LDS); K >= 64,
+ *   K % 64 == 0, N*K and M*N*4 < 2^31.  x fp32 [M,K] and q 16-byte aligned,
+ *   w_scale fp32 [N], y fp32 [M,N] 4-byte aligned.  xq_out [M,K] (16-byte
+ *   aligned), x_scale_out [M] and acc_out [M,N] are optional copies for parity
+ *   checks.  One launch, no workspace; an HBM stream of the N*K table bytes.
+ * ------------------------------------------------------------------------ */
+bitnet_status bitnet_i8_quant_weights_rows(const float *W, int64_t N, int64_t K, int8_t *q,
+                                           float *w_scale, void *stream);
+
+bitnet_status bitnet_embed_lookup(const int32_t *ids, int64_t T, const int8_t *q,
+                                  const float *w_scale, int64_t N, int64_t K, float *out,
+                                  void *stream);
+
+bitnet_status bitnet_lm_head(int64_t M, int64_t N, int64_t K, const float *x, const int8_t *q,
+                             const float *w_scale, float *y, int8_t *xq_out, float *x_scale_out,
+                             int32_t *acc_out, void *stream);
 
 /* ------------------------------------------------------------------------
  * Lookup-table variant of the single-row decode, for comparison with the

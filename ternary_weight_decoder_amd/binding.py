@@ -97,6 +97,15 @@ def lib():
         L.bitnet_i8_linear.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p, _sz, _p,
                                        _p]
         L.bitnet_i8_linear.restype = _i32
+        L.bitnet_i8_linear_rows.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p, _sz,
+                                            _p, _p]
+        L.bitnet_i8_linear_rows.restype = _i32
+        L.bitnet_i8_quant_weights_rows.argtypes = [_p, _i64, _i64, _p, _p, _p]
+        L.bitnet_i8_quant_weights_rows.restype = _i32
+        L.bitnet_embed_lookup.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _p]
+        L.bitnet_embed_lookup.restype = _i32
+        L.bitnet_lm_head.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p]
+        L.bitnet_lm_head.restype = _i32
         _lib = L
     return _lib
 
@@ -320,6 +329,91 @@ def bitnet_i8_linear(x: torch.Tensor, q: torch.Tensor, w_scale: torch.Tensor, bi
     ws = torch.empty(bitnet_i8_linear_workspace_bytes(M, K), dtype=torch.uint8, device=x.device)
     acc = torch.empty((M, N), dtype=torch.int32, device=x.device) if return_acc else None
     bitnet_i8_linear_into(M, N, K, x, q, w_scale, bias, relu, y, ws, acc, stream)
+    return (y, acc) if return_acc else y
+
+
+# ---- the 8-bit table with one scale per row: embeddings and lm_head ---------
+
+def bitnet_i8_quant_weights_rows_into(W, N, K, q, w_scale, stream=None) -> None:
+    _check(lib().bitnet_i8_quant_weights_rows(_ptr(W), N, K, _ptr(q), _ptr(w_scale),
+                                              _stream(stream)),
+           "bitnet_i8_quant_weights_rows")
+
+
+def bitnet_i8_quant_weights_rows(W: torch.Tensor, stream=None):
+    """fp32 W [N,K] -> (q int8 [N,K], w_scale fp32 [N]): one absmax scale per row."""
+    _dev(W, torch.float32, "W")
+    N, K = W.shape
+    q = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    w_scale = torch.empty(N, dtype=torch.float32, device=W.device)
+    bitnet_i8_quant_weights_rows_into(W, N, K, q, w_scale, stream)
+    return q, w_scale
+
+
+def bitnet_embed_lookup_into(ids, T, q, w_scale, N, K, out, stream=None) -> None:
+    _check(lib().bitnet_embed_lookup(_ptr(ids), T, _ptr(q), _ptr(w_scale), N, K, _ptr(out),
+                                     _stream(stream)),
+           "bitnet_embed_lookup")
+
+
+def bitnet_embed_lookup(ids: torch.Tensor, q: torch.Tensor, w_scale: torch.Tensor, stream=None):
+    """int32 token ids [T] -> fp32 embedding rows [T, K] of the int8 table."""
+    _dev(ids, torch.int32, "ids")
+    _dev(q, torch.int8, "q")
+    N, K = q.shape
+    T = ids.numel()
+    out = torch.empty((T, K), dtype=torch.float32, device=q.device)
+    bitnet_embed_lookup_into(ids, T, q, w_scale, N, K, out, stream)
+    return out
+
+
+def bitnet_lm_head_into(M, N, K, x, q, w_scale, y, xq_out=None, x_scale_out=None, acc_out=None,
+                        stream=None) -> None:
+    _check(lib().bitnet_lm_head(M, N, K, _ptr(x), _ptr(q), _ptr(w_scale), _ptr(y), _ptr(xq_out),
+                                _ptr(x_scale_out), _ptr(acc_out), _stream(stream)),
+           "bitnet_lm_head")
+
+
+def bitnet_lm_head(x: torch.Tensor, q: torch.Tensor, w_scale: torch.Tensor,
+                   return_parts: bool = False, stream=None):
+    """lm_head over the int8 table: fp32 x [M,K] (M <= 16) -> fp32 logits [M, N]; with
+    return_parts, a dict that also holds xq, x_scale and the int32 acc."""
+    _dev(x, torch.float32, "x")
+    _dev(q, torch.int8, "q")
+    M, K = x.shape
+    N = q.shape[0]
+    y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if not return_parts:
+        bitnet_lm_head_into(M, N, K, x, q, w_scale, y, stream=stream)
+        return y
+    xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    xs = torch.empty(M, dtype=torch.float32, device=x.device)
+    acc = torch.empty((M, N), dtype=torch.int32, device=x.device)
+    bitnet_lm_head_into(M, N, K, x, q, w_scale, y, xq, xs, acc, stream)
+    return {"y": y, "xq": xq, "x_scale": xs, "acc": acc}
+
+
+def bitnet_i8_linear_rows_into(M, N, K, x, q, w_scale, bias, relu, y, workspace, acc_out=None,
+                               stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().bitnet_i8_linear_rows(M, N, K, _ptr(x), _ptr(q), _ptr(w_scale), _ptr(bias),
+                                       int(bool(relu)), _ptr(y), _ptr(workspace), ws_bytes,
+                                       _ptr(acc_out), _stream(stream)),
+           "bitnet_i8_linear_rows")
+
+
+def bitnet_i8_linear_rows(x: torch.Tensor, q: torch.Tensor, w_scale: torch.Tensor, bias=None,
+                          relu: bool = False, return_acc: bool = False, stream=None):
+    """I8_S layer with per-channel weight scales: fp32 x [M,K], int8 q [N,K],
+    fp32 w_scale [N] -> fp32 y [M,N] (and int32 acc)."""
+    _dev(x, torch.float32, "x")
+    _dev(q, torch.int8, "q")
+    M, K = x.shape
+    N = q.shape[0]
+    y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    ws = torch.empty(bitnet_i8_linear_workspace_bytes(M, K), dtype=torch.uint8, device=x.device)
+    acc = torch.empty((M, N), dtype=torch.int32, device=x.device) if return_acc else None
+    bitnet_i8_linear_rows_into(M, N, K, x, q, w_scale, bias, relu, y, ws, acc, stream)
     return (y, acc) if return_acc else y
 
 

@@ -176,22 +176,26 @@ static bitnet_status matmul_from_ws(int64_t M, int64_t N, int64_t K, const uint8
       launch_gemm((int)M, (int)N, (int)K, xqp, xs, rs, packed, w_scale, y, acc_out, s));
 }
 
-bitnet_status bitnet_ternary_matmul(int64_t M, int64_t N, int64_t K, const float *x,
+// Argument checks of the single projection, apart from the workspace.
+static bitnet_status matmul_args_ok(int64_t M, int64_t N, int64_t K, const float *x,
                                     const uint8_t *packed, const float *w_scale, float *y,
-                                    void *workspace, size_t workspace_bytes, int8_t *xq_out,
-                                    float *x_scale_out, int32_t *acc_out, void *stream) {
+                                    int8_t *xq_out, float *x_scale_out, int32_t *acc_out) {
   if (!x || !packed || !w_scale || !y) return BITNET_ERR_NULL;
   if (!shape_ok(M, N, K)) return BITNET_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(w_scale, 4) || !aligned(y, 4) ||
       (xq_out && !aligned(xq_out, 16)) || (x_scale_out && !aligned(x_scale_out, 4)) ||
       (acc_out && !aligned(acc_out, 4)))
     return BITNET_ERR_ALIGN;
-  if (!workspace || workspace_bytes < bitnet_matmul_workspace_bytes(M, K))
-    return BITNET_ERR_WORKSPACE;
-  if (!aligned(workspace, 256)) return BITNET_ERR_ALIGN;
-  bitnet_status st = device_check();
-  if (st != BITNET_OK) return st;
-  hipStream_t s = as_stream(stream);
+  return BITNET_OK;
+}
+
+// The single projection once its arguments are checked; `workspace` holds at
+// least bitnet_matmul_workspace_bytes(M, K) bytes, 256-byte aligned.
+static bitnet_status matmul_run(int64_t M, int64_t N, int64_t K, const float *x,
+                                const uint8_t *packed, const float *w_scale, float *y,
+                                void *workspace, int8_t *xq_out, float *x_scale_out,
+                                int32_t *acc_out, hipStream_t s) {
+  bitnet_status st;
   if (M <= kGemvMaxM && gemv_fusable(M, K))
     return from_hip(launch_gemv_fused((int)M, (int)N, (int)K, x, packed, w_scale, y, xq_out,
                                       x_scale_out, acc_out, s));
@@ -203,6 +207,21 @@ bitnet_status bitnet_ternary_matmul(int64_t M, int64_t N, int64_t K, const float
                                   reinterpret_cast<int32_t *>(ws + L.rowsum), s));
   if (st != BITNET_OK) return st;
   return matmul_from_ws(M, N, K, packed, w_scale, y, ws, acc_out, s);
+}
+
+bitnet_status bitnet_ternary_matmul(int64_t M, int64_t N, int64_t K, const float *x,
+                                    const uint8_t *packed, const float *w_scale, float *y,
+                                    void *workspace, size_t workspace_bytes, int8_t *xq_out,
+                                    float *x_scale_out, int32_t *acc_out, void *stream) {
+  bitnet_status st = matmul_args_ok(M, N, K, x, packed, w_scale, y, xq_out, x_scale_out, acc_out);
+  if (st != BITNET_OK) return st;
+  if (!workspace || workspace_bytes < bitnet_matmul_workspace_bytes(M, K))
+    return BITNET_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BITNET_ERR_ALIGN;
+  st = device_check();
+  if (st != BITNET_OK) return st;
+  return matmul_run(M, N, K, x, packed, w_scale, y, workspace, xq_out, x_scale_out, acc_out,
+                    as_stream(stream));
 }
 
 bitnet_status bitnet_ternary_matmul_q8(int64_t M, int64_t N, int64_t K, const int8_t *xq,
@@ -358,10 +377,10 @@ size_t bitnet_i8_linear_workspace_bytes(int64_t M, int64_t K) {
   return align256((size_t)(M * K)) + align256((size_t)M * 4);
 }
 
-bitnet_status bitnet_i8_linear(int64_t M, int64_t N, int64_t K, const float *x, const int8_t *q,
-                               const float *w_scale, const float *bias, int32_t relu, float *y,
-                               void *workspace, size_t workspace_bytes, int32_t *acc_out,
-                               void *stream) {
+static bitnet_status i8_linear_common(int64_t M, int64_t N, int64_t K, const float *x,
+                                      const int8_t *q, const float *w_scale, bool per_channel,
+                                      const float *bias, int32_t relu, float *y, void *workspace,
+                                      size_t workspace_bytes, int32_t *acc_out, void *stream) {
   if (!x || !q || !w_scale || !y) return BITNET_ERR_NULL;
   if (!i8_shape_ok(M, N, K)) return BITNET_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(w_scale, 4) || !aligned(y, 4) ||
@@ -378,8 +397,63 @@ bitnet_status bitnet_i8_linear(int64_t M, int64_t N, int64_t K, const float *x, 
   float *xs = reinterpret_cast<float *>(ws + align256((size_t)(M * K)));
   st = from_hip(launch_quant_rows(x, (int)M, (int)K, xq, nullptr, xs, nullptr, nullptr, s));
   if (st != BITNET_OK) return st;
-  return from_hip(launch_i8_gemm((int)M, (int)N, (int)K, xq, xs, q, w_scale, bias,
+  return from_hip(launch_i8_gemm((int)M, (int)N, (int)K, xq, xs, q, w_scale, per_channel, bias,
                                  relu != 0 ? 1 : 0, y, acc_out, s));
+}
+
+bitnet_status bitnet_i8_linear(int64_t M, int64_t N, int64_t K, const float *x, const int8_t *q,
+                               const float *w_scale, const float *bias, int32_t relu, float *y,
+                               void *workspace, size_t workspace_bytes, int32_t *acc_out,
+                               void *stream) {
+  return i8_linear_common(M, N, K, x, q, w_scale, false, bias, relu, y, workspace,
+                          workspace_bytes, acc_out, stream);
+}
+
+bitnet_status bitnet_i8_linear_rows(int64_t M, int64_t N, int64_t K, const float *x,
+                                    const int8_t *q, const float *w_scale, const float *bias,
+                                    int32_t relu, float *y, void *workspace,
+                                    size_t workspace_bytes, int32_t *acc_out, void *stream) {
+  return i8_linear_common(M, N, K, x, q, w_scale, true, bias, relu, y, workspace,
+                          workspace_bytes, acc_out, stream);
+}
+
+bitnet_status bitnet_i8_quant_weights_rows(const float *W, int64_t N, int64_t K, int8_t *q,
+                                           float *w_scale, void *stream) {
+  if (!W || !q || !w_scale) return BITNET_ERR_NULL;
+  if (!i8_shape_ok(1, N, K)) return BITNET_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(q, 16) || !aligned(w_scale, 4)) return BITNET_ERR_ALIGN;
+  bitnet_status st = device_check();
+  if (st != BITNET_OK) return st;
+  return from_hip(launch_rowq_quant(W, N, K, q, w_scale, as_stream(stream)));
+}
+
+bitnet_status bitnet_embed_lookup(const int32_t *ids, int64_t T, const int8_t *q,
+                                  const float *w_scale, int64_t N, int64_t K, float *out,
+                                  void *stream) {
+  if (T == 0) return BITNET_OK;
+  if (!ids || !q || !w_scale || !out) return BITNET_ERR_NULL;
+  if (T < 0 || T >= kLimit || T * K >= kLimit || !i8_shape_ok(1, N, K)) return BITNET_ERR_SHAPE;
+  if (!aligned(ids, 4) || !aligned(q, 16) || !aligned(w_scale, 4) || !aligned(out, 16))
+    return BITNET_ERR_ALIGN;
+  bitnet_status st = device_check();
+  if (st != BITNET_OK) return st;
+  return from_hip(launch_embed(ids, T, q, w_scale, N, K, out, as_stream(stream)));
+}
+
+bitnet_status bitnet_lm_head(int64_t M, int64_t N, int64_t K, const float *x, const int8_t *q,
+                             const float *w_scale, float *y, int8_t *xq_out, float *x_scale_out,
+                             int32_t *acc_out, void *stream) {
+  if (!x || !q || !w_scale || !y) return BITNET_ERR_NULL;
+  if (!i8_shape_ok(M, N, K) || M > kGemvMaxM || M * (K + 16) > kLmHeadMaxRows)
+    return BITNET_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(w_scale, 4) || !aligned(y, 4) ||
+      (xq_out && !aligned(xq_out, 16)) || (x_scale_out && !aligned(x_scale_out, 4)) ||
+      (acc_out && !aligned(acc_out, 4)))
+    return BITNET_ERR_ALIGN;
+  bitnet_status st = device_check();
+  if (st != BITNET_OK) return st;
+  return from_hip(launch_lm_head((int)M, (int)N, (int)K, x, q, w_scale, y, xq_out, x_scale_out,
+                                 acc_out, as_stream(stream)));
 }
 
 bitnet_status bitnet_ternary_matmul_lut_grouped(const bitnet_problem *problems_dev,

@@ -18,8 +18,25 @@ hipError_t launch_lut_grouped(const bitnet_problem *problems, const GroupTable &
 // workspace (filled here).
 hipError_t launch_i8_quant_weights(const float *W, int64_t N, int64_t K, int8_t *q,
                                    float *w_scale, uint32_t *amax, hipStream_t stream);
+// per_channel: w_scale holds one scale per output channel [N] instead of one
+// device scalar.
 hipError_t launch_i8_gemm(int M, int N, int K, const int8_t *xq, const float *x_scale,
-                          const int8_t *q, const float *w_scale, const float *bias, int relu,
-                          float *y, int32_t *acc_out, hipStream_t stream);
+                          const int8_t *q, const float *w_scale, bool per_channel,
+                          const float *bias, int relu, float *y, int32_t *acc_out,
+                          hipStream_t stream);
+
+// lmhead.hip: the decoder's 8-bit table with one scale per row (embeddings,
+// lm_head).  lm_head: M <= kGemvMaxM and M * (K + 16) <= kLmHeadMaxRows; the
+// workgroup's dynamic LDS then stays within kLmHeadMaxLds.
+constexpr size_t kLmHeadMaxLds = 64512;    // with the static LDS, under 64 KB
+constexpr int64_t kLmHeadMaxRows = 57344;  // quantized rows in LDS
+size_t lm_head_lds_bytes(int64_t M, int64_t V, int64_t K);
+hipError_t launch_rowq_quant(const float *W, int64_t N, int64_t K, int8_t *q, float *w_scale,
+                             hipStream_t stream);
+hipError_t launch_embed(const int32_t *ids, int64_t T, const int8_t *q, const float *w_scale,
+                        int64_t N, int64_t K, float *out, hipStream_t stream);
+hipError_t launch_lm_head(int M, int V, int K, const float *x, const int8_t *q,
+                          const float *w_scale, float *y, int8_t *xq_out, float *x_scale_out,
+                          int32_t *acc_out, hipStream_t stream);
 
 }  // namespace bitnet

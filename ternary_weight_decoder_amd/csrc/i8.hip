@@ -62,7 +62,7 @@ struct I8Params {
   const int8_t *xq;        // [M][K] natural order
   const float *x_scale;    // [M]
   const int8_t *q;         // [N][K]
-  const float *w_scale;    // device scalar
+  const float *w_scale;    // device scalar, or [N] with one scale per output channel
   const float *bias;       // [N] or null
   float *y;                // [M][N]
   int32_t *acc_out;        // [M][N] or null
@@ -81,15 +81,17 @@ __device__ __forceinline__ void wait_for_step(int later) {
     __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_wait(0));
 }
 
-// Output value: relu?(fl32(fl32(acc) * factor) + bias).
+// Output value: relu?(fl32(fl32(acc * c) * factor) + bias), where with one
+// scale per tensor c = 1 and factor = fl32(w_scale / x_scale[m]), and with one
+// scale per output channel c = w_scale[n] and factor = fl32(1 / x_scale[m]).
 template <bool RELU>
-__device__ __forceinline__ float i8_out(float a, float f, float b) {
-  float v = a * f + b;
+__device__ __forceinline__ float i8_out(float a, float c, float f, float b) {
+  float v = (a * c) * f + b;
   if (RELU) v = v > 0.0f ? v : 0.0f;
   return v;
 }
 
-template <int BM, bool RELU>
+template <int BM, bool RELU, bool PERCOL>
 __global__ void __launch_bounds__(kThreads) i8_gemm_kernel(I8Params p) {
   constexpr int RB = BM / 64;            // 32-row blocks per wave
   constexpr int kDmaA = BM / 64;         // 1 KB activation loads per wave and step
@@ -156,16 +158,18 @@ __global__ void __launch_bounds__(kThreads) i8_gemm_kernel(I8Params p) {
   // Per-row dequantization factors of the tile (rows past M: any finite value).
   if (tid < BM) {
     const int row = min(m0 + tid, p.M - 1);
-    sh.factor[tid] = ld_global<float>(p.w_scale) / ld_global<float>(p.x_scale + row);
+    const float xs = ld_global<float>(p.x_scale + row);
+    sh.factor[tid] = PERCOL ? 1.0f / xs : ld_global<float>(p.w_scale) / xs;
   }
 
-  // The bias of the lane's columns, fetched now so that its latency hides
-  // behind the K loop.
-  float bias[2];
+  // The bias (and channel scale) of the lane's columns, fetched now so that
+  // their latency hides behind the K loop.
+  float bias[2], cscale[2];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const int n = n0 + wn * 64 + cb * 32 + li;
     bias[cb] = (p.bias && n < p.N) ? ld_global<float>(p.bias + n) : 0.0f;
+    cscale[cb] = (PERCOL && n < p.N) ? ld_global<float>(p.w_scale + n) : 1.0f;
   }
 
 #pragma unroll
@@ -237,8 +241,9 @@ __global__ void __launch_bounds__(kThreads) i8_gemm_kernel(I8Params p) {
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb) {
             const int a = acc[rb][cb][4 * g + k];
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, i8_out<RELU>((float)a, f4[k], bias[cb])),
-                                                  y_rsrc, vo[cb], so, kStoreAux);
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __builtin_bit_cast(int, i8_out<RELU>((float)a, cscale[cb], f4[k], bias[cb])), y_rsrc,
+                vo[cb], so, kStoreAux);
             if (p.acc_out) __builtin_amdgcn_raw_buffer_store_b32(a, c_rsrc, vo[cb], so, 0);
           }
         }
@@ -268,8 +273,9 @@ __global__ void __launch_bounds__(kThreads) i8_gemm_kernel(I8Params p) {
           const int a = acc[rb][cb][4 * g + k];
           const uint32_t off = (row_off | col_off[cb]) >= 0x80000000u ? y_bytes
                                                                       : row_off + col_off[cb];
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, i8_out<RELU>((float)a, f, bias[cb])),
-                                                y_rsrc, off, 0, kStoreAux);
+          __builtin_amdgcn_raw_buffer_store_b32(
+              __builtin_bit_cast(int, i8_out<RELU>((float)a, cscale[cb], f, bias[cb])), y_rsrc, off,
+              0, kStoreAux);
           if (p.acc_out) __builtin_amdgcn_raw_buffer_store_b32(a, c_rsrc, off, 0, 0);
         }
       }
@@ -348,24 +354,32 @@ hipError_t launch_i8_quant_weights(const float *W, int64_t N, int64_t K, int8_t 
   return hipGetLastError();
 }
 
+template <bool PERCOL>
+static hipError_t launch_i8_gemm_t(const I8Params &p, bool tall, bool relu, unsigned grid,
+                                   hipStream_t stream) {
+  if (tall && relu)
+    i8_gemm_kernel<128, true, PERCOL><<<grid, kThreads, 0, stream>>>(p);
+  else if (tall)
+    i8_gemm_kernel<128, false, PERCOL><<<grid, kThreads, 0, stream>>>(p);
+  else if (relu)
+    i8_gemm_kernel<64, true, PERCOL><<<grid, kThreads, 0, stream>>>(p);
+  else
+    i8_gemm_kernel<64, false, PERCOL><<<grid, kThreads, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
 hipError_t launch_i8_gemm(int M, int N, int K, const int8_t *xq, const float *x_scale,
-                          const int8_t *q, const float *w_scale, const float *bias, int relu,
-                          float *y, int32_t *acc_out, hipStream_t stream) {
+                          const int8_t *q, const float *w_scale, bool per_channel,
+                          const float *bias, int relu, float *y, int32_t *acc_out,
+                          hipStream_t stream) {
   I8Params p{xq, x_scale, q, w_scale, bias, y, acc_out, M, N, K, relu ? 1 : 0, 0, 0};
   p.NB = (N + kBN - 1) / kBN;
   const bool tall = i8_tall_tiles(M, N);
   p.MB = (M + (tall ? 127 : 63)) / (tall ? 128 : 64);
   const int64_t grid = (int64_t)8 * ((p.MB + 7) / 8) * p.NB;
   if (grid >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  if (tall && relu)
-    i8_gemm_kernel<128, true><<<(unsigned)grid, kThreads, 0, stream>>>(p);
-  else if (tall)
-    i8_gemm_kernel<128, false><<<(unsigned)grid, kThreads, 0, stream>>>(p);
-  else if (relu)
-    i8_gemm_kernel<64, true><<<(unsigned)grid, kThreads, 0, stream>>>(p);
-  else
-    i8_gemm_kernel<64, false><<<(unsigned)grid, kThreads, 0, stream>>>(p);
-  return hipGetLastError();
+  return per_channel ? launch_i8_gemm_t<true>(p, tall, relu != 0, (unsigned)grid, stream)
+                     : launch_i8_gemm_t<false>(p, tall, relu != 0, (unsigned)grid, stream);
 }
 
 }  // namespace bitnet

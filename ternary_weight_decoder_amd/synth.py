@@ -179,3 +179,23 @@ def i8_layer_inputs(name: str, seed: int = 70000):
     W = normal_weights(N, K, seed + 10 * off + 1)
     bias = np.random.default_rng(seed + 10 * off + 2).standard_normal(N, dtype=np.float32)
     return x, W, (bias * np.float32(0.1)).astype(np.float32)
+
+
+# ---- the decoder's 8-bit table: embeddings and lm_head ----------------------
+# [V, K] = [151936, 1536]: the prompt's token ids reach 151648 (<|speech_pad|>)
+# and V*K int8 plus one fp32 scale per row is the model card's 234 MB of
+# embeddings.  The table's master weights are drawn ~ N(0, 0.02^2) like the
+# projections' (no trained weights are used); the lm_head input is a hidden
+# state, N(0,1) with 1% of channels x20 like every other projection input.
+VOCAB = 151936
+TABLE_SEED = 80000
+
+
+def table_weights(V: int = VOCAB, K: int = HIDDEN, seed: int = TABLE_SEED) -> np.ndarray:
+    """fp32 master weights of the embedding / lm_head table, shape [V, K]."""
+    return normal_weights(V, K, seed)
+
+
+def token_ids(T: int, V: int = VOCAB, seed: int = TABLE_SEED + 1) -> np.ndarray:
+    """T token ids drawn uniformly from [0, V), int32."""
+    return np.random.default_rng(seed).integers(0, V, size=T, dtype=np.int64).astype(np.int32)

@@ -215,3 +215,34 @@ def test_stages_validation(L):
     # A reader in the same stage as its producer (k reads q's output).
     arr5, ref5 = problems(chain[0], (YQ, A, A, YK, 256, 1536), *chain[2:])
     assert g(1, A, 4, eref, 2, ref5, A, 1 << 30, NULL) == ERR["ALIAS"]
+
+
+def test_table_entry_points_validation(L):
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.bitnet_i8_quant_weights_rows.argtypes = [p, i64, i64, p, p, p]
+    L.bitnet_i8_quant_weights_rows.restype = i32
+    L.bitnet_embed_lookup.argtypes = [p, i64, p, p, i64, i64, p, p]
+    L.bitnet_embed_lookup.restype = i32
+    L.bitnet_lm_head.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, p]
+    L.bitnet_lm_head.restype = i32
+    rq = L.bitnet_i8_quant_weights_rows
+    assert rq(NULL, 8, 64, A, A, NULL) == ERR["NULL"]
+    assert rq(A, 8, 96, A, A, NULL) == ERR["SHAPE"]
+    assert rq(A, 0, 64, A, A, NULL) == ERR["SHAPE"]
+    assert rq(A, 8, 64, A + 4, A, NULL) == ERR["ALIGN"]
+    e = L.bitnet_embed_lookup
+    assert e(NULL, 0, NULL, NULL, 8, 64, NULL, NULL) == 0          # no tokens: nothing to do
+    assert e(A, 4, NULL, A, 8, 64, A, NULL) == ERR["NULL"]
+    assert e(A, -1, A, A, 8, 64, A, NULL) == ERR["SHAPE"]
+    assert e(A, 4, A, A, 8, 100, A, NULL) == ERR["SHAPE"]
+    assert e(A + 2, 4, A, A, 8, 64, A, NULL) == ERR["ALIGN"]
+    assert e(A, 4, A, A, 8, 64, A + 4, NULL) == ERR["ALIGN"]
+    h = L.bitnet_lm_head
+    assert h(1, 151936, 1536, NULL, A, A, A, NULL, NULL, NULL, NULL) == ERR["NULL"]
+    assert h(17, 151936, 1536, A, A, A, A, NULL, NULL, NULL, NULL) == ERR["SHAPE"]   # M > 16
+    assert h(0, 151936, 1536, A, A, A, A, NULL, NULL, NULL, NULL) == ERR["SHAPE"]
+    assert h(1, 151936, 1500, A, A, A, A, NULL, NULL, NULL, NULL) == ERR["SHAPE"]
+    assert h(16, 100, 4096, A, A, A, A, NULL, NULL, NULL, NULL) == ERR["SHAPE"]     # LDS
+    assert h(1, 151936, 1536, A + 4, A, A, A, NULL, NULL, NULL, NULL) == ERR["ALIGN"]
+    assert h(1, 151936, 1536, A, A, A, A, A + 4, NULL, NULL, NULL) == ERR["ALIGN"]
+
