@@ -45,10 +45,13 @@
  *   - All data pointers are DEVICE pointers on the current HIP device, which
  *     must be a gfx950 (MI355X).  `stream` is a hipStream_t passed as void*
  *     (NULL = the default stream).  Every call is asynchronous on `stream`.
- *   - The library never allocates device memory; callers own every buffer.
- *     Its only mutable host state is a per-device cache of the architecture
- *     check, filled on first use.  Calls on different streams are
- *     independent as long as their buffers do not overlap.
+ *   - The library never allocates device memory; callers own every buffer,
+ *     except the fixed scratch array of bitnet_ternary_matmul_noalloc, which
+ *     each device holds from module load to process exit.  Its only mutable
+ *     host state is per-device caches (the architecture check and that
+ *     array's device address), filled on first use under a lock.  Calls on
+ *     different streams are independent as long as their buffers do not
+ *     overlap.
  *   - Arguments are checked on the host before anything is launched.  On any
  *     error nothing is launched and nothing is written.  Faults inside kernels
  *     surface at the caller's next synchronization.
@@ -79,6 +82,7 @@ typedef int32_t bitnet_status;
 #define BITNET_ERR_HIP       5  /* a HIP call or kernel launch reported an error   */
 #define BITNET_ERR_DEVICE    6  /* the current device is not a gfx950             */
 #define BITNET_ERR_ALIAS     7  /* outputs overlap each other or an input          */
+#define BITNET_ERR_SCRATCH   8  /* needs more than the built-in scratch (noalloc)  */
 
 /* Maximum number of problems in one grouped call. */
 #define BITNET_MAX_GROUP     256
@@ -147,6 +151,26 @@ bitnet_status bitnet_ternary_matmul(int64_t M, int64_t N, int64_t K, const float
                                     const uint8_t *packed, const float *w_scale, float *y,
                                     void *workspace, size_t workspace_bytes, int8_t *xq_out,
                                     float *x_scale_out, int32_t *acc_out, void *stream);
+
+/* Same projection for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * no workspace argument; the quantized rows, scales and row sums go to a
+ * built-in scratch array of BITNET_SCRATCH_BYTES (= bitnet_scratch_bytes())
+ * per device.  Problems whose bitnet_matmul_workspace_bytes(M, K) exceeds it
+ * are rejected with BITNET_ERR_SCRATCH (M = 1800 fits up to K = 18560).
+ * Allocates nothing (no hipMalloc, no library allocation); the first call on
+ * a device looks up the array's address.  Every call on one device shares
+ * that array and leaves its contents behind: calls that overlap in time on
+ * one device (different streams, or host threads) race and must be ordered
+ * by the caller.  Outputs are identical to bitnet_ternary_matmul's. */
+#define BITNET_SCRATCH_BYTES ((size_t)32 << 20)
+
+size_t bitnet_scratch_bytes(void);
+
+bitnet_status bitnet_ternary_matmul_noalloc(int64_t M, int64_t N, int64_t K, const float *x,
+                                            const uint8_t *packed, const float *w_scale,
+                                            float *y, int8_t *xq_out, float *x_scale_out,
+                                            int32_t *acc_out, void *stream);
 
 /* Same projection from already-quantized activations (xq natural order, as
  * written by bitnet_quant_act).  workspace: bitnet_matmul_workspace_bytes(M, K). */

@@ -97,6 +97,11 @@ def lib():
         L.bitnet_i8_linear.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p, _sz, _p,
                                        _p]
         L.bitnet_i8_linear.restype = _i32
+        L.bitnet_scratch_bytes.argtypes = []
+        L.bitnet_scratch_bytes.restype = _sz
+        L.bitnet_ternary_matmul_noalloc.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p,
+                                                    _p, _p]
+        L.bitnet_ternary_matmul_noalloc.restype = _i32
         L.bitnet_i8_linear_rows.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p, _sz,
                                             _p, _p]
         L.bitnet_i8_linear_rows.restype = _i32
@@ -187,6 +192,19 @@ def bitnet_ternary_matmul_q8_into(M, N, K, xq, x_scale, packed, w_scale, y, work
 # ---------------------------------------------------------------------------
 # Convenience forms that allocate their outputs with torch (plumbing only).
 # ---------------------------------------------------------------------------
+
+def bitnet_scratch_bytes() -> int:
+    return int(lib().bitnet_scratch_bytes())
+
+
+def bitnet_ternary_matmul_noalloc_into(M, N, K, x, packed, w_scale, y, xq_out=None,
+                                       x_scale_out=None, acc_out=None, stream=None) -> None:
+    """The projection with the library's built-in scratch instead of a workspace."""
+    _check(lib().bitnet_ternary_matmul_noalloc(M, N, K, _ptr(x), _ptr(packed), _ptr(w_scale),
+                                               _ptr(y), _ptr(xq_out), _ptr(x_scale_out),
+                                               _ptr(acc_out), _stream(stream)),
+           "bitnet_ternary_matmul_noalloc")
+
 
 def bitnet_ternarize_pack(W: torch.Tensor, stream=None):
     """fp32 W [N,K] -> (packed uint8 [N*K/4], w_scale fp32 [1]) on W's device."""

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <mutex>
 #include <utility>
 
 #include "bitnet_internal.hpp"
@@ -13,6 +14,13 @@
 #include "bitnet_tm.h"
 
 using namespace bitnet;
+
+// Built-in workspace of bitnet_ternary_matmul_noalloc, for callers that cannot
+// allocate.  Every device the library runs on holds its own copy from module
+// load until the process ends.  In host code `scratch` only names the symbol:
+// its device address on the current device comes from hipGetSymbolAddress,
+// looked up once per device (scratch_address) and passed to the kernels.
+static __device__ __align__(256) uint8_t scratch[BITNET_SCRATCH_BYTES];
 
 namespace {
 
@@ -49,6 +57,29 @@ bitnet_status device_check() {
 }
 
 bitnet_status from_hip(hipError_t e) { return e == hipSuccess ? BITNET_OK : BITNET_ERR_HIP; }
+
+// Device address of `scratch` on each device (see its definition above).
+constexpr size_t kScratchBytes = BITNET_SCRATCH_BYTES;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+bitnet_status scratch_address(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BITNET_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return BITNET_ERR_DEVICE;
+  void *p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BITNET_ERR_HIP;
+      if (!aligned(p, 256)) return BITNET_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return BITNET_OK;
+}
 
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
@@ -116,6 +147,8 @@ const char *bitnet_status_string(bitnet_status s) {
     case BITNET_ERR_HIP: return "HIP runtime or launch error";
     case BITNET_ERR_DEVICE: return "current device is not a gfx950";
     case BITNET_ERR_ALIAS: return "outputs overlap each other or an input";
+    case BITNET_ERR_SCRATCH:
+      return "problem needs more workspace than the built-in scratch (bitnet_scratch_bytes())";
     default: return "unknown status";
   }
 }
@@ -221,6 +254,24 @@ bitnet_status bitnet_ternary_matmul(int64_t M, int64_t N, int64_t K, const float
   st = device_check();
   if (st != BITNET_OK) return st;
   return matmul_run(M, N, K, x, packed, w_scale, y, workspace, xq_out, x_scale_out, acc_out,
+                    as_stream(stream));
+}
+
+size_t bitnet_scratch_bytes(void) { return kScratchBytes; }
+
+bitnet_status bitnet_ternary_matmul_noalloc(int64_t M, int64_t N, int64_t K, const float *x,
+                                            const uint8_t *packed, const float *w_scale,
+                                            float *y, int8_t *xq_out, float *x_scale_out,
+                                            int32_t *acc_out, void *stream) {
+  bitnet_status st = matmul_args_ok(M, N, K, x, packed, w_scale, y, xq_out, x_scale_out, acc_out);
+  if (st != BITNET_OK) return st;
+  if (bitnet_matmul_workspace_bytes(M, K) > kScratchBytes) return BITNET_ERR_SCRATCH;
+  st = device_check();
+  if (st != BITNET_OK) return st;
+  void *ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != BITNET_OK) return st;
+  return matmul_run(M, N, K, x, packed, w_scale, y, ws, xq_out, x_scale_out, acc_out,
                     as_stream(stream));
 }
 

@@ -246,3 +246,19 @@ def test_table_entry_points_validation(L):
     assert h(1, 151936, 1536, A + 4, A, A, A, NULL, NULL, NULL, NULL) == ERR["ALIGN"]
     assert h(1, 151936, 1536, A, A, A, A, A + 4, NULL, NULL, NULL) == ERR["ALIGN"]
 
+
+def test_noalloc_validation(L):
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    L.bitnet_scratch_bytes.argtypes = []
+    L.bitnet_scratch_bytes.restype = sz
+    L.bitnet_ternary_matmul_noalloc.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, p]
+    L.bitnet_ternary_matmul_noalloc.restype = i32
+    assert L.bitnet_scratch_bytes() == 32 << 20
+    f = L.bitnet_ternary_matmul_noalloc
+    assert f(1, 1536, 1536, NULL, A, A, A, NULL, NULL, NULL, NULL) == ERR["NULL"]
+    assert f(1, 1536, 1000, A, A, A, A, NULL, NULL, NULL, NULL) == ERR["SHAPE"]
+    assert f(1, 1536, 1536, A + 4, A, A, A, NULL, NULL, NULL, NULL) == ERR["ALIGN"]
+    # beyond the built-in scratch: rejected on the host, nothing launched
+    assert L.bitnet_matmul_workspace_bytes(1800, 18688) > L.bitnet_scratch_bytes()
+    assert L.bitnet_matmul_workspace_bytes(1800, 18560) <= L.bitnet_scratch_bytes()
+    assert f(1800, 64, 18688, A, A, A, A, NULL, NULL, NULL, NULL) == 8
