@@ -214,3 +214,91 @@ def test_i8_linear_tall_tiles(tb):
     acc_ref, d, y_ref = oracle.i8_linear_sampled(xq, xs, q_ref, s_ref, None, False, ms, ns)
     np.testing.assert_array_equal(acc.cpu().numpy()[rows][:, cols].reshape(-1), acc_ref)
     check_y(y.cpu().numpy()[rows][:, cols].reshape(-1), y_ref, d, np.zeros(ms.size), "tall tiles")
+
+
+# ---- per-channel weight scales (bitnet_i8_linear_rows) ----------------------
+# Bound of the per-channel epilogue fl32(fl32(fl32(acc) * s[n]) * fl32(1 / x_scale))
+# + bias: five roundings.
+TOL_ROWS = 5.0 * 2.0 ** -24
+
+
+def check_y_rows(y, ref_y, d, bias_vals, what):
+    bound = TOL_ROWS * (np.abs(d) + np.abs(bias_vals)) + 1e-37
+    err = np.abs(y.astype(np.float64) - ref_y.astype(np.float64))
+    worst = (err / bound).max() if err.size else 0.0
+    assert worst <= 1.0, f"{what}: error {worst:.3f} x the bound"
+
+
+def run_linear_rows(tb, M, N, K, bias_on, relu, seed, zero_row=False, zero_channel=False):
+    import torch
+    dev = "cuda:0"
+    rng = np.random.default_rng(seed)
+    x = synth.activations(M, K, seed)
+    if zero_row:
+        x[M // 2] = 0
+    W = synth.student_t_weights(N, K, seed + 1)
+    if zero_channel:
+        W[N // 3] = 0
+    b = (rng.standard_normal(N, dtype=np.float32) * np.float32(0.1)) if bias_on else None
+    q, s = oracle.rowq_quant_weights(W)
+    qd, sd = tb.bitnet_i8_quant_weights_rows(torch.from_numpy(W).to(dev))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(qd.cpu().numpy(), q)
+    assert sd.cpu().numpy().tobytes() == s.tobytes()
+    ref = oracle.i8_linear_rows(x, q, s, b, relu)
+    bd = torch.from_numpy(b).to(dev) if b is not None else None
+    xd = torch.from_numpy(x).to(dev)
+    ybuf = torch.full((M * N + 64,), float("nan"), device=dev)
+    y = ybuf[:M * N].view(M, N)
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev)
+    ws = torch.empty(tb.bitnet_i8_linear_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    tb.bitnet_i8_linear_rows_into(M, N, K, xd, qd, sd, bd, relu, y, ws, acc)
+    torch.cuda.synchronize()
+    assert torch.isnan(ybuf[M * N:]).all().item(), "wrote past the end of y"
+    np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
+    d = (ref["acc"].astype(np.float64) * s.astype(np.float64)[None, :]
+         / ref["x_scale"].astype(np.float64)[:, None])
+    bias_vals = np.zeros((M, N)) if b is None else np.broadcast_to(b.astype(np.float64), (M, N))
+    check_y_rows(y.cpu().numpy(), ref["y"], d, bias_vals, f"M={M} N={N} K={K}")
+    if relu:
+        assert (y >= 0).all().item()
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (5, 7, 64), (130, 200, 192), (257, 129, 512),
+                                   (64, 2048, 512), (300, 96, 2048)])
+@pytest.mark.parametrize("bias_on,relu", [(True, True), (False, False)])
+def test_i8_linear_rows_parity(tb, M, N, K, bias_on, relu):
+    say(f"[i8 rows] linear M={M} N={N} K={K} bias={bias_on} relu={relu}")
+    run_linear_rows(tb, M, N, K, bias_on, relu, seed=M * 5 + N * 11 + K)
+
+
+def test_i8_linear_rows_zero_row_and_channel(tb):
+    say("[i8 rows] zero activation row and zero weight channel")
+    run_linear_rows(tb, 40, 130, 256, True, False, seed=91, zero_row=True, zero_channel=True)
+
+
+def test_i8_linear_rows_tall_tiles_sampled(tb):
+    """4096 tiles of 128 rows (the tall-tile path) with per-channel scales."""
+    import torch
+    M, N, K = 16384, 4096, 64
+    say(f"[i8 rows] linear M={M} N={N} K={K}, 128-row tiles")
+    dev = "cuda:0"
+    x = synth.activations(M, K, 6321)
+    W = synth.normal_weights(N, K, 6322)
+    b = (np.random.default_rng(6323).standard_normal(N, dtype=np.float32) * np.float32(0.1))
+    q, s = oracle.rowq_quant_weights(W)
+    y, acc = tb.bitnet_i8_linear_rows(torch.from_numpy(x).to(dev), torch.from_numpy(q).to(dev),
+                                      torch.from_numpy(s).to(dev), torch.from_numpy(b).to(dev),
+                                      True, return_acc=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 32)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 64)]))
+    xq, xs = oracle.quant_act(x[rows])
+    ms = np.repeat(np.arange(rows.size), cols.size).astype(np.int64)
+    ns = np.tile(cols, rows.size).astype(np.int64)
+    acc_ref, d, y_ref = oracle.i8_linear_rows_sampled(xq, xs, q, s, b, True, ms, ns)
+    np.testing.assert_array_equal(acc.cpu().numpy()[rows][:, cols].reshape(-1), acc_ref)
+    check_y_rows(y.cpu().numpy()[rows][:, cols].reshape(-1), y_ref, d, b[ns].astype(np.float64),
+                 "tall tiles")
+    assert not torch.isnan(y).any().item()
