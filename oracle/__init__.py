@@ -74,6 +74,11 @@ def lib():
         L.oracle_i8_linear_rows.argtypes = [i64, i64, i64, p, p, p, p, ctypes.c_int, p, p, p, p]
         L.oracle_i8_linear_rows_sampled.argtypes = [i64, p, p, p, p, p, ctypes.c_int, p, p, i64,
                                                     p, p, p]
+        L.oracle_table_bytes.argtypes = [i64, i64]
+        L.oracle_table_bytes.restype = i64
+        L.oracle_table_pack.argtypes = [p, i64, i64, p]
+        L.oracle_table_unpack.argtypes = [p, i64, i64, p]
+        L.oracle_table_unpack.restype = i64
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -360,3 +365,27 @@ def i8_linear_rows_sampled(xq, x_scale, q, w_scale, bias, relu, ms, ns):
                                         None if b is None else _ptr(b), int(bool(relu)),
                                         _ptr(ms), _ptr(ns), ms.size, _ptr(acc), _ptr(d), _ptr(y))
     return acc, d, y
+
+
+# ---- storage layout of the 8-bit table ----------------------------------------
+
+def table_bytes(V: int, K: int) -> int:
+    return int(lib().oracle_table_bytes(V, K))
+
+
+def table_pack(q: np.ndarray) -> np.ndarray:
+    """int8 codes [V,K] (row-major) -> the table's tiled bytes (int8, padded)."""
+    q = _c(q, np.int8)
+    V, K = q.shape
+    out = np.empty(table_bytes(V, K), np.int8)
+    lib().oracle_table_pack(_ptr(q), V, K, _ptr(out))
+    return out
+
+
+def table_unpack(table: np.ndarray, V: int, K: int):
+    """Tiled table bytes -> (codes int8 [V,K], number of nonzero padding bytes)."""
+    table = _c(table, np.int8)
+    assert table.size == table_bytes(V, K)
+    q = np.empty((V, K), np.int8)
+    bad = lib().oracle_table_unpack(_ptr(table), V, K, _ptr(q))
+    return q, int(bad)

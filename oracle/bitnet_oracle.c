@@ -499,3 +499,46 @@ void oracle_i8_linear_rows_sampled(int64_t K, const int8_t *xq, const float *x_s
         y[i] = (float)v;
     }
 }
+
+/* ---------------------------------------------------------------------- */
+/* Storage layout of the 8-bit table (the library's own)                    */
+/* ---------------------------------------------------------------------- */
+/*
+ * The pages fix only "8-bit per-row" for the table; its byte order in
+ * memory is this library's.  Rows are grouped by 16 and inputs by 256; each
+ * 16-row x 256-input tile is 4096 contiguous bytes, tiles ordered by row
+ * group, then by input chunk.  Inside a tile, input k = 64j + 16h + e
+ * (j, h < 4, e < 16) of tile row r sits at byte 1024j + 256h + 16r + e.
+ * The table is padded with zero codes to Vp = 16*ceil(V/16) rows and
+ * Kp = 256*ceil(K/256) inputs.
+ */
+int64_t oracle_table_bytes(int64_t V, int64_t K) {
+    int64_t Vp = (V + 15) / 16 * 16, Kp = (K + 255) / 256 * 256;
+    return Vp * Kp;
+}
+
+static int64_t table_offset(int64_t K, int64_t v, int64_t k) {
+    int64_t chunks = (K + 255) / 256;            /* 256-input chunks per row group */
+    int64_t tile = (v / 16) * chunks + k / 256;
+    int64_t j = (k % 256) / 64, h = (k % 64) / 16, e = k % 16;
+    return tile * 4096 + j * 1024 + h * 256 + (v % 16) * 16 + e;
+}
+
+void oracle_table_pack(const int8_t *q, int64_t V, int64_t K, int8_t *table) {
+    memset(table, 0, (size_t)oracle_table_bytes(V, K));
+    for (int64_t v = 0; v < V; ++v)
+        for (int64_t k = 0; k < K; ++k) table[table_offset(K, v, k)] = q[v * K + k];
+}
+
+/* Inverse of oracle_table_pack.  Returns the number of padding bytes that are
+ * not zero (a valid table has none). */
+int64_t oracle_table_unpack(const int8_t *table, int64_t V, int64_t K, int8_t *q) {
+    int64_t Vp = (V + 15) / 16 * 16, Kp = (K + 255) / 256 * 256, bad = 0;
+    for (int64_t v = 0; v < Vp; ++v)
+        for (int64_t k = 0; k < Kp; ++k) {
+            int8_t b = table[table_offset(K, v, k)];
+            if (v < V && k < K) q[v * K + k] = b;
+            else if (b != 0) ++bad;
+        }
+    return bad;
+}

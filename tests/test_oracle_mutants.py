@@ -82,6 +82,12 @@ ROWQ_MUTANTS = {
     # per-channel layer: one channel's scale for all
     "rows_scale_first": ("double v = (double)acc[m * N + n] * (double)w_scale[n] / (double)xs[m];",
                          "double v = (double)acc[m * N + n] * (double)w_scale[0] / (double)xs[m];"),
+    # table layout: the 16-input groups and the 64-input steps swapped
+    "table_h_j_swapped": ("return tile * 4096 + j * 1024 + h * 256 + (v % 16) * 16 + e;",
+                          "return tile * 4096 + h * 1024 + j * 256 + (v % 16) * 16 + e;"),
+    # table layout: tiles ordered by input chunk first
+    "table_chunk_major": ("int64_t tile = (v / 16) * chunks + k / 256;",
+                          "int64_t tile = (k / 256) * 16 + v / 16;"),
     # embedding rows read transposed
     "rowq_embed_transposed": ("(float)((double)q[id * K + k] * (double)w_scale[id])",
                               "(float)((double)q[(k % N) * K + id % K] * (double)w_scale[id])"),

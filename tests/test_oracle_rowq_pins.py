@@ -188,3 +188,41 @@ def test_per_channel_sampled_matches_full():
     acc, d, y = oracle.i8_linear_rows_sampled(full["xq"], full["x_scale"], q, s, b, True, ms, ns)
     np.testing.assert_array_equal(acc, full["acc"].ravel())
     np.testing.assert_array_equal(y, full["y"].ravel())
+
+
+# ---- the table's storage layout ----------------------------------------------
+
+def test_table_layout_golden():
+    rows = read_golden("table_layout.txt")
+    V = int([r for r in rows if r[0] == "V"][0][1])
+    K = int([r for r in rows if r[0] == "K"][0][1])
+    assert oracle.table_bytes(V, K) == int([r for r in rows if r[0] == "bytes"][0][1])
+    for r in rows:
+        if r[0] != "at":
+            continue
+        v, k, off = int(r[1]), int(r[2]), int(r[3])
+        q = np.zeros((V, K), np.int8)
+        q[v, k] = 7
+        t = oracle.table_pack(q)
+        assert np.flatnonzero(t).tolist() == [off], (v, k)
+
+
+@pytest.mark.parametrize("V,K", [(1, 64), (16, 256), (37, 320), (40, 1536), (100, 768)])
+def test_table_round_trip_and_padding(V, K):
+    rng = np.random.default_rng(V * K)
+    q = rng.integers(-127, 128, size=(V, K), dtype=np.int16).astype(np.int8)
+    t = oracle.table_pack(q)
+    assert t.size == ((V + 15) // 16 * 16) * ((K + 255) // 256 * 256)
+    back, bad = oracle.table_unpack(t, V, K)
+    assert bad == 0
+    np.testing.assert_array_equal(back, q)
+    # all-ones codes: the zero bytes of the table are exactly its padding, so
+    # the layout is a bijection onto the other bytes
+    ones = oracle.table_pack(np.ones((V, K), np.int8))
+    assert np.count_nonzero(ones) == V * K
+    pad = np.flatnonzero(ones == 0)
+    assert pad.size == t.size - V * K
+    if pad.size:
+        t2 = t.copy()
+        t2[pad[pad.size // 2]] = 1
+        assert oracle.table_unpack(t2, V, K)[1] == 1
