@@ -79,6 +79,8 @@ def lib():
         L.oracle_table_pack.argtypes = [p, i64, i64, p]
         L.oracle_table_unpack.argtypes = [p, i64, i64, p]
         L.oracle_table_unpack.restype = i64
+        L.oracle_i8_col_quant.argtypes = [p, i64, i64, i64, p, p]
+        L.oracle_i8_dwconv.argtypes = [i64, i64, i64, i64, p, p, p, p, ctypes.c_int, p, p, p, p]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -389,3 +391,35 @@ def table_unpack(table: np.ndarray, V: int, K: int):
     q = np.empty((V, K), np.int8)
     bad = lib().oracle_table_unpack(_ptr(table), V, K, _ptr(q))
     return q, int(bad)
+
+
+# ---- I8_S depthwise convolution over time --------------------------------------
+
+def i8_col_quant(x: np.ndarray):
+    """fp32 x [B,T,C] -> (xq int8 [B,T,C], x_scale float32 [B,C]): one absmax
+    scale per (sequence, channel)."""
+    x = _c(x, np.float32)
+    B, T, C = x.shape
+    xq = np.empty((B, T, C), np.int8)
+    xs = np.empty((B, C), np.float32)
+    lib().oracle_i8_col_quant(_ptr(x), B, T, C, _ptr(xq), _ptr(xs))
+    return xq, xs
+
+
+def i8_dwconv(x: np.ndarray, q: np.ndarray, w_scale: np.ndarray, bias=None, relu=False):
+    """Causal depthwise convolution over frames: x [B,T,C], int8 kernel q [C,k]
+    with per-channel scales -> dict(y [B,T,C], xq, x_scale [B,C], acc)."""
+    x = _c(x, np.float32)
+    q = _c(q, np.int8)
+    s = _c(w_scale, np.float32)
+    B, T, C = x.shape
+    k = q.shape[1]
+    b = None if bias is None else _c(bias, np.float32)
+    y = np.empty((B, T, C), np.float32)
+    xq = np.empty((B, T, C), np.int8)
+    xs = np.empty((B, C), np.float32)
+    acc = np.empty((B, T, C), np.int32)
+    lib().oracle_i8_dwconv(B, T, C, k, _ptr(x), _ptr(q), _ptr(s),
+                           None if b is None else _ptr(b), int(bool(relu)), _ptr(y), _ptr(xq),
+                           _ptr(xs), _ptr(acc))
+    return {"y": y, "xq": xq, "x_scale": xs, "acc": acc}

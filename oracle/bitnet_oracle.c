@@ -542,3 +542,81 @@ int64_t oracle_table_unpack(const int8_t *table, int64_t V, int64_t K, int8_t *q
         }
     return bad;
 }
+
+/* ---------------------------------------------------------------------- */
+/* I8_S depthwise convolution over time (the encoders' token mixer)         */
+/* ---------------------------------------------------------------------- */
+/*
+ * The encoders run fused int8 convolution and depthwise convolution routines
+ * with bias (aitrends.kr summary, technical-features section: fused conv,
+ * depthwise conv and matmul+bias+ReLU over permuted layouts); their ONNX
+ * export pads the convolutions causally (ONNX model card
+ * "multimodalart/VibeVoice-ASR-BitNet-ONNX", Provenance: static causal
+ * padding of the tokenizer encoders); the weights are int8 per channel (same
+ * card, Quantization table, row "VAE encoders").  Readings used here:
+ *  - x is [B, T, C] (sequences, frames, channels; channels innermost, the
+ *    layout of the pointwise layers' rows), the kernel w is [C, k];
+ *  - y[b,t,c] = sum_{j<k} w[c,j] * x[b, t-(k-1)+j, c], frames before 0 are 0;
+ *  - weights quantized per channel as the table rows above
+ *    (oracle_rowq_quant_weights on [C, k]);
+ *  - activations quantized with one scale per (sequence, channel): the
+ *    convolution sums over frames within a channel, so one scale per channel
+ *    keeps that sum exact in int32 (as one scale per row does for the
+ *    pointwise layers, which sum over channels within a frame):
+ *    s[b,c] = fl32(127 / max_t |x[b,t,c]|), xq = clamp(rint(fl32(x * s)),
+ *    -127, 127); an all-zero column gives xq = 0 and s = 1;
+ *  - y = relu?(acc * w_scale[c] / s[b,c] + bias[c]) in fp64, rounded once.
+ */
+void oracle_i8_col_quant(const float *x, int64_t B, int64_t T, int64_t C, int8_t *xq,
+                         float *x_scale) {
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < C; ++c) {
+            const float *col = x + b * T * C + c;     /* stride C */
+            float a = 0.0f;
+            for (int64_t t = 0; t < T; ++t) {
+                float v = fabsf(col[t * C]);
+                if (v > a) a = v;
+            }
+            int8_t *dst = xq + b * T * C + c;
+            if (a == 0.0f) {
+                for (int64_t t = 0; t < T; ++t) dst[t * C] = 0;
+                x_scale[b * C + c] = 1.0f;
+                continue;
+            }
+            float s = 127.0f / a;                    /* fp32, correctly rounded */
+            x_scale[b * C + c] = s;
+            for (int64_t t = 0; t < T; ++t) {
+                float u = rintf(col[t * C] * s);     /* fp32 product, half to even */
+                if (u > 127.0f) u = 127.0f;
+                if (u < -127.0f) u = -127.0f;
+                dst[t * C] = (int8_t)u;
+            }
+        }
+}
+
+void oracle_i8_dwconv(int64_t B, int64_t T, int64_t C, int64_t k, const float *x,
+                      const int8_t *q, const float *w_scale, const float *bias, int relu,
+                      float *y, int8_t *xq_out, float *x_scale_out, int32_t *acc_out) {
+    int8_t *xq = (int8_t *)malloc((size_t)(B * T * C));
+    float *xs = (float *)malloc(sizeof(float) * (size_t)(B * C));
+    oracle_i8_col_quant(x, B, T, C, xq, xs);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t c = 0; c < C; ++c) {
+                int32_t acc = 0;
+                for (int64_t j = 0; j < k; ++j) {
+                    int64_t src = t - (k - 1) + j;   /* causal: earlier frames only */
+                    if (src >= 0) acc += (int32_t)xq[(b * T + src) * C + c] * (int32_t)q[c * k + j];
+                }
+                int64_t o = (b * T + t) * C + c;
+                if (acc_out) acc_out[o] = acc;
+                double v = (double)acc * (double)w_scale[c] / (double)xs[b * C + c];
+                if (bias) v += (double)bias[c];
+                if (relu && v <= 0.0) v = 0.0;
+                y[o] = (float)v;
+            }
+    if (xq_out) memcpy(xq_out, xq, (size_t)(B * T * C));
+    if (x_scale_out) memcpy(x_scale_out, xs, sizeof(float) * (size_t)(B * C));
+    free(xq); free(xs);
+}

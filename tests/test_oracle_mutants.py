@@ -94,6 +94,26 @@ ROWQ_MUTANTS = {
 }
 
 
+# Slips in the I8_S depthwise convolution, caught by its pins.
+DWCONV_MUTANTS = {
+    # anti-causal: later frames instead of earlier ones
+    "dw_anticausal": ("int64_t src = t - (k - 1) + j;   /* causal: earlier frames only */",
+                      "int64_t src = t + j;"),
+    # kernel taps read in reverse
+    "dw_taps_reversed": ("acc += (int32_t)xq[(b * T + src) * C + c] * (int32_t)q[c * k + j];",
+                         "acc += (int32_t)xq[(b * T + src) * C + c] * (int32_t)q[c * k + (k - 1 - j)];"),
+    # one activation scale per channel shared by all sequences
+    "dw_scale_ignores_sequence": ("double v = (double)acc * (double)w_scale[c] / (double)xs[b * C + c];",
+                                  "double v = (double)acc * (double)w_scale[c] / (double)xs[c];"),
+    # activation column absmax over the first frame only
+    "dw_colmax_first_frame": ("for (int64_t t = 0; t < T; ++t) {\n                float v = fabsf(col[t * C]);",
+                              "for (int64_t t = 0; t < 1; ++t) {\n                float v = fabsf(col[t * C]);"),
+    # bias of the wrong channel
+    "dw_bias_index": ("if (bias) v += (double)bias[c];\n                if (relu && v <= 0.0) v = 0.0;\n                y[o] = (float)v;",
+                      "if (bias) v += (double)bias[(c + 1) % C];\n                if (relu && v <= 0.0) v = 0.0;\n                y[o] = (float)v;"),
+}
+
+
 def run_pins_on_mutant(tmp_path, old, new, pin_file):
     src = open(os.path.join(ROOT, "oracle", "bitnet_oracle.c")).read()
     assert old in src, "mutation site not found"
@@ -127,3 +147,10 @@ def test_rowq_pins_reject_mutant(name, tmp_path):
     old, new = ROWQ_MUTANTS[name]
     r = run_pins_on_mutant(tmp_path, old, new, "test_oracle_rowq_pins.py")
     assert r.returncode != 0, f"per-row table pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(DWCONV_MUTANTS))
+def test_dwconv_pins_reject_mutant(name, tmp_path):
+    old, new = DWCONV_MUTANTS[name]
+    r = run_pins_on_mutant(tmp_path, old, new, "test_oracle_dwconv_pins.py")
+    assert r.returncode != 0, f"depthwise-conv pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
