@@ -55,6 +55,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_grouped_decode_sweep_m1_pmc.
 DECODE_SOURCES = ("gemv.hip", "bitnet_device.hpp", "bitnet_internal.hpp")
 
 
+SWEEP_WEIGHTS = "0.02 N(0,1) fp32 masters, seed 10000+7l+p (the decode sweep's)"
+LONGFORM_WEIGHTS = "Student-t(3) fp32 masters scaled to std 0.01, seed 50000+7l+p"
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -233,7 +237,9 @@ def main():
     timer = Timer(torch, stream)
     if args.only == "i8":
         log("[bench] I8_S encoder layers only")
-        print(json.dumps(i8_configs(torch, tb, synth, timer, dev, steps=args.steps)), flush=True)
+        res = i8_configs(torch, tb, synth, timer, dev, steps=args.steps)
+        res["i8_dwconv_encoder"] = dwconv_config(torch, tb, synth, timer, dev, steps=args.steps)
+        print(json.dumps(res), flush=True)
         return
     if args.only == "lmhead":
         log("[bench] embedding / lm_head table only")
@@ -301,7 +307,14 @@ def main():
     if args.only == "prefill":
         M = args.prefill_m
         log(f"[bench] prefill M={M} only")
-        res = prefill_config(torch, tb, timer, problems, packed, w_scales, M, dev)
+        if M == synth.PREFILL_M_LONG:
+            lf = synth.longform_problems(args.layers)
+            lf_packed, lf_scales = pack_set(torch, tb, synth, lf, True, dev)
+            res = prefill_config(torch, tb, synth, timer, lf, lf_packed, lf_scales, M, dev,
+                                 LONGFORM_WEIGHTS)
+        else:
+            res = prefill_config(torch, tb, synth, timer, synth.prefill_problems(args.layers),
+                                 packed, w_scales, M, dev, SWEEP_WEIGHTS)
         if args.prefill_shapes:
             res["per_shape"] = prefill_shapes_config(torch, tb, timer, problems, packed,
                                                       w_scales, M, dev)
@@ -458,6 +471,51 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def gen_workers() -> int:
+    """Host processes for drawing the workloads' arrays (the machine's CPU share)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def pack_set(torch, tb, synth, problems, heavy_tail, dev):
+    """Draw the problems' fp32 masters on the host (worker processes), ternarize
+    and pack each on the GPU; returns (packed, w_scales)."""
+    packed, w_scales = [], []
+    ws_t = torch.empty(tb.bitnet_ternarize_workspace_bytes(synth.INTERMEDIATE),
+                       dtype=torch.uint8, device=dev)
+    for i, (p, W) in enumerate(zip(problems, synth.problem_weights_iter(problems, heavy_tail,
+                                                                      gen_workers()))):
+        if i % 28 == 0:
+            log(f"[bench] packing matrix {i} of {len(problems)}")
+        Wd = torch.from_numpy(W).to(dev)
+        pk = torch.empty(p.N * p.K // 4, dtype=torch.uint8, device=dev)
+        sc = torch.empty(1, dtype=torch.float32, device=dev)
+        tb.bitnet_ternarize_pack_into(Wd, p.N, p.K, pk, sc, ws_t)
+        packed.append(pk)
+        w_scales.append(sc)
+        del Wd
+    torch.cuda.synchronize()
+    return packed, w_scales
+
+
+def zero_code_fraction(torch, packed) -> float:
+    """Share of codes equal to 0 (2-bit field value 1) over packed buffers."""
+    zeros = total = 0
+    for t in packed:
+        v = t.to(torch.int32)
+        for sh in (0, 2, 4, 6):
+            zeros += int(((v >> sh) & 3).eq(1).sum().item())
+        total += 4 * t.numel()
+    return zeros / total
+
+
+def host_activations(torch, synth, problems, M, dev):
+    """problem_activations(p, M) for each problem (drawn on the host in worker
+    processes: N(0,1), round(0.01 K) channels x20), copied to the device."""
+    log(f"[bench] drawing activations for {len(problems)} problems, M={M}")
+    return [torch.from_numpy(x).to(dev)
+            for x in synth.problem_activations_iter(problems, M, gen_workers())]
+
+
 def gpu_activations(torch, g, M, K, dev):
     """~N(0,1) rows with 1% of the channels scaled by 20, drawn on the GPU."""
     x = torch.randn((M, K), generator=g, device=dev)
@@ -466,31 +524,43 @@ def gpu_activations(torch, g, M, K, dev):
     return x
 
 
-def prefill_config(torch, tb, timer, problems, packed, w_scales, M, dev):
-    g = torch.Generator(device=dev)
-    g.manual_seed(30000 + M)
-    xs = [gpu_activations(torch, g, M, p.K, dev) for p in problems]
+def prefill_config(torch, tb, synth, timer, problems, packed, w_scales, M, dev, weights,
+                   zero_codes_check=False):
+    """Prefill at M rows over all the problems in one grouped call per step
+    (quantization launch + GEMM launch); activations drawn per problem from its
+    own seed.  zero_codes_check: also time the same step with every code 0."""
+    xs = host_activations(torch, synth, problems, M, dev)
     ys = [torch.empty((M, p.N), device=dev) for p in problems]
     plan = tb.GroupedPlan(M, xs, packed, w_scales, ys, [p.N for p in problems],
                           [p.K for p in problems])
-    ms = timer.time(lambda i=0: plan.run(), 5 if M > 1000 else 10, warmup=5)
+    steps = 5 if M > 1000 else 10
+    ms = timer.time(lambda i=0: plan.run(), steps, warmup=5)
     ops = 2.0 * M * sum(p.N * p.K for p in problems)
     res = {"ms_per_step": round(ms, 4), "int8_TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
            "frac_of_int8_peak": round(ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
            "step": "quantization launch + int8 MFMA GEMM launch over all matrices",
-           "activations": "seeded on the GPU: N(0,1), 1% of channels x20"}
+           "weights": weights,
+           "activations": f"host numpy, seed {problems[0].x_seed - 7 * problems[0].layer - problems[0].proj}"
+                          "+7l+p: N(0,1), round(0.01 K) channels x20"}
+    if zero_codes_check:
+        zc = [torch.full_like(t, 0x55) for t in packed]
+        zplan = tb.GroupedPlan(M, xs, zc, w_scales, ys, [p.N for p in problems],
+                               [p.K for p in problems])
+        ms_z = timer.time(lambda i=0: zplan.run(), steps, warmup=3)
+        ms_r = timer.time(lambda i=0: plan.run(), steps, warmup=3)
+        res["code_independence"] = {"ms_per_step_all_zero_codes": round(ms_z, 4),
+                                    "ms_per_step_these_codes": round(ms_r, 4)}
+        del zc, zplan
     del xs, ys, plan
     torch.cuda.empty_cache()
     return res
 
 
-def prefill_layer_config(torch, tb, timer, problems, packed, w_scales, M, dev):
+def prefill_layer_config(torch, tb, synth, timer, problems, packed, w_scales, M, dev):
     """One layer's 7 projections at prefill in one grouped call (quantization +
     GEMM); step i runs layer i % 28, so every step reads its codes from HBM."""
-    g = torch.Generator(device=dev)
-    g.manual_seed(31000 + M)
     layer = problems[:7]
-    xs = [gpu_activations(torch, g, M, p.K, dev) for p in layer]
+    xs = host_activations(torch, synth, layer, M, dev)
     ys = [torch.empty((M, p.N), device=dev) for p in layer]
     layers = len(problems) // 7
     plans = [tb.GroupedPlan(M, xs, packed[7 * l:7 * l + 7], w_scales[7 * l:7 * l + 7], ys,
@@ -585,7 +655,13 @@ def chain_configs(torch, tb, synth, timer, problems, packed, w_scales, alg_bytes
         "us_per_token_eager_launches": round(ms_eager * 1e3, 2),
         "graph_replays_match_eager": bool(replay_ok),
         "note": "28 layers x 4 dependent grouped launches (qkv, o, gate+up, down), HIP graph"}
-    del chain, chain_ys, eager, graph
+    # Tear the graph down here, while the process is fully alive: free its
+    # executable and its private memory pool, and drain the capture stream.
+    graph.reset()
+    cap.synchronize()
+    torch.cuda.synchronize()
+    del chain, chain_ys, eager, graph, cap
+    torch.cuda.empty_cache()
 
     # The same token as one staged call: 112 stages in one cooperative launch,
     # each stage reading what the one before it wrote (q,k,v read h; o reads
@@ -619,11 +695,15 @@ def chain_configs(torch, tb, synth, timer, problems, packed, w_scales, alg_bytes
     staged_ok = all(torch.equal(a, b) for a, b in zip(flow_ys, ref)) and not staged.timed_out()
     ms = timer.time(lambda i=0: staged.run(), 100)
     timed_out = staged.timed_out()
+    # every call of this plan so far (checks, warm-up, timed): calls in which
+    # some wait between stages ran out
+    timeouts_total = staged.timeouts_total()
     out["decode_token_staged_m1"] = {
         "us_per_token": round(ms * 1e3, 2), "launches": 1, "stages": len(stages),
         "weight_GBps": round(sum(p.N * p.K // 4 for p in problems) / (ms * 1e-3) / 1e9, 1),
         "frac_of_hbm_peak": round(alg_bytes(1, problems) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "matches_grouped_launches": bool(staged_ok), "wait_timed_out": bool(timed_out),
+        "calls_with_a_wait_timed_out": int(timeouts_total),
         "note": "one token, 28 layers x 4 dependent stages, one cooperative launch"}
     del staged, launches, stages, flow_ys, ref
 
@@ -660,6 +740,30 @@ def i8_configs(torch, tb, synth, timer, dev, steps=100):
     return out
 
 
+def dwconv_config(torch, tb, synth, timer, dev, steps=100):
+    """The encoder block's causal depthwise convolution (I8_S: per-channel int8
+    kernel, per-channel activation scales) over 8192 frames x 512 channels, 7
+    taps, with bias: the column-maximum launch and the convolution launch.
+    Four (x, y) buffer sets rotate."""
+    B, T, C, k = 1, synth.I8_FRAMES, 512, 7
+    x0 = torch.from_numpy(synth.activations(B * T, C, 70100).reshape(B, T, C)).to(dev)
+    W = torch.from_numpy(synth.normal_weights(C, k, 70101, std=0.1)).to(dev)
+    b = torch.from_numpy(synth.normal_weights(1, C, 70102, std=0.1)[0]).to(dev)
+    q, s = tb.bitnet_i8_dwconv_quant_weights(W)
+    xs = [x0] + [x0.clone() for _ in range(3)]
+    ys = [torch.empty_like(x0) for _ in range(4)]
+    ws = torch.empty(tb.bitnet_i8_dwconv_workspace_bytes(B, T, C), dtype=torch.uint8, device=dev)
+    ms = timer.time(lambda i=0: tb.bitnet_i8_dwconv_into(B, T, C, k, xs[i % 4], q, s, b, False,
+                                                         ys[i % 4], ws), steps, warmup=50)
+    alg = 2 * B * T * C * 4 + C * k + 2 * C * 4
+    return {"shape": {"B": B, "T": T, "C": C, "k": k, "bias": True},
+            "us_per_call": round(ms * 1e3, 2),
+            "GBps_moved": round(alg / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "algorithmic_bytes": alg,
+            "step": "column-maximum launch + convolution launch (x read twice, once per launch)"}
+
+
 def lmhead_configs(torch, tb, synth, timer, dev, steps=200):
     """The decoder's 8-bit table (151,936 x 1536, one scale per row): the
     lm_head at M = 1, 4 and 16 (one launch each: per-row activation
@@ -668,7 +772,7 @@ def lmhead_configs(torch, tb, synth, timer, dev, steps=200):
     embedding lookup of a 256-token prompt."""
     V, K = synth.VOCAB, synth.HIDDEN
     W = torch.from_numpy(synth.table_weights()).to(dev)
-    q, s = tb.bitnet_i8_quant_weights_rows(W)
+    q, s = tb.bitnet_table_quant(W)
     del W
     qs = [q] + [q.clone() for _ in range(2)]
     out = {}
@@ -813,6 +917,7 @@ def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, a
 
     pbytes = sum(p.N * p.K // 4 for p in problems)
     out.update(i8_configs(torch, tb, synth, timer, dev))
+    out["i8_dwconv_encoder"] = dwconv_config(torch, tb, synth, timer, dev)
     out.update(lmhead_configs(torch, tb, synth, timer, dev))
     out["decode_sweep_m1_lut"] = lut_config(torch, tb, synth, timer, problems, packed, copy_b,
                                             w_scales, alg_bytes, decode_plans, dev)
@@ -850,34 +955,55 @@ def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, a
             "frac_of_hbm_peak": round(sb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
         del plans, ys, xs_sh, shared
 
-    # Prefill: M=256 (30 s of audio + prompt) and M=1800 (4 min of audio) over
-    # the same 196 matrices.
-    for M in (synth.PREFILL_M_30S, synth.PREFILL_M_LONG):
-        out[f"prefill_m{M}"] = prefill_config(torch, tb, timer, problems, packed, w_scales, M, dev)
-    out[f"prefill_one_layer_m{synth.PREFILL_M_30S}"] = prefill_layer_config(
-        torch, tb, timer, problems, packed, w_scales, synth.PREFILL_M_30S, dev)
+    # Prefill at M=256 (30 s of audio + prompt) over the sweep's 196 matrices,
+    # activations seed 30000+7l+p.
+    layers = len(problems) // 7
+    M = synth.PREFILL_M_30S
+    out[f"prefill_m{M}"] = prefill_config(torch, tb, synth, timer, synth.prefill_problems(layers),
+                                          packed, w_scales, M, dev, SWEEP_WEIGHTS)
+    out[f"prefill_one_layer_m{M}"] = prefill_layer_config(
+        torch, tb, synth, timer, synth.prefill_problems(layers), packed, w_scales, M, dev)
+
+    # Long-form prefill (M=1800, 4 min of audio) and batched decode (M=32, 64)
+    # on their own weights: 196 Student-t(3) masters scaled to std 0.01,
+    # weights seed 50000+7l+p, activations seed 60000+7l+p.
+    lf = synth.longform_problems(layers)
+    t0 = time.perf_counter()
+    lf_packed, lf_scales = pack_set(torch, tb, synth, lf, True, dev)
+    lf_zero = zero_code_fraction(torch, lf_packed)
+    out["longform_weights"] = {"matrices": len(lf), "zero_code_fraction": round(lf_zero, 4),
+                               "host_draw_and_pack_s": round(time.perf_counter() - t0, 1),
+                               "generator": LONGFORM_WEIGHTS}
+    M = synth.PREFILL_M_LONG
+    out[f"prefill_m{M}"] = prefill_config(torch, tb, synth, timer, lf, lf_packed, lf_scales, M,
+                                          dev, LONGFORM_WEIGHTS, zero_codes_check=True)
+    out[f"prefill_m{M}"]["zero_code_fraction"] = round(lf_zero, 4)
     for M in (synth.PREFILL_M_30S, synth.PREFILL_M_LONG):
         out[f"prefill_per_shape_m{M}"] = prefill_shapes_config(
             torch, tb, timer, problems, packed, w_scales, M, dev)
 
-    # Batched decode: M=32 and 64 on the 28 gate and 28 down matrices.
-    sub = [p for p in problems if p.proj in (4, 6)]
-    g = torch.Generator(device=dev)
+    # Batched decode: M=32 and 64 on the 28 gate and 28 down long-form matrices,
+    # two packed copies alternating.
+    sub_i = [i for i, p in enumerate(lf) if p.proj in (4, 6)]
+    sub = [lf[i] for i in sub_i]
+    lf_copy = {i: lf_packed[i].clone() for i in sub_i}
     for M in (32, 64):
-        g.manual_seed(40000 + M)
-        xs = [gpu_activations(torch, g, M, p.K, dev) for p in sub]
-        idx = [problems.index(p) for p in sub]
+        xs = host_activations(torch, synth, sub, M, dev)
         ys = [torch.empty((M, p.N), device=dev) for p in sub]
-        plans = [tb.GroupedPlan(M, xs, [c[i] for i in idx], [w_scales[i] for i in idx], ys,
-                                [p.N for p in sub], [p.K for p in sub]) for c in (packed, copy_b)]
+        plans = [tb.GroupedPlan(M, xs, [c[i] for i in sub_i], [lf_scales[i] for i in sub_i], ys,
+                                [p.N for p in sub], [p.K for p in sub])
+                 for c in (lf_packed, lf_copy)]
         ms = timer.time(lambda i=0: plans[i % 2].run(), 500, warmup=100)
         sb = sum(p.N * p.K // 4 for p in sub)
         ops = 2.0 * M * sum(p.N * p.K for p in sub)
         out[f"batched_decode_m{M}"] = {
             "us_per_step": round(ms * 1e3, 2), "weight_GBps": round(sb / (ms * 1e-3) / 1e9, 1),
             "int8_TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
-            "frac_of_hbm_peak": round(alg_bytes(M, sub) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+            "frac_of_hbm_peak": round(alg_bytes(M, sub) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "weights": LONGFORM_WEIGHTS, "zero_code_fraction": round(lf_zero, 4)}
         del xs, ys, plans
+    del lf_packed, lf_scales, lf_copy
+    torch.cuda.empty_cache()
     return out
 
 

@@ -269,50 +269,106 @@ bitnet_status bitnet_i8_linear(int64_t M, int64_t N, int64_t K, const float *x, 
                                void *stream);
 
 /* ------------------------------------------------------------------------
+ * I8_S causal depthwise convolution over frames: the encoders' token mixer.
+ * The encoders fuse int8 convolution and depthwise convolution with bias
+ * (aitrends.kr summary, technical-features section), padded causally in the
+ * ONNX export (ONNX model card, Provenance), with int8 per-channel weights
+ * (same card, Quantization table, row "VAE encoders").  The pages give no
+ * formula; this library's:
+ *   y[b,t,c] = relu?(acc * w_scale[c] / x_scale[b,c] + bias[c]), rounded
+ *              once to fp32 from fp64 (exact product, correctly rounded
+ *              division, then the bias add), bit-exact;
+ *   acc      = sum_{j<k} q[c,j] * xq[b, t-(k-1)+j, c] (frames before 0 count
+ *              as 0), int32;
+ *   xq, x_scale: x quantized with one absmax scale per (sequence, channel),
+ *              x_scale = fl32(127 / max_t |x[b,t,c]|), round half to even,
+ *              clamp +-127; an all-zero column gives xq = 0, x_scale = 1.
+ *
+ * bitnet_i8_dwconv_quant_weights: W fp32 [C,k] -> q int8 [C,k] and w_scale
+ *   fp32 [C], per channel as the table rows (bitnet_table_quant's formula).
+ *   C % 64 == 0, 1 <= k <= 64.  One launch.
+ * bitnet_i8_dwconv: x fp32 [B,T,C] (channels innermost, 16-byte aligned),
+ *   y fp32 [B,T,C] (16-byte aligned), bias [C] or NULL, acc_out int32
+ *   [B,T,C] (16-byte aligned) and x_scale_out fp32 [B,C] optional.
+ *   B <= 65535, C % 64 == 0, 1 <= k <= 64, B*T*C < 2^29.  workspace:
+ *   bitnet_i8_dwconv_workspace_bytes(B, T, C) bytes, 16-byte aligned (the
+ *   column maxima of each 128-frame chunk).  Two launches.
+ * ------------------------------------------------------------------------ */
+bitnet_status bitnet_i8_dwconv_quant_weights(const float *W, int64_t C, int64_t k, int8_t *q,
+                                             float *w_scale, void *stream);
+
+size_t bitnet_i8_dwconv_workspace_bytes(int64_t B, int64_t T, int64_t C);
+
+bitnet_status bitnet_i8_dwconv(int64_t B, int64_t T, int64_t C, int64_t k, const float *x,
+                               const int8_t *q, const float *w_scale, const float *bias,
+                               int32_t relu, float *y, void *workspace, size_t workspace_bytes,
+                               int32_t *acc_out, float *x_scale_out, void *stream);
+
+/* ------------------------------------------------------------------------
  * The decoder's 8-bit table with one scale per row: token embeddings and the
  * lm_head.  The ONNX build stores both at 8 bits, "per-row / per-column", where
  * the GGUF build uses Q6_K (ONNX model card "multimodalart/VibeVoice-ASR-
  * BitNet-ONNX", Quantization table, row "Embeddings / lm_head"; xujun.org
  * article, heterogeneous-quantization section: I2_S plus Q6_K embeddings).
- * One table [V, K] (vocabulary x hidden, row-major) serves both: row v is
+ * One table (V vocabulary rows x K hidden inputs) serves both: row v is
  * token v's embedding and, read as the lm_head weight, the weights of logit v,
  * so its per-row scales are the lm_head's per-column scales.  The Q6_K block
  * format is not on the pages; this 8-bit form is the card's ONNX one.
  *
- * bitnet_i8_quant_weights_rows: W fp32 [N,K] row-major -> q int8 [N,K] and
- *   w_scale fp32 [N]: per row n, w_scale[n] = fl32(max_k |W[n,k]| / 127),
- *   q = clamp(rint(fl32(W / w_scale[n])), -127, 127), half to even; a zero row
- *   gives w_scale[n] = 0 and q = 0.  Bit-exact.  N >= 1, K >= 64, K % 64 == 0,
- *   N*K < 2^31; W and q 16-byte aligned, w_scale 4-byte.  One launch, no
- *   workspace.  The same scales serve as per-output-channel scales of an
- *   I8_S layer (bitnet_i8_linear_rows).
+ * Table storage order (this library's own; the pages fix only 8 bits per code
+ * and one scale per row): rows are grouped by 16 and inputs by 256; each
+ * 16-row x 256-input tile is 4096 contiguous bytes, tiles ordered by row group
+ * and then by input chunk; inside a tile, input k = 64j + 16h + e (j, h < 4,
+ * e < 16) of tile row r sits at byte 1024j + 256h + 16r + e.  The table is
+ * padded with zero codes to Vp = 16*ceil(V/16) rows and Kp = 256*ceil(K/256)
+ * inputs: bitnet_table_bytes(V, K) = Vp * Kp bytes (0 for shapes outside the
+ * limits).
  *
- * bitnet_embed_lookup: out[t,k] = fl32(q[ids[t],k] * w_scale[ids[t]]) for
- *   t < T; an id outside [0, N) gives a zero row (ids are device data and are
- *   not checked on the host).  ids int32 [T] (4-byte aligned), q int8 [N,K]
- *   and out fp32 [T,K] 16-byte aligned.  T == 0 launches nothing and returns
- *   BITNET_OK.  K >= 64, K % 64 == 0, T*K and N*K < 2^31.  Bit-exact.
+ * bitnet_table_quant: W fp32 [V,K] row-major master weights -> the table in
+ *   the storage order above (all Vp * Kp bytes written, padding 0) and
+ *   w_scale fp32 [V]: per row v, w_scale[v] = fl32(max_k |W[v,k]| / 127),
+ *   code = clamp(rint(fl32(W / w_scale[v])), -127, 127), half to even; a zero
+ *   row gives w_scale[v] = 0 and codes 0.  Bit-exact.  V >= 1, K >= 64,
+ *   K % 64 == 0, V*K and Vp*Kp < 2^31; W and table 16-byte aligned, w_scale
+ *   4-byte.  One launch, no workspace.
  *
- * bitnet_lm_head: y[m,n] = acc[m,n] * w_scale[n] / x_scale[m], rounded once to
+ * bitnet_i8_quant_weights_rows: the same per-row quantization into plain
+ *   row-major q int8 [N,K], for the per-channel I8_S layer
+ *   (bitnet_i8_linear_rows).  Same limits; N*K < 2^31.
+ *
+ * bitnet_embed_lookup: out[t,k] = fl32(code[ids[t],k] * w_scale[ids[t]]) for
+ *   t < T, from a table made by bitnet_table_quant (V rows); an id outside
+ *   [0, V) gives a zero row (ids are device data and are not checked on the
+ *   host).  ids int32 [T] (4-byte aligned), table and out fp32 [T,K] 16-byte
+ *   aligned.  T == 0 launches nothing and returns BITNET_OK.  K >= 64,
+ *   K % 64 == 0, T*K < 2^31.  Bit-exact.
+ *
+ * bitnet_lm_head: y[m,v] = acc[m,v] * w_scale[v] / x_scale[m], rounded once to
  *   fp32 (the product in fp64, exact; the division in fp64, correctly rounded),
  *   with xq, x_scale the per-row quantization of x (as bitnet_quant_act) and
- *   acc = sum_k xq[m,k] * q[n,k] in int32.  Decode only: 1 <= M <= 16 and
- *   M * (K + 16) <= 57344 (the quantized rows stay in LDS); K >= 64,
- *   K % 64 == 0, N*K and M*N*4 < 2^31.  x fp32 [M,K] and q 16-byte aligned,
- *   w_scale fp32 [N], y fp32 [M,N] 4-byte aligned.  xq_out [M,K] (16-byte
- *   aligned), x_scale_out [M] and acc_out [M,N] are optional copies for parity
- *   checks.  One launch, no workspace; an HBM stream of the N*K table bytes.
+ *   acc = sum_k xq[m,k] * code[v,k] in int32; the table as made by
+ *   bitnet_table_quant.  Decode only: 1 <= M <= 16 and M * (K + 16) <= 57344
+ *   (the quantized rows stay in LDS); K >= 64, K % 64 == 0, M*V*4 < 2^31.
+ *   x fp32 [M,K] and table 16-byte aligned, w_scale fp32 [V], y fp32 [M,V]
+ *   4-byte aligned.  xq_out [M,K] (16-byte aligned), x_scale_out [M] and
+ *   acc_out [M,V] are optional copies for parity checks.  One launch, no
+ *   workspace; an HBM stream of the table.
  * ------------------------------------------------------------------------ */
+size_t bitnet_table_bytes(int64_t V, int64_t K);
+
+bitnet_status bitnet_table_quant(const float *W, int64_t V, int64_t K, int8_t *table,
+                                 float *w_scale, void *stream);
+
 bitnet_status bitnet_i8_quant_weights_rows(const float *W, int64_t N, int64_t K, int8_t *q,
                                            float *w_scale, void *stream);
 
-bitnet_status bitnet_embed_lookup(const int32_t *ids, int64_t T, const int8_t *q,
-                                  const float *w_scale, int64_t N, int64_t K, float *out,
+bitnet_status bitnet_embed_lookup(const int32_t *ids, int64_t T, const int8_t *table,
+                                  const float *w_scale, int64_t V, int64_t K, float *out,
                                   void *stream);
 
-bitnet_status bitnet_lm_head(int64_t M, int64_t N, int64_t K, const float *x, const int8_t *q,
-                             const float *w_scale, float *y, int8_t *xq_out, float *x_scale_out,
-                             int32_t *acc_out, void *stream);
+bitnet_status bitnet_lm_head(int64_t M, int64_t V, int64_t K, const float *x,
+                             const int8_t *table, const float *w_scale, float *y, int8_t *xq_out,
+                             float *x_scale_out, int32_t *acc_out, void *stream);
 
 /* ------------------------------------------------------------------------
  * Lookup-table variant of the single-row decode, for comparison with the
@@ -361,6 +417,8 @@ bitnet_status bitnet_ternary_matmul_lut_grouped(const bitnet_problem *problems_d
  *               completes if a wait for a producer ran past its bound (200 ms
  *               of the device's wall clock; once one wait has run out the
  *               later ones return at once); the outputs are then not valid.
+ *               Word 2 (uint32) counts the calls in which that happened since
+ *               the workspace was zero-filled; the library never clears it.
  *               The call never waits without bound.
  * One one-thread kernel (advances the counter), then one cooperative launch
  * (all workgroups resident at once); no device-wide barrier: each tile waits

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libbitnet_tm.so")
 
-SOURCES = ["api.hip", "ternarize.hip", "quant.hip", "gemv.hip", "gemm.hip", "stages.hip", "lut.hip", "i8.hip", "lmhead.hip"]
+SOURCES = ["api.hip", "ternarize.hip", "quant.hip", "gemv.hip", "gemm.hip", "stages.hip", "lut.hip", "i8.hip", "lmhead.hip", "dwconv.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

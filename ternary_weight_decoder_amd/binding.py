@@ -105,6 +105,17 @@ def lib():
         L.bitnet_i8_linear_rows.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p, _sz,
                                             _p, _p]
         L.bitnet_i8_linear_rows.restype = _i32
+        L.bitnet_i8_dwconv_quant_weights.argtypes = [_p, _i64, _i64, _p, _p, _p]
+        L.bitnet_i8_dwconv_quant_weights.restype = _i32
+        L.bitnet_i8_dwconv_workspace_bytes.argtypes = [_i64, _i64, _i64]
+        L.bitnet_i8_dwconv_workspace_bytes.restype = _sz
+        L.bitnet_i8_dwconv.argtypes = [_i64, _i64, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p, _sz,
+                                       _p, _p, _p]
+        L.bitnet_i8_dwconv.restype = _i32
+        L.bitnet_table_bytes.argtypes = [_i64, _i64]
+        L.bitnet_table_bytes.restype = _sz
+        L.bitnet_table_quant.argtypes = [_p, _i64, _i64, _p, _p, _p]
+        L.bitnet_table_quant.restype = _i32
         L.bitnet_i8_quant_weights_rows.argtypes = [_p, _i64, _i64, _p, _p, _p]
         L.bitnet_i8_quant_weights_rows.restype = _i32
         L.bitnet_embed_lookup.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _p]
@@ -368,46 +379,68 @@ def bitnet_i8_quant_weights_rows(W: torch.Tensor, stream=None):
     return q, w_scale
 
 
-def bitnet_embed_lookup_into(ids, T, q, w_scale, N, K, out, stream=None) -> None:
-    _check(lib().bitnet_embed_lookup(_ptr(ids), T, _ptr(q), _ptr(w_scale), N, K, _ptr(out),
+def bitnet_table_bytes(V: int, K: int) -> int:
+    return int(lib().bitnet_table_bytes(V, K))
+
+
+def bitnet_table_quant_into(W, V, K, table, w_scale, stream=None) -> None:
+    _check(lib().bitnet_table_quant(_ptr(W), V, K, _ptr(table), _ptr(w_scale), _stream(stream)),
+           "bitnet_table_quant")
+
+
+def bitnet_table_quant(W: torch.Tensor, stream=None):
+    """fp32 W [V,K] -> (table int8 [bitnet_table_bytes(V, K)] in the library's
+    storage order, w_scale fp32 [V])."""
+    _dev(W, torch.float32, "W")
+    V, K = W.shape
+    table = torch.empty(bitnet_table_bytes(V, K), dtype=torch.int8, device=W.device)
+    w_scale = torch.empty(V, dtype=torch.float32, device=W.device)
+    bitnet_table_quant_into(W, V, K, table, w_scale, stream)
+    return table, w_scale
+
+
+def bitnet_embed_lookup_into(ids, T, table, w_scale, V, K, out, stream=None) -> None:
+    _check(lib().bitnet_embed_lookup(_ptr(ids), T, _ptr(table), _ptr(w_scale), V, K, _ptr(out),
                                      _stream(stream)),
            "bitnet_embed_lookup")
 
 
-def bitnet_embed_lookup(ids: torch.Tensor, q: torch.Tensor, w_scale: torch.Tensor, stream=None):
-    """int32 token ids [T] -> fp32 embedding rows [T, K] of the int8 table."""
+def bitnet_embed_lookup(ids: torch.Tensor, table: torch.Tensor, w_scale: torch.Tensor, K: int,
+                        stream=None):
+    """int32 token ids [T] -> fp32 embedding rows [T, K] of the table (V = w_scale.numel())."""
     _dev(ids, torch.int32, "ids")
-    _dev(q, torch.int8, "q")
-    N, K = q.shape
+    _dev(table, torch.int8, "table")
+    V = w_scale.numel()
     T = ids.numel()
-    out = torch.empty((T, K), dtype=torch.float32, device=q.device)
-    bitnet_embed_lookup_into(ids, T, q, w_scale, N, K, out, stream)
+    out = torch.empty((T, K), dtype=torch.float32, device=table.device)
+    bitnet_embed_lookup_into(ids, T, table, w_scale, V, K, out, stream)
     return out
 
 
-def bitnet_lm_head_into(M, N, K, x, q, w_scale, y, xq_out=None, x_scale_out=None, acc_out=None,
-                        stream=None) -> None:
-    _check(lib().bitnet_lm_head(M, N, K, _ptr(x), _ptr(q), _ptr(w_scale), _ptr(y), _ptr(xq_out),
-                                _ptr(x_scale_out), _ptr(acc_out), _stream(stream)),
+def bitnet_lm_head_into(M, V, K, x, table, w_scale, y, xq_out=None, x_scale_out=None,
+                        acc_out=None, stream=None) -> None:
+    _check(lib().bitnet_lm_head(M, V, K, _ptr(x), _ptr(table), _ptr(w_scale), _ptr(y),
+                                _ptr(xq_out), _ptr(x_scale_out), _ptr(acc_out), _stream(stream)),
            "bitnet_lm_head")
 
 
-def bitnet_lm_head(x: torch.Tensor, q: torch.Tensor, w_scale: torch.Tensor,
+def bitnet_lm_head(x: torch.Tensor, table: torch.Tensor, w_scale: torch.Tensor,
                    return_parts: bool = False, stream=None):
-    """lm_head over the int8 table: fp32 x [M,K] (M <= 16) -> fp32 logits [M, N]; with
-    return_parts, a dict that also holds xq, x_scale and the int32 acc."""
+    """lm_head over the table: fp32 x [M,K] (M <= 16) -> fp32 logits [M, V]
+    (V = w_scale.numel()); with return_parts, a dict that also holds xq,
+    x_scale and the int32 acc."""
     _dev(x, torch.float32, "x")
-    _dev(q, torch.int8, "q")
+    _dev(table, torch.int8, "table")
     M, K = x.shape
-    N = q.shape[0]
-    y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    V = w_scale.numel()
+    y = torch.empty((M, V), dtype=torch.float32, device=x.device)
     if not return_parts:
-        bitnet_lm_head_into(M, N, K, x, q, w_scale, y, stream=stream)
+        bitnet_lm_head_into(M, V, K, x, table, w_scale, y, stream=stream)
         return y
     xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
     xs = torch.empty(M, dtype=torch.float32, device=x.device)
-    acc = torch.empty((M, N), dtype=torch.int32, device=x.device)
-    bitnet_lm_head_into(M, N, K, x, q, w_scale, y, xq, xs, acc, stream)
+    acc = torch.empty((M, V), dtype=torch.int32, device=x.device)
+    bitnet_lm_head_into(M, V, K, x, table, w_scale, y, xq, xs, acc, stream)
     return {"y": y, "xq": xq, "x_scale": xs, "acc": acc}
 
 
@@ -433,6 +466,52 @@ def bitnet_i8_linear_rows(x: torch.Tensor, q: torch.Tensor, w_scale: torch.Tenso
     acc = torch.empty((M, N), dtype=torch.int32, device=x.device) if return_acc else None
     bitnet_i8_linear_rows_into(M, N, K, x, q, w_scale, bias, relu, y, ws, acc, stream)
     return (y, acc) if return_acc else y
+
+
+# ---- I8_S causal depthwise convolution ---------------------------------------
+
+def bitnet_i8_dwconv_quant_weights(W: torch.Tensor, stream=None):
+    """fp32 kernel W [C,k] -> (q int8 [C,k], w_scale fp32 [C]), per channel."""
+    _dev(W, torch.float32, "W")
+    C, k = W.shape
+    q = torch.empty((C, k), dtype=torch.int8, device=W.device)
+    s = torch.empty(C, dtype=torch.float32, device=W.device)
+    _check(lib().bitnet_i8_dwconv_quant_weights(_ptr(W), C, k, _ptr(q), _ptr(s), _stream(stream)),
+           "bitnet_i8_dwconv_quant_weights")
+    return q, s
+
+
+def bitnet_i8_dwconv_workspace_bytes(B: int, T: int, C: int) -> int:
+    return int(lib().bitnet_i8_dwconv_workspace_bytes(B, T, C))
+
+
+def bitnet_i8_dwconv_into(B, T, C, k, x, q, w_scale, bias, relu, y, workspace, acc_out=None,
+                          x_scale_out=None, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().bitnet_i8_dwconv(B, T, C, k, _ptr(x), _ptr(q), _ptr(w_scale), _ptr(bias),
+                                  int(bool(relu)), _ptr(y), _ptr(workspace), ws_bytes,
+                                  _ptr(acc_out), _ptr(x_scale_out), _stream(stream)),
+           "bitnet_i8_dwconv")
+
+
+def bitnet_i8_dwconv(x: torch.Tensor, q: torch.Tensor, w_scale: torch.Tensor, bias=None,
+                     relu: bool = False, return_parts: bool = False, stream=None):
+    """Causal depthwise convolution over frames: fp32 x [B,T,C], int8 q [C,k] ->
+    fp32 y [B,T,C] (with return_parts, a dict that also holds acc and x_scale)."""
+    _dev(x, torch.float32, "x")
+    _dev(q, torch.int8, "q")
+    B, T, C = x.shape
+    k = q.shape[1]
+    y = torch.empty((B, T, C), dtype=torch.float32, device=x.device)
+    ws = torch.empty(bitnet_i8_dwconv_workspace_bytes(B, T, C), dtype=torch.uint8,
+                     device=x.device)
+    if not return_parts:
+        bitnet_i8_dwconv_into(B, T, C, k, x, q, w_scale, bias, relu, y, ws, stream=stream)
+        return y
+    acc = torch.empty((B, T, C), dtype=torch.int32, device=x.device)
+    xs = torch.empty((B, C), dtype=torch.float32, device=x.device)
+    bitnet_i8_dwconv_into(B, T, C, k, x, q, w_scale, bias, relu, y, ws, acc, xs, stream)
+    return {"y": y, "acc": acc, "x_scale": xs}
 
 
 def bitnet_ternary_matmul_lut_grouped(problems_dev, count, problems_host, stream=None) -> None:
@@ -515,3 +594,7 @@ class StagedPlan:
     def timed_out(self) -> bool:
         """After the call has completed: did a wait between stages run out?"""
         return int(self.workspace[4:8].view(torch.int32).item()) != 0
+
+    def timeouts_total(self) -> int:
+        """Calls with a wait that ran out, since the workspace was zero-filled."""
+        return int(self.workspace[8:12].view(torch.int32).item())

@@ -475,7 +475,22 @@ bitnet_status bitnet_i8_quant_weights_rows(const float *W, int64_t N, int64_t K,
   if (!aligned(W, 16) || !aligned(q, 16) || !aligned(w_scale, 4)) return BITNET_ERR_ALIGN;
   bitnet_status st = device_check();
   if (st != BITNET_OK) return st;
-  return from_hip(launch_rowq_quant(W, N, K, q, w_scale, as_stream(stream)));
+  return from_hip(launch_rowq_quant(W, N, K, q, w_scale, false, as_stream(stream)));
+}
+
+size_t bitnet_table_bytes(int64_t V, int64_t K) {
+  if (!i8_shape_ok(1, V, K)) return 0;
+  return table_bytes(V, K);
+}
+
+bitnet_status bitnet_table_quant(const float *W, int64_t V, int64_t K, int8_t *table,
+                                 float *w_scale, void *stream) {
+  if (!W || !table || !w_scale) return BITNET_ERR_NULL;
+  if (!i8_shape_ok(1, V, K) || table_bytes(V, K) >= (size_t)kLimit) return BITNET_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(table, 16) || !aligned(w_scale, 4)) return BITNET_ERR_ALIGN;
+  bitnet_status st = device_check();
+  if (st != BITNET_OK) return st;
+  return from_hip(launch_rowq_quant(W, V, K, table, w_scale, true, as_stream(stream)));
 }
 
 bitnet_status bitnet_embed_lookup(const int32_t *ids, int64_t T, const int8_t *q,
@@ -483,7 +498,9 @@ bitnet_status bitnet_embed_lookup(const int32_t *ids, int64_t T, const int8_t *q
                                   void *stream) {
   if (T == 0) return BITNET_OK;
   if (!ids || !q || !w_scale || !out) return BITNET_ERR_NULL;
-  if (T < 0 || T >= kLimit || T * K >= kLimit || !i8_shape_ok(1, N, K)) return BITNET_ERR_SHAPE;
+  if (T < 0 || T >= kLimit || T * K >= kLimit || !i8_shape_ok(1, N, K) ||
+      table_bytes(N, K) >= (size_t)kLimit)
+    return BITNET_ERR_SHAPE;
   if (!aligned(ids, 4) || !aligned(q, 16) || !aligned(w_scale, 4) || !aligned(out, 16))
     return BITNET_ERR_ALIGN;
   bitnet_status st = device_check();
@@ -495,7 +512,8 @@ bitnet_status bitnet_lm_head(int64_t M, int64_t N, int64_t K, const float *x, co
                              const float *w_scale, float *y, int8_t *xq_out, float *x_scale_out,
                              int32_t *acc_out, void *stream) {
   if (!x || !q || !w_scale || !y) return BITNET_ERR_NULL;
-  if (!i8_shape_ok(M, N, K) || M > kGemvMaxM || M * (K + 16) > kLmHeadMaxRows)
+  if (!i8_shape_ok(M, N, K) || M > kGemvMaxM || M * (K + 16) > kLmHeadMaxRows ||
+      table_bytes(N, K) >= (size_t)kLimit)
     return BITNET_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(w_scale, 4) || !aligned(y, 4) ||
       (xq_out && !aligned(xq_out, 16)) || (x_scale_out && !aligned(x_scale_out, 4)) ||
@@ -505,6 +523,47 @@ bitnet_status bitnet_lm_head(int64_t M, int64_t N, int64_t K, const float *x, co
   if (st != BITNET_OK) return st;
   return from_hip(launch_lm_head((int)M, (int)N, (int)K, x, q, w_scale, y, xq_out, x_scale_out,
                                  acc_out, as_stream(stream)));
+}
+
+static bool dw_shape_ok(int64_t B, int64_t T, int64_t C, int64_t k) {
+  if (B < 1 || T < 1 || C < 64 || C % 64 != 0 || k < 1 || k > kMaxDwTaps) return false;
+  if (B > 65535 || C >= kLimit || T >= kLimit || B * T * C >= kLimit / 4) return false;
+  return true;
+}
+
+bitnet_status bitnet_i8_dwconv_quant_weights(const float *W, int64_t C, int64_t k, int8_t *q,
+                                             float *w_scale, void *stream) {
+  if (!W || !q || !w_scale) return BITNET_ERR_NULL;
+  if (!dw_shape_ok(1, 1, C, k)) return BITNET_ERR_SHAPE;
+  if (!aligned(W, 4) || !aligned(w_scale, 4)) return BITNET_ERR_ALIGN;
+  bitnet_status st = device_check();
+  if (st != BITNET_OK) return st;
+  return from_hip(launch_dw_quant_weights(W, C, k, q, w_scale, as_stream(stream)));
+}
+
+size_t bitnet_i8_dwconv_workspace_bytes(int64_t B, int64_t T, int64_t C) {
+  if (!dw_shape_ok(B, T, C, 1)) return 0;
+  return (size_t)B * dw_chunks(T) * C * sizeof(float);
+}
+
+bitnet_status bitnet_i8_dwconv(int64_t B, int64_t T, int64_t C, int64_t k, const float *x,
+                               const int8_t *q, const float *w_scale, const float *bias,
+                               int32_t relu, float *y, void *workspace, size_t workspace_bytes,
+                               int32_t *acc_out, float *x_scale_out, void *stream) {
+  if (!x || !q || !w_scale || !y) return BITNET_ERR_NULL;
+  if (!dw_shape_ok(B, T, C, k)) return BITNET_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(w_scale, 4) || !aligned(y, 16) ||
+      (bias && !aligned(bias, 4)) || (acc_out && !aligned(acc_out, 16)) ||
+      (x_scale_out && !aligned(x_scale_out, 4)))
+    return BITNET_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bitnet_i8_dwconv_workspace_bytes(B, T, C))
+    return BITNET_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return BITNET_ERR_ALIGN;
+  bitnet_status st = device_check();
+  if (st != BITNET_OK) return st;
+  return from_hip(launch_dwconv((int)B, (int)T, (int)C, (int)k, x, q, w_scale, bias,
+                                relu != 0 ? 1 : 0, y, reinterpret_cast<float *>(workspace),
+                                acc_out, x_scale_out, as_stream(stream)));
 }
 
 bitnet_status bitnet_ternary_matmul_lut_grouped(const bitnet_problem *problems_dev,

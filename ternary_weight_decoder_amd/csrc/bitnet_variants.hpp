@@ -31,12 +31,28 @@ hipError_t launch_i8_gemm(int M, int N, int K, const int8_t *xq, const float *x_
 constexpr size_t kLmHeadMaxLds = 64512;    // with the static LDS, under 64 KB
 constexpr int64_t kLmHeadMaxRows = 57344;  // quantized rows in LDS
 size_t lm_head_lds_bytes(int64_t M, int64_t V, int64_t K);
+// Bytes of the table in its storage order (16-row x 256-input tiles, padded).
+size_t table_bytes(int64_t V, int64_t K);
+// tiled: write the table's storage order (embeddings, lm_head); otherwise
+// row-major [N][K] (per-channel I8_S weights).
 hipError_t launch_rowq_quant(const float *W, int64_t N, int64_t K, int8_t *q, float *w_scale,
-                             hipStream_t stream);
+                             bool tiled, hipStream_t stream);
 hipError_t launch_embed(const int32_t *ids, int64_t T, const int8_t *q, const float *w_scale,
                         int64_t N, int64_t K, float *out, hipStream_t stream);
 hipError_t launch_lm_head(int M, int V, int K, const float *x, const int8_t *q,
                           const float *w_scale, float *y, int8_t *xq_out, float *x_scale_out,
                           int32_t *acc_out, hipStream_t stream);
+
+// dwconv.hip: I8_S causal depthwise convolution over frames, x [B][T][C],
+// C % 64 == 0, 1 <= k <= kMaxDwTaps.  partial: workspace of
+// B * dw_chunks(T) * C floats (per-chunk column maxima).
+constexpr int kMaxDwTaps = 64;
+int dw_chunks(int64_t T);
+hipError_t launch_dw_quant_weights(const float *W, int64_t C, int64_t k, int8_t *q,
+                                   float *w_scale, hipStream_t stream);
+hipError_t launch_dwconv(int B, int T, int C, int k, const float *x, const int8_t *q,
+                         const float *w_scale, const float *bias, int relu, float *y,
+                         float *partial, int32_t *acc_out, float *x_scale_out,
+                         hipStream_t stream);
 
 }  // namespace bitnet

@@ -16,19 +16,25 @@
 //     every projection of the decoder), acc = sum_k xq * q in int32 on
 //     v_mfma_i32_16x16x64_i8, y = acc * s[v] / x_scale[m] rounded once.
 //
+// Storage order.  The table is kept in 16-row x 256-input tiles of 4096
+// contiguous bytes, ordered by row group and then by input chunk; inside a
+// tile, input k = 64j + 16h + e of tile row r sits at byte 1024j + 256h + 16r
+// + e.  Rows and inputs are padded with zero codes to multiples of 16 and 256.
+//
 // lm_head work split.  The table is read once per call, so the kernel is an
-// HBM stream of V*K bytes (233 MB for the 151,936 x 1536 table).  Each wave
-// owns a contiguous run of whole 16-column blocks, the same number for every
-// wave, and walks them with a ring of items kept `D` ahead: item (b, c) is
-// block b's 256 inputs [256c, 256c + 256).  Lane (col = lane % 16, h = lane
-// / 16) loads, for step j = 0..3 of the item, the 16 bytes at input
-// 256c + 64j + 16h of table row 16b + col; one such load instruction covers 64
-// contiguous bytes of each of 16 rows.  The activation operand of MFMA j is
-// the 16 bytes at the same inputs of row col of the quantized rows in LDS, so
-// both operands of every MFMA agree on k.  Loads past V, past K or past the
-// wave's run are aimed beyond the buffer and return zeros without a memory
-// access.  The workgroup quantizes the rows into LDS itself, after issuing the
-// first D items, so the first weight loads overlap the quantization.
+// HBM stream of its bytes (233 MB for the 151,936 x 1536 table).  Each wave
+// owns a contiguous run of whole 16-column blocks (row groups), the same
+// number for every wave, and walks them with a ring of items kept `D` ahead:
+// item (b, c) is tile c of row group b.  Lane L = col + 16h loads, for step
+// j = 0..3 of the item, the 16 bytes at tile byte 1024j + 16L: table row
+// 16b + col, inputs 256c + 64j + 16h .. + 16.  One load instruction reads 1 KB
+// contiguous, and a wave's run is one contiguous stretch of the table.  The
+// activation operand of MFMA j is the 16 bytes at the same inputs of row col
+// of the quantized rows in LDS, so both operands of every MFMA agree on k;
+// padding inputs carry zero codes.  Loads past the wave's run are aimed beyond
+// the buffer and return zeros without a memory access.  The workgroup
+// quantizes the rows into LDS itself, after issuing the first D items, so the
+// first table loads overlap the quantization.
 #include <algorithm>
 
 #include "bitnet_device.hpp"
@@ -43,7 +49,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kItemK = 256;               // inputs per ring item
 constexpr int kRowPad = 16;               // bytes between quantized rows in LDS
 #ifndef BITNET_LMHEAD_DEPTH
-#define BITNET_LMHEAD_DEPTH 4
+#define BITNET_LMHEAD_DEPTH 6
 #endif
 #ifndef BITNET_LMHEAD_WAVES
 #define BITNET_LMHEAD_WAVES 2048
@@ -51,12 +57,16 @@ constexpr int kRowPad = 16;               // bytes between quantized rows in LDS
 constexpr int kDepth = BITNET_LMHEAD_DEPTH;       // items in flight per wave
 constexpr int kTargetWaves = BITNET_LMHEAD_WAVES; // waves of a launch, before balancing
 constexpr int kMaxBpw = 8;                        // blocks per wave at most
-// The table is read once per call: non-temporal loads keep it from evicting
-// the quantized rows and scales.
-constexpr int kTableAux = 2;
+constexpr int kTileBytes = 16 * kItemK;   // one 16-row x 256-input tile
+// Cache policy of the table loads, which are read once per call: non-temporal
+// (on this storage order 36.2 us per call against 41.2 us for plain loads).
+#ifndef BITNET_LMHEAD_AUX
+#define BITNET_LMHEAD_AUX 2
+#endif
+constexpr int kTableAux = BITNET_LMHEAD_AUX;
 
 struct LmShared {
-  float red[kGemvMaxM][kWaves];
+  uint32_t amax[kGemvMaxM];   // bit patterns of the rows' absmax
   float scale[kGemvMaxM];
 };
 
@@ -73,39 +83,72 @@ struct LmParams {
   int nblk;                // 16-column blocks of the table
 };
 
-// Quantize the M rows of x into LDS (natural order, row stride K + kRowPad):
-// pass 1 takes each row's absmax, pass 2 scales, rounds and stores.
+// Quantize the M rows of x into LDS (natural order, row stride K + kRowPad).
+// The rows are one flat run of M*K/4 fp32 quads; each thread takes every
+// kThreads-th quad, kQuantBatch loads at a time, so a pass costs a few memory
+// round trips however many rows there are.  Pass 1 takes each row's absmax
+// (non-negative floats order like their bit patterns: an integer max in LDS,
+// one per wave when the wave's quads lie in one row); pass 2 scales, rounds
+// and stores.
+constexpr int kQuantBatch = 8;
+
 __device__ __forceinline__ void lm_quant_rows(const LmParams &p, LmShared &sh, int8_t *xq,
                                               bool write_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n4 = p.K >> 2;
+  const int total = p.M * n4;
   const int stride = p.K + kRowPad;
-  for (int m = 0; m < p.M; ++m) {
-    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(p.x + (size_t)m * p.K);
-    float a = 0.0f;
-    for (int i = tid; i < n4; i += kThreads) {
-      const f32x4 v = ld_global<f32x4>(x4 + i);
-      a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  const f32x4 *x4 = reinterpret_cast<const f32x4 *>(p.x);
+  if (tid < p.M) sh.amax[tid] = 0u;
+  __syncthreads();
+  for (int e0 = 0; e0 < total; e0 += kQuantBatch * kThreads) {
+    f32x4 v[kQuantBatch];
+#pragma unroll
+    for (int u = 0; u < kQuantBatch; ++u) {
+      const int e = e0 + u * kThreads + tid;
+      v[u] = e < total ? ld_global<f32x4>(x4 + e) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    a = wave_max(a);
-    if (lane == 0) sh.red[m][wave] = a;
+#pragma unroll
+    for (int u = 0; u < kQuantBatch; ++u) {
+      const int w0 = e0 + u * kThreads + 64 * wave;   // first quad of this wave
+      if (w0 >= total) break;
+      const int e = w0 + lane;
+      float a = fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w)));
+      const int m0 = w0 / n4, m1 = min(w0 + 63, total - 1) / n4;
+      if (m0 == m1) {
+        a = wave_max(a);
+        if (lane == 0) atomicMax(&sh.amax[m0], __builtin_bit_cast(uint32_t, a));
+      } else if (e < total) {
+        atomicMax(&sh.amax[e / n4], __builtin_bit_cast(uint32_t, a));
+      }
+    }
   }
   __syncthreads();
-  for (int m = 0; m < p.M; ++m) {
-    const float a = fmaxf(fmaxf(sh.red[m][0], sh.red[m][1]), fmaxf(sh.red[m][2], sh.red[m][3]));
+  if (tid < p.M) {
+    const float a = __builtin_bit_cast(float, sh.amax[tid]);
     const float s = (a == 0.0f) ? 1.0f : 127.0f / a;
-    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(p.x + (size_t)m * p.K);
-    int8_t *dst = xq + (size_t)m * stride;
-    for (int i = tid; i < n4; i += kThreads) {
-      const f32x4 v = ld_global<f32x4>(x4 + i);
-      const uint32_t w = pack4_i8(quant_one(v.x, s), quant_one(v.y, s), quant_one(v.z, s),
-                                  quant_one(v.w, s));
-      *reinterpret_cast<uint32_t *>(dst + 4 * i) = w;
-      if (write_out) st_global<uint32_t>(p.xq_out + (size_t)m * p.K + 4 * i, w);
+    sh.scale[tid] = s;
+    if (write_out) st_global<float>(p.x_scale_out + tid, s);
+  }
+  __syncthreads();
+  for (int e0 = 0; e0 < total; e0 += kQuantBatch * kThreads) {
+    f32x4 v[kQuantBatch];
+#pragma unroll
+    for (int u = 0; u < kQuantBatch; ++u) {
+      const int e = e0 + u * kThreads + tid;
+      v[u] = e < total ? ld_global<f32x4>(x4 + e) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    if (tid == 0) {
-      sh.scale[m] = s;
-      if (write_out) st_global<float>(p.x_scale_out + m, s);
+#pragma unroll
+    for (int u = 0; u < kQuantBatch; ++u) {
+      const int e = e0 + u * kThreads + tid;
+      if (e < total) {
+        const int m = e / n4, i = e - m * n4;
+        const float s = sh.scale[m];
+        const uint32_t w = pack4_i8(quant_one(v[u].x, s), quant_one(v[u].y, s),
+                                    quant_one(v[u].z, s), quant_one(v[u].w, s));
+        *reinterpret_cast<uint32_t *>(xq + (size_t)m * stride + 4 * i) = w;
+        if (write_out) st_global<uint32_t>(p.xq_out + 4 * (size_t)e, w);
+      }
     }
   }
   __syncthreads();
@@ -130,7 +173,9 @@ __global__ void __launch_bounds__(kThreads) lm_head_kernel(LmParams p) {
   __shared__ LmShared sh;
   extern __shared__ __attribute__((aligned(16))) int8_t lds[];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // The wave index is uniform: said so, the run's bounds and the ring's item
+  // count live in scalar registers and the load addressing stays branch-free.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;
   const int h = lane >> 4;
   const int bpw = p.blocks_per_wave;
@@ -145,25 +190,22 @@ __global__ void __launch_bounds__(kThreads) lm_head_kernel(LmParams p) {
   float *scale_lds = wave_lds;                                           // [kMaxBpw * 16]
   int *acc_lds = reinterpret_cast<int *>(wave_lds + kMaxBpw * 16);       // [bpw][M][16]
 
-  const uint32_t q_bytes = (uint32_t)((size_t)p.V * p.K);
+  const uint32_t q_bytes = (uint32_t)((size_t)p.nblk * cpb * kTileBytes);
   const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(p.q, q_bytes);
-  // Next item to fetch: block fb of the wave's run, chunk fc of that block.
-  int fb = 0, fc = 0, fetched = 0;
+  // Next item to fetch: the wave's run is items [blk0 * cpb, (blk0 + nb) * cpb)
+  // of the table, one 4 KB tile each.
+  int fetched = 0;
+  const uint32_t run0 = (uint32_t)blk0 * cpb * kTileBytes + 16u * lane;
   auto load_item = [&](v4i (&w)[4]) {
-    const int n = (blk0 + fb) * 16 + col;
-    const bool live = fetched < items && n < p.V;
+    const bool live = fetched < items;
+    const uint32_t base = run0 + (uint32_t)fetched * kTileBytes;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int k = fc * kItemK + 64 * j + 16 * h;
-      const uint32_t off = (live && k < p.K) ? (uint32_t)n * (uint32_t)p.K + (uint32_t)k : q_bytes;
+      const uint32_t off = live ? base + 1024u * j : q_bytes;
       w[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, off, 0,
                                                                             kTableAux));
     }
     ++fetched;
-    if (++fc == cpb) {
-      fc = 0;
-      ++fb;
-    }
   };
   v4i wr[D][4];
 #pragma unroll
@@ -230,25 +272,40 @@ __global__ void __launch_bounds__(kThreads) lm_head_kernel(LmParams p) {
   }
 }
 
-// Per-row quantization, one wave per row.
+// Byte of code (v, k) in the table's storage order; cpb = 256-input chunks
+// per row group.
+__device__ __forceinline__ uint32_t table_off(int v, int k, int cpb) {
+  return (uint32_t)(((v >> 4) * cpb + (k >> 8)) * kTileBytes) + ((k & 255) >> 6) * 1024u +
+         ((k & 63) >> 4) * 256u + (v & 15) * 16u + (k & 15);
+}
+
+// Per-row quantization, one wave per row.  TILED: write the table's storage
+// order over the padded Vp x Kp table (padding rows and inputs get zero codes);
+// otherwise plain row-major [N][K].
+template <bool TILED>
 __global__ void __launch_bounds__(kThreads) rowq_quant_kernel(const float *W, int N, int K,
-                                                              int8_t *q, float *w_scale) {
+                                                              int rows, int8_t *q,
+                                                              float *w_scale) {
   const int lane = threadIdx.x & 63;
   const int n = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (n >= N) return;
+  if (n >= rows) return;
   const int n4 = K >> 2;
-  const f32x4 *w4 = reinterpret_cast<const f32x4 *>(W + (size_t)n * K);
+  const int cpb = (K + kItemK - 1) / kItemK;
+  const bool live = n < N;
+  const f32x4 *w4 = reinterpret_cast<const f32x4 *>(W + (size_t)(live ? n : 0) * K);
   float a = 0.0f;
-  for (int i = lane; i < n4; i += 64) {
-    const f32x4 v = ld_global<f32x4>(w4 + i);
-    a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-  }
+  if (live)
+    for (int i = lane; i < n4; i += 64) {
+      const f32x4 v = ld_global<f32x4>(w4 + i);
+      a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
   a = wave_max(a);
   const float s = a / 127.0f;
-  if (lane == 0) st_global<float>(w_scale + n, a == 0.0f ? 0.0f : s);
-  for (int i = lane; i < n4; i += 64) {
+  if (live && lane == 0) st_global<float>(w_scale + n, a == 0.0f ? 0.0f : s);
+  const int nout4 = TILED ? cpb * (kItemK / 4) : n4;
+  for (int i = lane; i < nout4; i += 64) {
     uint32_t packed = 0;
-    if (a != 0.0f) {
+    if (live && a != 0.0f && i < n4) {
       const f32x4 v = ld_global<f32x4>(w4 + i);
       int c[4] = {0, 0, 0, 0};
       const float e[4] = {v.x, v.y, v.z, v.w};
@@ -259,11 +316,15 @@ __global__ void __launch_bounds__(kThreads) rowq_quant_kernel(const float *W, in
       }
       packed = pack4_i8(c[0], c[1], c[2], c[3]);
     }
-    st_global<uint32_t>(q + (size_t)n * K + 4 * i, packed);
+    if (TILED)
+      st_global<uint32_t>(q + table_off(n, 4 * i, cpb), packed);
+    else
+      st_global<uint32_t>(q + (size_t)n * K + 4 * i, packed);
   }
 }
 
-// Embedding rows, one wave per token.
+// Embedding rows from the table, one wave per token; lane g takes inputs
+// [16g, 16g + 16) (one 16-byte group of the storage order).
 __global__ void __launch_bounds__(kThreads) embed_kernel(const int32_t *ids, int T,
                                                          const int8_t *q, const float *w_scale,
                                                          int N, int K, float *out) {
@@ -273,17 +334,21 @@ __global__ void __launch_bounds__(kThreads) embed_kernel(const int32_t *ids, int
   const int id = ld_global<int>(ids + t);
   const bool live = id >= 0 && id < N;
   const float s = live ? ld_global<float>(w_scale + id) : 0.0f;
-  const int n4 = K >> 2;
-  for (int i = lane; i < n4; i += 64) {
-    f32x4 v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (live) {
-      const uint32_t d = ld_global<uint32_t>(q + (size_t)id * K + 4 * i);
-      v.x = (float)(int8_t)(d & 0xff) * s;
-      v.y = (float)(int8_t)((d >> 8) & 0xff) * s;
-      v.z = (float)(int8_t)((d >> 16) & 0xff) * s;
-      v.w = (float)(int8_t)(d >> 24) * s;
+  const int cpb = (K + kItemK - 1) / kItemK;
+  for (int g = lane; g < (K >> 4); g += 64) {
+    v4i d = v4i{0, 0, 0, 0};
+    if (live) d = ld_global<v4i>(q + table_off(id, 16 * g, cpb));
+    float *o = out + (size_t)t * K + 16 * g;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t b = (uint32_t)d[w];
+      f32x4 v;
+      v.x = (float)(int8_t)(b & 0xff) * s;
+      v.y = (float)(int8_t)((b >> 8) & 0xff) * s;
+      v.z = (float)(int8_t)((b >> 16) & 0xff) * s;
+      v.w = (float)(int8_t)(b >> 24) * s;
+      st_global<f32x4>(o + 4 * w, v);
     }
-    st_global<f32x4>(out + (size_t)t * K + 4 * i, v);
   }
 }
 
@@ -306,10 +371,20 @@ size_t lm_head_lds_bytes(int64_t M, int64_t V, int64_t K) {
   return lm_rows_bytes((int)M, (int)K) + kWaves * lm_wave_bytes((int)M, lm_bpw(M, V, K));
 }
 
+size_t table_bytes(int64_t V, int64_t K) {
+  return (size_t)((V + 15) / 16 * 16) * (size_t)((K + kItemK - 1) / kItemK * kItemK);
+}
+
 hipError_t launch_rowq_quant(const float *W, int64_t N, int64_t K, int8_t *q, float *w_scale,
-                             hipStream_t stream) {
-  const int64_t blocks = (N + kWaves - 1) / kWaves;
-  rowq_quant_kernel<<<(unsigned)blocks, kThreads, 0, stream>>>(W, (int)N, (int)K, q, w_scale);
+                             bool tiled, hipStream_t stream) {
+  const int64_t rows = tiled ? (N + 15) / 16 * 16 : N;
+  const int64_t blocks = (rows + kWaves - 1) / kWaves;
+  if (tiled)
+    rowq_quant_kernel<true><<<(unsigned)blocks, kThreads, 0, stream>>>(W, (int)N, (int)K,
+                                                                       (int)rows, q, w_scale);
+  else
+    rowq_quant_kernel<false><<<(unsigned)blocks, kThreads, 0, stream>>>(W, (int)N, (int)K,
+                                                                        (int)rows, q, w_scale);
   return hipGetLastError();
 }
 

@@ -67,7 +67,7 @@ struct StageIo {
   const uint64_t *x_tagged;   // producer's (value, epoch) pairs, or null: read x
   uint64_t *y_tagged;         // this problem's pairs, or null: no later reader
   uint32_t epoch;
-  uint32_t *flags;            // workspace words: [0] epoch, [1] timeout flag
+  uint32_t *flags;            // workspace words: [0] epoch, [1] timeout flag, [2] timeout count
   uint64_t timeout;           // wall-clock ticks per wait
 };
 
@@ -110,6 +110,13 @@ __device__ __forceinline__ bool pair_ok(uint64_t q, uint32_t epoch) {
 // Read vector e (4 activations) of every thread's share of the M x K block
 // into v[]: directly from x, or from the producer's tagged pairs (one 64-bit
 // atomic load per pair), waiting until every pair carries the current epoch.
+// A wait ran past its bound: raise this call's flag (word 1) and, the first
+// time in the call, count the call in word 2, which nothing clears (so the
+// count covers every call since the workspace was zero-filled).
+__device__ __forceinline__ void note_timeout(uint32_t *flags) {
+  if (atomicOr(&flags[1], 1u) == 0u) atomicAdd(&flags[2], 1u);
+}
+
 __device__ __forceinline__ void stage_load_x(const float *x, const StageIo &io, int total,
                                              f32x4 (&v)[kStageXVec]) {
   const int tid = threadIdx.x;
@@ -130,7 +137,7 @@ __device__ __forceinline__ void stage_load_x(const float *x, const StageIo &io, 
   // Probe: poll the first pair (written by the producer's first tile) first.
   while (!expired && !pair_ok(ld_pair(xt, 0u), io.epoch)) {
     if (wall_clock64() - t0 > io.timeout) {
-      atomicOr(&io.flags[1], 1u);
+      note_timeout(io.flags);
       expired = true;
     }
     __builtin_amdgcn_s_sleep(2);
@@ -167,7 +174,7 @@ __device__ __forceinline__ void stage_load_x(const float *x, const StageIo &io, 
       }
     }
     if (pending != 0 && wall_clock64() - t0 > io.timeout) {
-      atomicOr(&io.flags[1], 1u);
+      note_timeout(io.flags);
       expired = true;
     }
   }

@@ -22,6 +22,7 @@ directly in float32; Student-t draws are made in float64 and cast.
 from __future__ import annotations
 
 import math
+import multiprocessing
 from dataclasses import dataclass
 
 import numpy as np
@@ -199,3 +200,40 @@ def table_weights(V: int = VOCAB, K: int = HIDDEN, seed: int = TABLE_SEED) -> np
 def token_ids(T: int, V: int = VOCAB, seed: int = TABLE_SEED + 1) -> np.ndarray:
     """T token ids drawn uniformly from [0, V), int32."""
     return np.random.default_rng(seed).integers(0, V, size=T, dtype=np.int64).astype(np.int32)
+
+
+# ---- generation in worker processes -------------------------------------------
+# The workloads' arrays are drawn with numpy on the host, one seeded stream per
+# matrix; drawing the 196 Student-t masters of the long-form workload takes
+# over a minute on one core, so the benchmark spreads the matrices over worker
+# processes (spawned, so that they never touch the GPU).  Results arrive in
+# the order of the problems, identical to drawing them one by one.
+
+def _weights_job(args):
+    N, K, seed, heavy = args
+    return student_t_weights(N, K, seed) if heavy else normal_weights(N, K, seed)
+
+
+def _activations_job(args):
+    M, K, seed = args
+    return activations(M, K, seed)
+
+
+def _parallel(job, jobs, workers):
+    if workers <= 1:
+        yield from map(job, jobs)
+        return
+    ctx = multiprocessing.get_context("spawn")
+    with ctx.Pool(workers) as pool:
+        yield from pool.imap(job, jobs, chunksize=1)
+
+
+def problem_weights_iter(problems, heavy_tail: bool = False, workers: int = 1):
+    """problem_weights(p, heavy_tail) for each problem, in order."""
+    yield from _parallel(_weights_job, [(p.N, p.K, p.w_seed, heavy_tail) for p in problems],
+                         workers)
+
+
+def problem_activations_iter(problems, M: int, workers: int = 1):
+    """problem_activations(p, M) for each problem, in order."""
+    yield from _parallel(_activations_job, [(M, p.K, p.x_seed) for p in problems], workers)

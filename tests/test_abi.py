@@ -225,6 +225,18 @@ def test_table_entry_points_validation(L):
     L.bitnet_embed_lookup.restype = i32
     L.bitnet_lm_head.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, p]
     L.bitnet_lm_head.restype = i32
+    L.bitnet_table_bytes.argtypes = [i64, i64]
+    L.bitnet_table_bytes.restype = ctypes.c_size_t
+    L.bitnet_table_quant.argtypes = [p, i64, i64, p, p, p]
+    L.bitnet_table_quant.restype = i32
+    assert L.bitnet_table_bytes(151936, 1536) == 151936 * 1536
+    assert L.bitnet_table_bytes(40, 1536) == 48 * 1536
+    assert L.bitnet_table_bytes(17, 320) == 32 * 512
+    assert L.bitnet_table_bytes(8, 100) == 0
+    tq = L.bitnet_table_quant
+    assert tq(NULL, 8, 64, A, A, NULL) == ERR["NULL"]
+    assert tq(A, 8, 96, A, A, NULL) == ERR["SHAPE"]
+    assert tq(A, 8, 64, A, A + 2, NULL) == ERR["ALIGN"]
     rq = L.bitnet_i8_quant_weights_rows
     assert rq(NULL, 8, 64, A, A, NULL) == ERR["NULL"]
     assert rq(A, 8, 96, A, A, NULL) == ERR["SHAPE"]
@@ -262,3 +274,22 @@ def test_noalloc_validation(L):
     assert L.bitnet_matmul_workspace_bytes(1800, 18688) > L.bitnet_scratch_bytes()
     assert L.bitnet_matmul_workspace_bytes(1800, 18560) <= L.bitnet_scratch_bytes()
     assert f(1800, 64, 18688, A, A, A, A, NULL, NULL, NULL, NULL) == 8
+
+
+def test_dwconv_validation(L):
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    L.bitnet_i8_dwconv_workspace_bytes.argtypes = [i64, i64, i64]
+    L.bitnet_i8_dwconv_workspace_bytes.restype = sz
+    L.bitnet_i8_dwconv.argtypes = [i64, i64, i64, i64, p, p, p, p, i32, p, p, sz, p, p, p]
+    L.bitnet_i8_dwconv.restype = i32
+    wsb = L.bitnet_i8_dwconv_workspace_bytes
+    assert wsb(1, 8192, 512) == 64 * 512 * 4 and wsb(2, 129, 64) == 2 * 2 * 64 * 4
+    assert wsb(1, 10, 100) == 0
+    f = L.bitnet_i8_dwconv
+    ws = wsb(1, 100, 64)
+    assert f(1, 100, 64, 7, NULL, A, A, NULL, 0, A, A, ws, NULL, NULL, NULL) == ERR["NULL"]
+    assert f(1, 100, 96, 7, A, A, A, NULL, 0, A, A, ws, NULL, NULL, NULL) == ERR["SHAPE"]
+    assert f(1, 100, 64, 65, A, A, A, NULL, 0, A, A, ws, NULL, NULL, NULL) == ERR["SHAPE"]
+    assert f(1, 100, 64, 0, A, A, A, NULL, 0, A, A, ws, NULL, NULL, NULL) == ERR["SHAPE"]
+    assert f(1, 100, 64, 7, A + 4, A, A, NULL, 0, A, A, ws, NULL, NULL, NULL) == ERR["ALIGN"]
+    assert f(1, 100, 64, 7, A, A, A, NULL, 0, A, A, ws - 4, NULL, NULL, NULL) == ERR["WORKSPACE"]

@@ -1,8 +1,10 @@
 """GPU parity of the decoder's 8-bit per-row table (embeddings and lm_head)
 against the oracle, through the C ABI.
 
-Table codes and scales, embedding rows, int8 activations, int32 accumulators
-and the lm_head outputs (exactly rounded fp64 epilogue) are all bit-exact.
+Table bytes (the oracle's own packing of its codes into the storage order,
+zero padding included) and scales, embedding rows, int8 activations, int32
+accumulators and the lm_head outputs (exactly rounded fp64 epilogue) are all
+bit-exact.
 Shapes cover ragged V around the 16-column block, K of one MFMA step (64),
 ragged 256-input items, every M from 1 to 16, the LDS limit, zero rows on
 both sides, out-of-range token ids, and the full 151,936 x 1536 table.
@@ -53,25 +55,27 @@ def canary_ok(buf, n):
 
 
 def gpu_table(tb, W):
+    """The table in its storage order and the row scales, made on the GPU."""
     import torch
-    N, K = W.shape
-    qb, q = guarded(N * K, torch.int8, 77)
-    sb, s = guarded(N, torch.float32, float("nan"))
-    tb.bitnet_i8_quant_weights_rows_into(dev(W), N, K, q, s)
+    V, K = W.shape
+    nb = tb.bitnet_table_bytes(V, K)
+    qb, q = guarded(nb, torch.int8, 77)
+    sb, s = guarded(V, torch.float32, float("nan"))
+    tb.bitnet_table_quant_into(dev(W), V, K, q, s)
     torch.cuda.synchronize()
-    assert canary_ok(qb, N * K) and canary_ok(sb, N)
-    return q.view(N, K), s
+    assert canary_ok(qb, nb) and canary_ok(sb, V)
+    return q, s
 
 
-def run_lm_head(tb, x, q_dev, s_dev):
+def run_lm_head(tb, x, t_dev, s_dev):
     import torch
     M, K = x.shape
-    N = q_dev.shape[0]
+    N = s_dev.numel()
     yb, y = guarded(M * N, torch.float32, float("nan"))
     ab, acc = guarded(M * N, torch.int32, -7)
     xq = torch.empty((M, K), dtype=torch.int8, device="cuda:0")
     xs = torch.empty(M, dtype=torch.float32, device="cuda:0")
-    tb.bitnet_lm_head_into(M, N, K, dev(x), q_dev, s_dev, y, xq, xs, acc)
+    tb.bitnet_lm_head_into(M, N, K, dev(x), t_dev, s_dev, y, xq, xs, acc)
     torch.cuda.synchronize()
     assert canary_ok(yb, M * N), "y canary overwritten"
     assert canary_ok(ab, M * N), "acc canary overwritten"
@@ -79,7 +83,8 @@ def run_lm_head(tb, x, q_dev, s_dev):
             xs.cpu().numpy())
 
 
-@pytest.mark.parametrize("N,K", [(1, 64), (200, 192), (37, 1536), (1000, 4096), (16, 8960)])
+@pytest.mark.parametrize("N,K", [(1, 64), (200, 192), (37, 1536), (1000, 4096), (16, 8960),
+                                 (21, 320)])
 def test_table_quant_bit_exact(tb, N, K):
     say(f"[table quant] N={N} K={K}")
     W = synth.student_t_weights(N, K, 900 + N + K)
@@ -87,7 +92,19 @@ def test_table_quant_bit_exact(tb, N, K):
         W[3] = 0.0                       # zero row: scale 0, codes 0
         W[4, -1] = np.float32(-1.0)      # the row maximum at the last entry
     q_ref, s_ref = oracle.rowq_quant_weights(W)
-    q, s = gpu_table(tb, W)
+    t, s = gpu_table(tb, W)
+    assert t.cpu().numpy().tobytes() == oracle.table_pack(q_ref).tobytes()
+    assert s.cpu().numpy().tobytes() == s_ref.tobytes()
+
+
+@pytest.mark.parametrize("N,K", [(3, 64), (200, 192)])
+def test_row_major_quant_bit_exact(tb, N, K):
+    # the per-channel I8_S weights: the same codes, plain row-major
+    import torch
+    W = synth.normal_weights(N, K, 950 + N)
+    q_ref, s_ref = oracle.rowq_quant_weights(W)
+    q, s = tb.bitnet_i8_quant_weights_rows(torch.from_numpy(W).to("cuda:0"))
+    torch.cuda.synchronize()
     np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
     assert s.cpu().numpy().tobytes() == s_ref.tobytes()
 
@@ -100,7 +117,8 @@ def test_worked_example(tb):
     W = np.zeros((4, 64), np.float32)
     W[:, :4] = np.array([[float.fromhex(v) for v in r[1:]] for r in g["w_hex"]], np.float32)
     q, s = gpu_table(tb, W)
-    qh = q.cpu().numpy()
+    qh, bad = oracle.table_unpack(q.cpu().numpy(), 4, 64)
+    assert bad == 0
     np.testing.assert_array_equal(qh[:, :4], np.array([r[1:] for r in g["q"]], np.int8))
     assert not qh[:, 4:].any()
     want_s = np.array([int(h, 16) for h in g["scale_bits"][0]], np.uint32).view(np.float32)
@@ -141,7 +159,7 @@ def test_lm_head_shapes(tb, M, N, K):
     x = synth.activations(M, K, 921 + K)
     q_ref, s_ref = oracle.rowq_quant_weights(W)
     ref = oracle.rowq_linear(x, q_ref, s_ref)
-    y, acc, xq, xs = run_lm_head(tb, x, dev(q_ref), dev(s_ref))
+    y, acc, xq, xs = run_lm_head(tb, x, dev(oracle.table_pack(q_ref)), dev(s_ref))
     np.testing.assert_array_equal(xq, ref["xq"])
     np.testing.assert_array_equal(acc, ref["acc"])
     assert y.tobytes() == ref["y"].tobytes()
@@ -158,7 +176,7 @@ def test_lm_head_worst_case_magnitude(tb):
     q_ref, s_ref = oracle.rowq_quant_weights(W)
     ref = oracle.rowq_linear(x, q_ref, s_ref)
     assert abs(int(ref["acc"][0, 0])) == 127 * 127 * K
-    y, acc, _, _ = run_lm_head(tb, x, dev(q_ref), dev(s_ref))
+    y, acc, _, _ = run_lm_head(tb, x, dev(oracle.table_pack(q_ref)), dev(s_ref))
     np.testing.assert_array_equal(acc, ref["acc"])
     assert y.tobytes() == ref["y"].tobytes()
 
@@ -169,7 +187,7 @@ def test_lm_head_repeat_and_sensitivity(tb):
     W = synth.normal_weights(N, K, 930)
     x = synth.activations(M, K, 931)
     q_ref, s_ref = oracle.rowq_quant_weights(W)
-    qd, sd = dev(q_ref), dev(s_ref)
+    qd, sd = dev(oracle.table_pack(q_ref)), dev(s_ref)
     y1, _, _, _ = run_lm_head(tb, x, qd, sd)
     y2, _, _, _ = run_lm_head(tb, x, qd, sd)
     assert y1.tobytes() == y2.tobytes()
@@ -190,12 +208,13 @@ def test_embed_lookup(tb):
     ref = oracle.rowq_embed(ids, q_ref, s_ref)
     T = ids.size
     ob, out = guarded(T * K, torch.float32, float("nan"))
-    tb.bitnet_embed_lookup_into(dev(ids), T, dev(q_ref), dev(s_ref), N, K, out)
+    table = dev(oracle.table_pack(q_ref))
+    tb.bitnet_embed_lookup_into(dev(ids), T, table, dev(s_ref), N, K, out)
     torch.cuda.synchronize()
     assert canary_ok(ob, T * K)
     assert out.view(T, K).cpu().numpy().tobytes() == ref.tobytes()
     # no tokens: nothing launched, nothing written
-    tb.bitnet_embed_lookup_into(dev(ids[:1]), 0, dev(q_ref), dev(s_ref), N, K, ob[T * K:])
+    tb.bitnet_embed_lookup_into(dev(ids[:1]), 0, table, dev(s_ref), N, K, ob[T * K:])
     torch.cuda.synchronize()
     assert canary_ok(ob, T * K)
 
@@ -210,12 +229,12 @@ def test_full_table(tb):
     W = synth.table_weights()
     q_ref, s_ref = oracle.rowq_quant_weights(W)
     Wd = dev(W)
-    q = torch.empty((V, K), dtype=torch.int8, device="cuda:0")
+    q = torch.empty(tb.bitnet_table_bytes(V, K), dtype=torch.int8, device="cuda:0")
     s = torch.empty(V, dtype=torch.float32, device="cuda:0")
-    tb.bitnet_i8_quant_weights_rows_into(Wd, V, K, q, s)
+    tb.bitnet_table_quant_into(Wd, V, K, q, s)
     torch.cuda.synchronize()
     del Wd
-    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(q.cpu().numpy(), oracle.table_pack(q_ref))
     assert s.cpu().numpy().tobytes() == s_ref.tobytes()
     x1 = synth.activations(1, K, synth.TABLE_SEED + 2)
     ref = oracle.rowq_linear(x1, q_ref, s_ref)
@@ -233,6 +252,6 @@ def test_full_table(tb):
     np.testing.assert_array_equal(acc[ms, ns], acc_s)
     assert y[ms, ns].tobytes() == y_s.tobytes()
     ids = synth.token_ids(64)
-    out = tb.bitnet_embed_lookup(dev(ids), q, s)
+    out = tb.bitnet_embed_lookup(dev(ids), q, s, K)
     torch.cuda.synchronize()
     assert out.cpu().numpy().tobytes() == oracle.rowq_embed(ids, q_ref, s_ref).tobytes()

@@ -85,7 +85,7 @@ def test_stages_chain_bit_exact(tb, layers):
     plan = tb.StagedPlan(1, stages)
     plan.run()
     torch.cuda.synchronize()
-    assert not plan.timed_out()
+    assert not plan.timed_out() and plan.timeouts_total() == 0
     ref = oracle_chain(problems, packs, h0, layers)
     for l in range(layers):
         for j in range(7):
@@ -97,7 +97,7 @@ def test_stages_chain_bit_exact(tb, layers):
     first = [bufs[l][j].clone() for l in range(layers) for j in range(7)]
     plan.run()
     torch.cuda.synchronize()
-    assert not plan.timed_out()
+    assert not plan.timed_out() and plan.timeouts_total() == 0
     again = [bufs[l][j] for l in range(layers) for j in range(7)]
     assert all(torch.equal(a, b) for a, b in zip(first, again))
 
@@ -120,7 +120,7 @@ def test_stages_single_stage_matches_grouped(tb):
     g = tb.GroupedPlan(1, xs, dp, ds, y2, [p.N for p in problems], [p.K for p in problems])
     g.run()
     torch.cuda.synchronize()
-    assert not plan.timed_out()
+    assert not plan.timed_out() and plan.timeouts_total() == 0
     for a, b in zip(y1, y2):
         assert torch.equal(a, b)
 
@@ -150,7 +150,7 @@ def test_stages_general_shapes_bit_exact(tb, M):
     plan = tb.StagedPlan(M, stages)
     plan.run()
     torch.cuda.synchronize()
-    assert not plan.timed_out()
+    assert not plan.timed_out() and plan.timeouts_total() == 0
     ref = {}
     for st in order:
         for n in st:

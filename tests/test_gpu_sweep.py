@@ -1,11 +1,16 @@
 """GPU parity at full size: all 196 projections of the 28-layer decoder, in the
 grouped launches the benchmark times, checked on sampled outputs.
 
-The weights are drawn once (seeded, on the host).  Every matrix is ternarized
-and packed twice, by the oracle and by the library, and the two packings must
-be bit-identical with identical scales.  The expected outputs use only the
-oracle's packing and the oracle's quantization of the sampled rows.
+Two weight sets, each drawn once (seeded, on the host): the decode sweep's
+0.02 N(0,1) masters (also prefill at M=256), and the long-form set of
+Student-t(3) masters scaled to std 0.01 (prefill at M=1800, batched decode at
+M=32 and 64).  Every matrix is ternarized and packed twice, by the oracle and
+by the library, and the two packings must be bit-identical with identical
+scales.  Activations are drawn on the host from each workload's own seeds.
+The expected outputs use only the oracle's packing and the oracle's
+quantization of the sampled rows.
 """
+import os
 import sys
 
 import numpy as np
@@ -26,20 +31,16 @@ def say(msg):
     sys.stdout.flush()
 
 
-@pytest.fixture(scope="module")
-def sweep():
+def _ternarized_set(problems, heavy_tail, what):
     import torch
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
     from ternary_weight_decoder_amd import binding as tb
     tb.lib()
-    problems = synth.sweep_problems()
-    say(f"[sweep] ternarizing {len(problems)} matrices on the host and on the GPU")
+    say(f"[{what}] ternarizing {len(problems)} matrices on the host and on the GPU")
     ws = torch.empty(tb.bitnet_ternarize_workspace_bytes(synth.INTERMEDIATE), dtype=torch.uint8,
                      device="cuda:0")
+    workers = max(1, min(16, os.cpu_count() or 1))
     packs, packed_dev, scales_dev = [], [], []
-    for p in problems:
-        W = synth.problem_weights(p)
+    for p, W in zip(problems, synth.problem_weights_iter(problems, heavy_tail, workers)):
         ref_packed, ref_scale = oracle.ternarize_pack(W)
         pk = torch.empty(p.N * p.K // 4, dtype=torch.uint8, device="cuda:0")
         sc = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda:0")
@@ -54,6 +55,22 @@ def sweep():
             "scales": scales_dev}
 
 
+@pytest.fixture(scope="module")
+def sweep():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return _ternarized_set(synth.sweep_problems(), False, "sweep")
+
+
+@pytest.fixture(scope="module")
+def longform():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return _ternarized_set(synth.longform_problems(), True, "long-form")
+
+
 def gpu_activations(M, K, seed):
     """N(0,1) rows with 1% of the channels x20, drawn on the GPU (seeded)."""
     import torch
@@ -65,13 +82,18 @@ def gpu_activations(M, K, seed):
     return x
 
 
-def run_and_check(sweep, M, subset, host_x, lut=False):
+def run_and_check(sweep, M, subset, host_x, lut=False, x_problems=None):
+    """x_problems: problems whose activation seeds to use (same order as the
+    set's), default the set's own."""
     import torch
     tb = sweep["tb"]
     idx = [i for i, p in enumerate(sweep["problems"]) if subset(p)]
     probs = [sweep["problems"][i] for i in idx]
     if host_x:
-        xs = [torch.from_numpy(synth.problem_activations(p, M)).to("cuda:0") for p in probs]
+        xp = [(x_problems or sweep["problems"])[i] for i in idx]
+        workers = max(1, min(16, os.cpu_count() or 1))
+        xs = [torch.from_numpy(x).to("cuda:0")
+              for x in synth.problem_activations_iter(xp, M, workers)]
     else:
         xs = [gpu_activations(M, p.K, 70000 + 7 * p.layer + p.proj) for p in probs]
     ys = [torch.full((M, p.N), float("nan"), device="cuda:0") for p in probs]
@@ -120,14 +142,29 @@ def test_lut_decode_sweep_sampled(sweep):
 
 
 @pytest.mark.parametrize("M", [32, 64])
-def test_batched_decode_sampled(sweep, M):
-    """Batched decode on the 28 gate and 28 down projections."""
-    say(f"[sweep] batched decode M={M}")
-    run_and_check(sweep, M, lambda p: p.proj in (4, 6), host_x=False)
+def test_batched_decode_sampled(longform, M):
+    """Batched decode on the 28 gate and 28 down long-form projections
+    (Student-t(3) weights; activations seed 60000+7l+p)."""
+    say(f"[long-form] batched decode M={M}")
+    run_and_check(longform, M, lambda p: p.proj in (4, 6), host_x=True)
 
 
-@pytest.mark.parametrize("M", [256, 1800])
-def test_prefill_sweep_sampled(sweep, M):
-    """Prefill over all 196 projections in one grouped launch."""
-    say(f"[sweep] prefill M={M}")
-    run_and_check(sweep, M, lambda p: True, host_x=False)
+def test_prefill_m256_sampled(sweep):
+    """Prefill at M=256 over all 196 projections in one grouped launch
+    (activations seed 30000+7l+p)."""
+    say("[sweep] prefill M=256")
+    run_and_check(sweep, 256, lambda p: True, host_x=True, x_problems=synth.prefill_problems())
+
+
+def test_prefill_m1800_longform_sampled(longform):
+    """Long-form prefill at M=1800 over all 196 Student-t(3) projections in one
+    grouped launch (activations seed 60000+7l+p)."""
+    say("[long-form] prefill M=1800")
+    run_and_check(longform, 1800, lambda p: True, host_x=True)
+
+
+def test_prefill_m1800_gpu_activations_sampled(sweep):
+    """Prefill at M=1800 over the sweep's weights with activations drawn on the
+    GPU (a second, independent input stream)."""
+    say("[sweep] prefill M=1800, GPU-drawn activations")
+    run_and_check(sweep, 1800, lambda p: True, host_x=False)
