@@ -56,6 +56,7 @@ DECODE_SOURCES = ("gemv.hip", "bitnet_device.hpp", "bitnet_internal.hpp")
 
 
 SWEEP_WEIGHTS = "0.02 N(0,1) fp32 masters, seed 10000+7l+p (the decode sweep's)"
+OVERLAP_CHUNKS = (4, 7, 14, 28)
 LONGFORM_WEIGHTS = "Student-t(3) fp32 masters scaled to std 0.01, seed 50000+7l+p"
 
 
@@ -94,6 +95,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the timed CPU-oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gen-workers", type=int, default=0,
+                    help="host processes drawing the workloads' arrays (0: one per CPU, at "
+                         "most 16; 1: in this process, as profiler runs need)")
+    ap.add_argument("--cache-dir", default="",
+                    help="keep drawn arrays as .npy files here and reuse them (profiler runs "
+                         "that repeat one workload)")
     return ap.parse_args()
 
 
@@ -158,6 +165,38 @@ class Timer:
                 "last_batches_us_per_step":
                 [round(prev * 1e3, 2) if prev else None, round(ms * 1e3, 2)]}
 
+    def graph_time(self, fn, calls, replays=20):
+        """Device time per call: `calls` calls captured once in a HIP graph and
+        the graph replayed back to back, so the host's launch rate (Python,
+        ctypes, one enqueue per kernel) drops out of the figure.  Returns ms
+        per call."""
+        torch = self.torch
+        fn(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(calls):
+                    fn(i)
+        torch.cuda.current_stream().wait_stream(cap)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (replays * calls)
+        g.reset()
+        cap.synchronize()
+        del g
+        return ms
+
     def per_step(self, fn, steps, warmup=3):
         """Device time of each step on its own (an event pair around every
         launch): median, minimum and interquartile range in microseconds."""
@@ -215,6 +254,7 @@ def vendor_reference(torch):
 
 def main():
     args = parse()
+    GEN["workers"], GEN["cache"] = args.gen_workers, args.cache_dir
     if args.gpus != 1:
         print(f"bench.py: this implementation runs on one GPU; --gpus {args.gpus} is not "
               "supported (multi-GPU operation would replicate the packed weights per GPU; "
@@ -471,9 +511,32 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+GEN = {"workers": 0, "cache": ""}
+
+
 def gen_workers() -> int:
     """Host processes for drawing the workloads' arrays (the machine's CPU share)."""
+    if GEN["workers"] > 0:
+        return GEN["workers"]
     return max(1, min(16, os.cpu_count() or 1))
+
+
+def cached(kind, items, draw):
+    """draw(items) -> iterator of arrays, one per item, unless --cache-dir holds
+    them (file per item, named by kind and the item's key)."""
+    d = GEN["cache"]
+    if not d:
+        yield from draw(items)
+        return
+    os.makedirs(d, exist_ok=True)
+    paths = [os.path.join(d, f"{kind}_{k}.npy") for k, _ in items]
+    if all(os.path.exists(p) for p in paths):
+        for p in paths:
+            yield np.load(p)
+        return
+    for p, a in zip(paths, draw(items)):
+        np.save(p, a)
+        yield a
 
 
 def pack_set(torch, tb, synth, problems, heavy_tail, dev):
@@ -482,8 +545,9 @@ def pack_set(torch, tb, synth, problems, heavy_tail, dev):
     packed, w_scales = [], []
     ws_t = torch.empty(tb.bitnet_ternarize_workspace_bytes(synth.INTERMEDIATE),
                        dtype=torch.uint8, device=dev)
-    for i, (p, W) in enumerate(zip(problems, synth.problem_weights_iter(problems, heavy_tail,
-                                                                      gen_workers()))):
+    items = [(f"{p.w_seed}_{p.N}x{p.K}_{int(heavy_tail)}", p) for p in problems]
+    draw = lambda it: synth.problem_weights_iter([p for _, p in it], heavy_tail, gen_workers())
+    for i, (p, W) in enumerate(zip(problems, cached("w", items, draw))):
         if i % 28 == 0:
             log(f"[bench] packing matrix {i} of {len(problems)}")
         Wd = torch.from_numpy(W).to(dev)
@@ -512,8 +576,9 @@ def host_activations(torch, synth, problems, M, dev):
     """problem_activations(p, M) for each problem (drawn on the host in worker
     processes: N(0,1), round(0.01 K) channels x20), copied to the device."""
     log(f"[bench] drawing activations for {len(problems)} problems, M={M}")
-    return [torch.from_numpy(x).to(dev)
-            for x in synth.problem_activations_iter(problems, M, gen_workers())]
+    items = [(f"{p.x_seed}_{M}x{p.K}", p) for p in problems]
+    draw = lambda it: synth.problem_activations_iter([p for _, p in it], M, gen_workers())
+    return [torch.from_numpy(x).to(dev) for x in cached("x", items, draw)]
 
 
 def gpu_activations(torch, g, M, K, dev):
@@ -542,6 +607,22 @@ def prefill_config(torch, tb, synth, timer, problems, packed, w_scales, M, dev, 
            "weights": weights,
            "activations": f"host numpy, seed {problems[0].x_seed - 7 * problems[0].layer - problems[0].proj}"
                           "+7l+p: N(0,1), round(0.01 K) channels x20"}
+    # The same step with the quantization of later chunks of problems on a
+    # second stream, overlapping the contraction of earlier ones.
+    aux = torch.cuda.Stream()
+    overlap = {}
+    for nch in OVERLAP_CHUNKS:
+        ms_o = timer.time(lambda i=0: plan.run_overlap(aux, nch), steps, warmup=3)
+        overlap[str(nch)] = round(ms_o, 4)
+    best = min(overlap, key=overlap.get)
+    ms_b = overlap[best]
+    res["overlapped"] = {"ms_per_step_by_chunks": overlap, "best_chunks": int(best),
+                         "ms_per_step": ms_b,
+                         "int8_TOPS": round(ops / (ms_b * 1e-3) / 1e12, 1),
+                         "frac_of_int8_peak": round(ops / (ms_b * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                         "step": "bitnet_ternary_matmul_grouped_overlap: quantization launches "
+                                 "on a second stream, GEMM launches on the timed stream"}
+    aux.synchronize()
     if zero_codes_check:
         zc = [torch.full_like(t, 0x55) for t in packed]
         zplan = tb.GroupedPlan(M, xs, zc, w_scales, ys, [p.N for p in problems],
@@ -753,15 +834,19 @@ def dwconv_config(torch, tb, synth, timer, dev, steps=100):
     xs = [x0] + [x0.clone() for _ in range(3)]
     ys = [torch.empty_like(x0) for _ in range(4)]
     ws = torch.empty(tb.bitnet_i8_dwconv_workspace_bytes(B, T, C), dtype=torch.uint8, device=dev)
-    ms = timer.time(lambda i=0: tb.bitnet_i8_dwconv_into(B, T, C, k, xs[i % 4], q, s, b, False,
-                                                         ys[i % 4], ws), steps, warmup=50)
+    call = lambda i=0: tb.bitnet_i8_dwconv_into(B, T, C, k, xs[i % 4], q, s, b, False,
+                                                 ys[i % 4], ws)
+    ms_host = timer.time(call, steps, warmup=50)
+    ms = timer.graph_time(call, 40)
     alg = 2 * B * T * C * 4 + C * k + 2 * C * 4
     return {"shape": {"B": B, "T": T, "C": C, "k": k, "bias": True},
             "us_per_call": round(ms * 1e3, 2),
+            "us_per_call_python_launches": round(ms_host * 1e3, 2),
             "GBps_moved": round(alg / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "algorithmic_bytes": alg,
-            "step": "column-maximum launch + convolution launch (x read twice, once per launch)"}
+            "step": "column-maximum, column-scale and convolution launches (x read twice); "
+                    "us_per_call is device time (40 calls in a HIP graph, replayed)"}
 
 
 def lmhead_configs(torch, tb, synth, timer, dev, steps=200):
@@ -836,12 +921,16 @@ def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, a
     xd = torch.from_numpy(x).to(dev)
     y = torch.empty((1, 1536), device=dev)
     ws = torch.empty(tb.bitnet_matmul_workspace_bytes(1, 1536), dtype=torch.uint8, device=dev)
-    ms = timer.time(lambda i=0: tb.bitnet_ternary_matmul_into(1, 1536, 1536, xd, copies[i % 600],
-                                                              sc, y, ws), 600)
+    call = lambda i=0: tb.bitnet_ternary_matmul_into(1, 1536, 1536, xd, copies[i % 600], sc, y, ws)
+    ms_host = timer.time(call, 600)
+    ms = timer.graph_time(call, 600)
     out["single_gemv_1536x1536_m1"] = {
         "us_per_call": round(ms * 1e3, 2),
         "weight_GBps": round(1536 * 1536 / 4 / (ms * 1e-3) / 1e9, 1),
-        "note": "one 590 KB matrix per launch: launch and latency bound"}
+        "us_per_call_python_launches": round(ms_host * 1e3, 2),
+        "note": "one 590 KB matrix per launch, latency bound; us_per_call is device time "
+                "(600 calls in a HIP graph, replayed); the other figure is bound by the "
+                "host's Python launch rate"}
     del copies
 
     # One decoder layer (7 projections, M=1) per grouped launch; steps walk the 28
@@ -872,8 +961,10 @@ def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, a
         inst = [(c[i], w_scales[i]) for c in (packed, copy_b) for i in idx]
         xd = torch.from_numpy(synth.problem_activations(problems[idx[0]], 1)).to(dev)
         yd = torch.empty((1, N), device=dev)
-        ms1 = timer.time(lambda i=0: tb.bitnet_ternary_matmul_into(
-            1, N, K, xd, inst[i % len(inst)][0], inst[i % len(inst)][1], yd, ws1), 4 * len(inst))
+        call = lambda i=0: tb.bitnet_ternary_matmul_into(
+            1, N, K, xd, inst[i % len(inst)][0], inst[i % len(inst)][1], yd, ws1)
+        ms1_host = timer.time(call, 4 * len(inst))
+        ms1 = timer.graph_time(call, 2 * len(inst))
         plans, _, _ = decode_plans(1, [problems[i] for i in idx])
         msg = timer.time(lambda i=0: plans[i % 2].run(), 100)
         b1 = N * K // 4
@@ -881,6 +972,7 @@ def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, a
             "K": K, "N": N,
             "single_us_per_call": round(ms1 * 1e3, 2),
             "single_weight_GBps": round(b1 / (ms1 * 1e-3) / 1e9, 1),
+            "single_us_per_call_python_launches": round(ms1_host * 1e3, 2),
             "grouped28_us_per_launch": round(msg * 1e3, 2),
             "grouped28_weight_GBps": round(28 * b1 / (msg * 1e-3) / 1e9, 1)}
         del plans
@@ -890,9 +982,14 @@ def other_configs(torch, tb, synth, timer, problems, packed, copy_b, w_scales, a
     pk0, sc0 = tb.bitnet_ternarize_pack(torch.ones((64, 128), device=dev))
     x0 = torch.ones((1, 128), device=dev)
     y0 = torch.empty((1, 64), device=dev)
-    ms0 = timer.time(lambda i=0: tb.bitnet_ternary_matmul_into(1, 64, 128, x0, pk0, sc0, y0, ws1),
-                     500)
-    out["launch_floor_m1_n64_k128"] = {"us_per_call": round(ms0 * 1e3, 2)}
+    call = lambda i=0: tb.bitnet_ternary_matmul_into(1, 64, 128, x0, pk0, sc0, y0, ws1)
+    ms0_host = timer.time(call, 500)
+    ms0 = timer.graph_time(call, 200)
+    out["launch_floor_m1_n64_k128"] = {
+        "us_per_call": round(ms0 * 1e3, 2),
+        "us_per_call_python_launches": round(ms0_host * 1e3, 2),
+        "note": "the smallest call: device time per launch in a replayed HIP graph, and the "
+                "rate at which Python enqueues the same call"}
 
     # The decode time must not depend on the codes: the sweep again with every
     # code 0 (field value 1 in all four positions of a byte).

@@ -41,6 +41,14 @@
  *   contiguous ("unit-column-major").  This bit placement is this library's
  *   own; the pages fix only the unit size and the 2-bit width.
  *
+ * Workspaces.  Every entry point that needs temporary device memory takes it
+ * as a caller-provided workspace argument with a size helper
+ * (bitnet_*_workspace_bytes), so the library itself never allocates; that is
+ * why the ternarization, the q8 matmul and the grouped calls carry workspace
+ * arguments, and why the matmul's size helper is named for the matmul
+ * (bitnet_matmul_workspace_bytes).  The one exception, for callers that
+ * cannot allocate at all, is bitnet_ternary_matmul_noalloc.
+ *
  * Conventions for every entry point:
  *   - All data pointers are DEVICE pointers on the current HIP device, which
  *     must be a gfx950 (MI355X).  `stream` is a hipStream_t passed as void*
@@ -173,7 +181,12 @@ bitnet_status bitnet_ternary_matmul_noalloc(int64_t M, int64_t N, int64_t K, con
                                             int32_t *acc_out, void *stream);
 
 /* Same projection from already-quantized activations (xq natural order, as
- * written by bitnet_quant_act).  workspace: bitnet_matmul_workspace_bytes(M, K). */
+ * written by bitnet_quant_act): the prefill GEMM proper, separable from the
+ * quantization.  workspace: bitnet_matmul_workspace_bytes(M, K) (the rows
+ * permuted to the packed order, and their sums).  Passage: as for
+ * bitnet_ternary_matmul; the pages' own interface also keeps the quantized
+ * tensors apart from the matmul node that consumes them (ONNX model card,
+ * Quantization table, row "LM projections": MatMulNBits over packed blocks). */
 bitnet_status bitnet_ternary_matmul_q8(int64_t M, int64_t N, int64_t K, const int8_t *xq,
                                        const float *x_scale, const uint8_t *packed,
                                        const float *w_scale, float *y, void *workspace,
@@ -196,6 +209,10 @@ bitnet_status bitnet_ternary_matmul_q8(int64_t M, int64_t N, int64_t K, const in
  * x pointer and the same K (a decoder's q, k and v, or its gate and up) share
  * one quantized copy of their rows: it is made once per call and takes
  * workspace once.  The outputs are the same as with separate copies.
+ * Passage: the decoder has 196 such matrices and reads all of them for every
+ * token (blog, "What the model is trying to do"; ONNX model card, Quantization
+ * table, row "LM projections (196 mats)"), so one token's projections are a
+ * stream of independent problems that one launch can cover.
  * ------------------------------------------------------------------------ */
 typedef struct bitnet_problem {
     const float *x;          /* [M,K] fp32 activations                     */
@@ -213,6 +230,28 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
                                             int32_t count, const bitnet_problem *problems_host,
                                             void *workspace, size_t workspace_bytes,
                                             void *stream);
+
+/* The same grouped projections at prefill (M > 16) with the activation
+ * quantization overlapped with the contraction: the problems are cut into
+ * `nchunks` contiguous runs of about equal work; the quantization launch of
+ * run c + 1 goes on aux_stream while the GEMM launch of run c runs on
+ * `stream` (the two kernels fit on a compute unit together: the GEMM leaves
+ * register room for a quantization wave), ordered by events the call creates
+ * and releases.  aux_stream first waits for the work already queued on
+ * `stream`; after the call, `stream` holds the whole result, and later work
+ * on aux_stream is ordered after the quantizations only.  Outputs are those of
+ * bitnet_ternary_matmul_grouped (the same kernels).  With M <= 16, nchunks <=
+ * 1 or aux_stream == stream this is the plain grouped call on `stream`.
+ * nchunks <= count and <= BITNET_MAX_CHUNKS; workspace as for the grouped
+ * call.  Use distinct, default-priority streams. */
+#define BITNET_MAX_CHUNKS 32
+
+bitnet_status bitnet_ternary_matmul_grouped_overlap(int64_t M, const bitnet_problem *problems_dev,
+                                                    int32_t count,
+                                                    const bitnet_problem *problems_host,
+                                                    int32_t nchunks, void *workspace,
+                                                    size_t workspace_bytes, void *stream,
+                                                    void *aux_stream);
 
 /* ------------------------------------------------------------------------
  * I8_S: int8 weights x int8 activations, the audio encoders' linear layers.
@@ -292,7 +331,7 @@ bitnet_status bitnet_i8_linear(int64_t M, int64_t N, int64_t K, const float *x, 
  *   [B,T,C] (16-byte aligned) and x_scale_out fp32 [B,C] optional.
  *   B <= 65535, C % 64 == 0, 1 <= k <= 64, B*T*C < 2^29.  workspace:
  *   bitnet_i8_dwconv_workspace_bytes(B, T, C) bytes, 16-byte aligned (the
- *   column maxima of each 128-frame chunk).  Two launches.
+ *   column maxima of each 128-frame chunk, then the scales).  Three launches.
  * ------------------------------------------------------------------------ */
 bitnet_status bitnet_i8_dwconv_quant_weights(const float *W, int64_t C, int64_t k, int8_t *q,
                                              float *w_scale, void *stream);

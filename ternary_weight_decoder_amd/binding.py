@@ -105,6 +105,9 @@ def lib():
         L.bitnet_i8_linear_rows.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p, _sz,
                                             _p, _p]
         L.bitnet_i8_linear_rows.restype = _i32
+        L.bitnet_ternary_matmul_grouped_overlap.argtypes = [_i64, _p, _i32, _p, _i32, _p, _sz, _p,
+                                                            _p]
+        L.bitnet_ternary_matmul_grouped_overlap.restype = _i32
         L.bitnet_i8_dwconv_quant_weights.argtypes = [_p, _i64, _i64, _p, _p, _p]
         L.bitnet_i8_dwconv_quant_weights.restype = _i32
         L.bitnet_i8_dwconv_workspace_bytes.argtypes = [_i64, _i64, _i64]
@@ -300,6 +303,22 @@ class GroupedPlan:
     def run(self, stream=None) -> None:
         bitnet_ternary_matmul_grouped(self.M, self.dev, self.count, self.host, self.workspace,
                                       stream)
+
+    def run_overlap(self, aux_stream, nchunks: int, stream=None) -> None:
+        """The same call with the quantization of later chunks on aux_stream,
+        overlapping the contraction of earlier ones (prefill, M > 16)."""
+        bitnet_ternary_matmul_grouped_overlap(self.M, self.dev, self.count, self.host, nchunks,
+                                              self.workspace, stream, aux_stream)
+
+
+def bitnet_ternary_matmul_grouped_overlap(M, problems_dev, count, problems_host, nchunks,
+                                          workspace, stream=None, aux_stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().bitnet_ternary_matmul_grouped_overlap(M, _ptr(problems_dev), count,
+                                                       _c.byref(problems_host), int(nchunks),
+                                                       _ptr(workspace), ws_bytes,
+                                                       _stream(stream), _stream(aux_stream)),
+           "bitnet_ternary_matmul_grouped_overlap")
 
 
 def bitnet_grouped_workspace_bytes(M: int, problems_host, count: int) -> int:

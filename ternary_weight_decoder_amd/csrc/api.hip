@@ -395,6 +395,119 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
   return from_hip(launch_gemm_grouped(problems_dev, tab, ws, hs));
 }
 
+// The prefill part of a grouped call over problems sub[0..n) (indices into
+// the whole problem array, whose workspace offsets and input owners are
+// given): the quantization launch of the inputs owned inside sub goes on qs,
+// the GEMM launch on gs; with ev, gs waits for qs through it in between.
+static bitnet_status prefill_chunk(int64_t M, const bitnet_problem *problems_dev,
+                                   const bitnet_problem *ph, const int32_t *sub, int32_t n,
+                                   const uint32_t *ws_off, const int32_t *owner, uint8_t *ws,
+                                   hipStream_t qs, hipStream_t gs, hipEvent_t ev) {
+  int32_t idx[kMaxGroup];
+  std::copy(sub, sub + n, idx);
+  std::stable_sort(idx, idx + n, [&](int32_t a, int32_t b) { return ph[a].K > ph[b].K; });
+  GroupTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  tab.count = n;
+  tab.M = (int32_t)M;
+  std::memcpy(tab.ws_off, ws_off, sizeof(tab.ws_off));
+  uint32_t tiles[kMaxGroup];
+  uint64_t total = 0;
+  for (int32_t s = 0; s < n; ++s) {
+    tiles[s] = (uint32_t)gemm_blocks(M, ph[idx[s]].N);
+    total += tiles[s];
+    if (total >= ((uint64_t)1 << 31)) return BITNET_ERR_SHAPE;
+    tab.blk_end[s] = (uint32_t)total;
+    tab.order[s] = (uint16_t)idx[s];
+  }
+  QuantTable qt;
+  std::memset(&qt, 0, sizeof(qt));
+  qt.M = (int32_t)M;
+  uint64_t qtotal = 0;
+  for (int32_t s = 0; s < n; ++s) {
+    if (owner[idx[s]] != idx[s]) continue;   // owned in this chunk or an earlier one
+    qtotal += (uint64_t)quant_grouped_blocks(M, ph[idx[s]].K);
+    if (qtotal >= ((uint64_t)1 << 31)) return BITNET_ERR_SHAPE;
+    qt.wg_end[qt.count] = (uint32_t)qtotal;
+    qt.order[qt.count] = (uint16_t)idx[s];
+    ++qt.count;
+  }
+  std::memcpy(qt.ws_off, ws_off, sizeof(qt.ws_off));
+  if (qt.count > 0) {
+    bitnet_status st = from_hip(launch_quant_grouped(problems_dev, qt, ws, qs));
+    if (st != BITNET_OK) return st;
+  }
+  if (ev) {
+    if (hipEventRecord(ev, qs) != hipSuccess || hipStreamWaitEvent(gs, ev, 0) != hipSuccess)
+      return BITNET_ERR_HIP;
+  }
+  xcd_schedule(tab, ph, tiles);
+  return from_hip(launch_gemm_grouped(problems_dev, tab, ws, gs));
+}
+
+bitnet_status bitnet_ternary_matmul_grouped_overlap(int64_t M, const bitnet_problem *problems_dev,
+                                                    int32_t count,
+                                                    const bitnet_problem *problems_host,
+                                                    int32_t nchunks, void *workspace,
+                                                    size_t workspace_bytes, void *stream,
+                                                    void *aux_stream) {
+  if (M <= kGemvMaxM || nchunks <= 1 || aux_stream == stream)
+    return bitnet_ternary_matmul_grouped(M, problems_dev, count, problems_host, workspace,
+                                         workspace_bytes, stream);
+  if (!problems_dev || !problems_host) return BITNET_ERR_NULL;
+  if (count < 1 || count > kMaxGroup || nchunks > count || nchunks > BITNET_MAX_CHUNKS)
+    return BITNET_ERR_SHAPE;
+  if (!aligned(problems_dev, 8)) return BITNET_ERR_ALIGN;
+  for (int32_t i = 0; i < count; ++i) {
+    bitnet_status st = check_problem(M, problems_host[i]);
+    if (st != BITNET_OK) return st;
+  }
+  uint32_t ws_off[kMaxGroup] = {0};
+  int32_t owner[kMaxGroup];
+  const size_t need = group_ws(M, problems_host, count, ws_off, owner);
+  if (!workspace || workspace_bytes < need) return BITNET_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return BITNET_ERR_ALIGN;
+  bitnet_status st = device_check();
+  if (st != BITNET_OK) return st;
+  // Chunks: contiguous runs of problems of about equal contraction work.
+  uint64_t work_total = 0;
+  for (int32_t i = 0; i < count; ++i)
+    work_total += (uint64_t)problems_host[i].N * (uint64_t)problems_host[i].K;
+  int32_t first[BITNET_MAX_CHUNKS + 1];
+  int32_t c = 0;
+  uint64_t acc = 0;
+  first[0] = 0;
+  for (int32_t i = 0; i < count && c + 1 < nchunks; ++i) {
+    acc += (uint64_t)problems_host[i].N * (uint64_t)problems_host[i].K;
+    if (acc * (uint64_t)nchunks >= work_total * (uint64_t)(c + 1) && i + 1 < count)
+      first[++c] = i + 1;
+  }
+  const int32_t chunks = c + 1;
+  first[chunks] = count;
+  hipStream_t gs = as_stream(stream), qs = as_stream(aux_stream);
+  uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
+  // The auxiliary stream starts after everything already queued on the main
+  // stream (the inputs, and an earlier call's contractions over the same
+  // workspace).  Events are released after use; HIP frees them once their
+  // pending work completes.
+  hipEvent_t start = nullptr;
+  if (hipEventCreateWithFlags(&start, hipEventDisableTiming) != hipSuccess) return BITNET_ERR_HIP;
+  st = (hipEventRecord(start, gs) == hipSuccess && hipStreamWaitEvent(qs, start, 0) == hipSuccess)
+           ? BITNET_OK
+           : BITNET_ERR_HIP;
+  hipEventDestroy(start);
+  int32_t sub[kMaxGroup];
+  for (int32_t k = 0; k < chunks && st == BITNET_OK; ++k) {
+    const int32_t n = first[k + 1] - first[k];
+    for (int32_t i = 0; i < n; ++i) sub[i] = first[k] + i;
+    hipEvent_t ev = nullptr;
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return BITNET_ERR_HIP;
+    st = prefill_chunk(M, problems_dev, problems_host, sub, n, ws_off, owner, ws, qs, gs, ev);
+    hipEventDestroy(ev);
+  }
+  return st;
+}
+
 // I8_S shapes: K a multiple of 64 (one GEMM step), the same size limits as the
 // ternary path.
 static bool i8_shape_ok(int64_t M, int64_t N, int64_t K) {

@@ -16,10 +16,10 @@
 // division, bias add, one rounding to fp32), so outputs are bit-exact.
 //
 // Launches (all HBM-bound): colmax_kernel writes the maximum |x| of each
-// (sequence, 128-frame chunk, channel) to the workspace; dwconv_kernel takes
-// one sequence's 64-frame x 64-channel output tile, reduces its channels'
-// chunk maxima to the scales, quantizes the tile's input frames (6 halo
-// frames before it for k = 7) into LDS, and convolves from LDS.
+// (sequence, 128-frame chunk, channel) to the workspace; colscale_kernel turns
+// each column's chunk maxima into its scale; dwconv_kernel takes one
+// sequence's 64-frame x 64-channel output tile, quantizes the tile's input
+// frames (6 halo frames before it for k = 7) into LDS, and convolves from LDS.
 #include <algorithm>
 
 #include "bitnet_device.hpp"
@@ -42,7 +42,7 @@ struct DwParams {
   float *y;                // [B][T][C]
   int32_t *acc_out;        // [B][T][C] or null
   float *x_scale_out;      // [B][C] or null
-  const float *partial;    // [B][nchunk][C] chunk maxima
+  const float *partial;    // [B][nchunk][C] chunk maxima; chunk 0 holds the scales
   int B, T, C, k, nchunk, relu;
 };
 
@@ -57,12 +57,18 @@ __global__ void __launch_bounds__(kThreads) colmax_kernel(const float *x, int T,
   const int t0 = chunk * kChunkFrames;
   const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x + (size_t)b * T * C + c0) + cq;
   f32x4 m = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int t = t0 + fr; t < min(t0 + kChunkFrames, T); t += 16) {
-    const f32x4 v = ld_global<f32x4>(x4 + (size_t)t * (C / 4));
-    m.x = fmaxf(m.x, fabsf(v.x));
-    m.y = fmaxf(m.y, fabsf(v.y));
-    m.z = fmaxf(m.z, fabsf(v.z));
-    m.w = fmaxf(m.w, fabsf(v.w));
+  f32x4 v[kChunkFrames / 16];
+#pragma unroll
+  for (int i = 0; i < kChunkFrames / 16; ++i) {
+    const int t = t0 + fr + 16 * i;
+    v[i] = t < T ? ld_global<f32x4>(x4 + (size_t)t * (C / 4)) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+#pragma unroll
+  for (int i = 0; i < kChunkFrames / 16; ++i) {
+    m.x = fmaxf(m.x, fabsf(v[i].x));
+    m.y = fmaxf(m.y, fabsf(v[i].y));
+    m.z = fmaxf(m.z, fabsf(v[i].z));
+    m.w = fmaxf(m.w, fabsf(v[i].w));
   }
   red[tid] = m;
   __syncthreads();
@@ -79,9 +85,30 @@ __global__ void __launch_bounds__(kThreads) colmax_kernel(const float *x, int T,
   }
 }
 
+// Scales of every (sequence, channel): the maximum of its chunk maxima, one
+// thread per (sequence, channel); written over chunk 0's maxima.
+__global__ void __launch_bounds__(kThreads) colscale_kernel(float *partial, int B, int C,
+                                                            int nchunk, float *x_scale_out) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= B * C) return;
+  const int b = i / C, c = i - b * C;
+  float *col = partial + (size_t)b * nchunk * C + c;
+  float a = 0.0f;
+  for (int ch0 = 0; ch0 < nchunk; ch0 += 16) {   // 16 loads in flight at a time
+    float m[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      m[u] = ch0 + u < nchunk ? ld_global<float>(col + (size_t)(ch0 + u) * C) : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) a = fmaxf(a, m[u]);
+  }
+  const float s = (a == 0.0f) ? 1.0f : 127.0f / a;
+  st_global<float>(col, s);
+  if (x_scale_out) st_global<float>(x_scale_out + i, s);
+}
+
 template <bool RELU>
 __global__ void __launch_bounds__(kThreads) dwconv_kernel(DwParams p) {
-  __shared__ float amax[4][kTileC];
   __shared__ float sx[kTileC], sw[kTileC], bs[kTileC];
   __shared__ int8_t qk[kTileC][kMaxDwTaps];
   // quantized input frames t0 - (k-1) .. t0 + kTileT - 1, 64 channels each
@@ -91,15 +118,23 @@ __global__ void __launch_bounds__(kThreads) dwconv_kernel(DwParams p) {
   const int t0 = tt * kTileT;
   const int halo = p.k - 1;
 
-  // Scales of the tile's channels: maximum over the sequence's chunk maxima.
-  {
-    const int c = tid & 63, part = tid >> 6;
-    float a = 0.0f;
-    for (int ch = part; ch < p.nchunk; ch += 4)
-      a = fmaxf(a, ld_global<float>(p.partial + ((size_t)b * p.nchunk + ch) * p.C + c0 + c));
-    amax[part][c] = a;
+  // The tile's input frames t0 - halo .. t0 + kTileT - 1 (frames before 0 and
+  // past T are zeros), all loads of a thread at once; thread (cq, fr) takes
+  // channels 4cq..4cq+3 of frames fr, fr + 16, ...
+  const int cq = tid & 15, fr = tid >> 4;
+  const int rows = kTileT + halo;
+  const f32x4 *x4 = reinterpret_cast<const f32x4 *>(p.x + (size_t)b * p.T * p.C + c0) + cq;
+  constexpr int kRowLoads = (kTileT + kMaxDwTaps - 1 + 15) / 16;
+  f32x4 v[kRowLoads];
+#pragma unroll
+  for (int i = 0; i < kRowLoads; ++i) {
+    const int r = fr + 16 * i, t = t0 - halo + r;
+    v[i] = (r < rows && t >= 0 && t < p.T) ? ld_global<f32x4>(x4 + (size_t)t * (p.C / 4))
+                                           : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
+  // Scales (from the column-scale launch), kernel taps, bias.
   if (tid < kTileC) {
+    sx[tid] = ld_global<float>(p.partial + (size_t)b * p.nchunk * p.C + c0 + tid);
     sw[tid] = ld_global<float>(p.w_scale + c0 + tid);
     bs[tid] = p.bias ? ld_global<float>(p.bias + c0 + tid) : 0.0f;
   }
@@ -108,28 +143,14 @@ __global__ void __launch_bounds__(kThreads) dwconv_kernel(DwParams p) {
     qk[c][j] = p.q[(size_t)(c0 + c) * p.k + j];
   }
   __syncthreads();
-  if (tid < kTileC) {
-    const float a = fmaxf(fmaxf(amax[0][tid], amax[1][tid]), fmaxf(amax[2][tid], amax[3][tid]));
-    const float s = (a == 0.0f) ? 1.0f : 127.0f / a;
-    sx[tid] = s;
-    if (p.x_scale_out && tt == 0) st_global<float>(p.x_scale_out + (size_t)b * p.C + c0 + tid, s);
-  }
-  __syncthreads();
-
-  // Quantize the input frames of the tile into LDS (frames before 0 and past
-  // T are zeros); thread (cq, fr) takes channels 4cq..4cq+3.
-  const int cq = tid & 15, fr = tid >> 4;
-  const int rows = kTileT + halo;
-  const f32x4 *x4 = reinterpret_cast<const f32x4 *>(p.x + (size_t)b * p.T * p.C + c0) + cq;
   const float s0 = sx[4 * cq], s1 = sx[4 * cq + 1], s2 = sx[4 * cq + 2], s3 = sx[4 * cq + 3];
-  for (int r = fr; r < rows; r += 16) {
-    const int t = t0 - halo + r;
-    uint32_t w = 0;
-    if (t >= 0 && t < p.T) {
-      const f32x4 v = ld_global<f32x4>(x4 + (size_t)t * (p.C / 4));
-      w = pack4_i8(quant_one(v.x, s0), quant_one(v.y, s1), quant_one(v.z, s2), quant_one(v.w, s3));
-    }
-    *reinterpret_cast<uint32_t *>(&xq[r * kTileC + 4 * cq]) = w;
+#pragma unroll
+  for (int i = 0; i < kRowLoads; ++i) {
+    const int r = fr + 16 * i;
+    if (r < rows)
+      *reinterpret_cast<uint32_t *>(&xq[r * kTileC + 4 * cq]) =
+          pack4_i8(quant_one(v[i].x, s0), quant_one(v[i].y, s1), quant_one(v[i].z, s2),
+                   quant_one(v[i].w, s3));
   }
   __syncthreads();
 
@@ -196,7 +217,9 @@ hipError_t launch_dwconv(int B, int T, int C, int k, const float *x, const int8_
                          hipStream_t stream) {
   const int nchunk = dw_chunks(T);
   colmax_kernel<<<dim3(nchunk, C / kTileC, B), kThreads, 0, stream>>>(x, T, C, nchunk, partial);
-  DwParams p{x, q, w_scale, bias, y, acc_out, x_scale_out, partial, B, T, C, k, nchunk, relu};
+  colscale_kernel<<<(unsigned)((B * C + kThreads - 1) / kThreads), kThreads, 0, stream>>>(
+      partial, B, C, nchunk, x_scale_out);
+  DwParams p{x, q, w_scale, bias, y, acc_out, nullptr, partial, B, T, C, k, nchunk, relu};
   const dim3 grid((T + kTileT - 1) / kTileT, C / kTileC, B);
   if (relu)
     dwconv_kernel<true><<<grid, kThreads, 0, stream>>>(p);

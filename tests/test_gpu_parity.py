@@ -399,6 +399,45 @@ def test_grouped_many_ragged_parity(tb, M):
         assert_y_matches(ys[i].cpu().numpy(), ref["y"], M)
 
 
+@pytest.mark.parametrize("M,nchunks", [(40, 2), (300, 5), (1800, 7)])
+def test_grouped_overlap_matches_grouped(tb, M, nchunks):
+    """The prefill grouped call with its quantization on a second stream gives
+    the plain grouped call's outputs, bit for bit, twice in a row over the same
+    workspace (the second call's quantization must wait for the first call's
+    contraction).  Problems share inputs across chunk boundaries."""
+    import torch
+    say(f"[grouped overlap] M={M} chunks={nchunks}")
+    rng = np.random.default_rng(930 + M)
+    shapes = [(int(rng.choice([72, 520, 1536, 2600])), int(rng.choice([128, 1536, 2176])))
+              for _ in range(24)]
+    Ws = [synth.normal_weights(N, K, seed=7000 + i) for i, (N, K) in enumerate(shapes)]
+    packs = [oracle.ternarize_pack(W) for W in Ws]
+    xd = {}
+    dx = []
+    for i, (N, K) in enumerate(shapes):
+        key = (i // 3, K)        # neighbours with the same K read one input buffer
+        if key not in xd:
+            xd[key] = dev_tensor(synth.activations(M, K, seed=8000 + i))
+        dx.append(xd[key])
+    dp = [dev_tensor(p) for p, _ in packs]
+    ds = [dev_tensor(np.array([s], np.float32)) for _, s in packs]
+    Ns, Ks = [N for N, _ in shapes], [K for _, K in shapes]
+    ys_ref = [torch.full((M, N), float("nan"), device="cuda:0") for N in Ns]
+    tb.GroupedPlan(M, dx, dp, ds, ys_ref, Ns, Ks).run()
+    torch.cuda.synchronize()
+    ys = [torch.full((M, N), float("nan"), device="cuda:0") for N in Ns]
+    plan = tb.GroupedPlan(M, dx, dp, ds, ys, Ns, Ks)
+    aux = torch.cuda.Stream()
+    for _ in range(2):
+        for y in ys:
+            y.fill_(float("nan"))
+        plan.run_overlap(aux, nchunks)
+        plan.run_overlap(aux, nchunks)
+        torch.cuda.synchronize()
+        for a, b in zip(ys, ys_ref):
+            assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("M", [1, 4, 16, 40, 200])
 def test_grouped_shared_inputs_parity(tb, M):
     """One layer called the way a decoder calls it: q, k and v read one input
