@@ -845,7 +845,7 @@ def dwconv_config(torch, tb, synth, timer, dev, steps=100):
             "GBps_moved": round(alg / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "algorithmic_bytes": alg,
-            "step": "column-maximum, column-scale and convolution launches (x read twice); "
+            "step": "column-maximum and convolution launches (x read twice); "
                     "us_per_call is device time (40 calls in a HIP graph, replayed)"}
 
 

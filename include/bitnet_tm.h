@@ -331,7 +331,10 @@ bitnet_status bitnet_i8_linear(int64_t M, int64_t N, int64_t K, const float *x, 
  *   [B,T,C] (16-byte aligned) and x_scale_out fp32 [B,C] optional.
  *   B <= 65535, C % 64 == 0, 1 <= k <= 64, B*T*C < 2^29.  workspace:
  *   bitnet_i8_dwconv_workspace_bytes(B, T, C) bytes, 16-byte aligned (the
- *   column maxima of each 128-frame chunk, then the scales).  Three launches.
+ *   column maxima of each frame chunk: chunks of 128 frames, or of a larger
+ *   power of two so that a sequence has at most 64).  Two launches: the
+ *   chunk maxima, then the convolution, whose workgroups reduce them to the
+ *   scales of their channels.
  * ------------------------------------------------------------------------ */
 bitnet_status bitnet_i8_dwconv_quant_weights(const float *W, int64_t C, int64_t k, int8_t *q,
                                              float *w_scale, void *stream);

@@ -15,11 +15,12 @@
 // the plain definition in its order (exact product, correctly rounded
 // division, bias add, one rounding to fp32), so outputs are bit-exact.
 //
-// Launches (all HBM-bound): colmax_kernel writes the maximum |x| of each
-// (sequence, 128-frame chunk, channel) to the workspace; colscale_kernel turns
-// each column's chunk maxima into its scale; dwconv_kernel takes one
-// sequence's 64-frame x 64-channel output tile, quantizes the tile's input
-// frames (6 halo frames before it for k = 7) into LDS, and convolves from LDS.
+// Launches (both HBM-bound): colmax_kernel writes the maximum |x| of each
+// (sequence, frame chunk, channel) to the workspace, with chunks of 128 frames
+// or more so that a sequence has at most kMaxChunks of them; dwconv_kernel
+// takes one sequence's 64-frame x 64-channel output tile, reduces its
+// channels' chunk maxima to the scales, quantizes the tile's input frames (6
+// halo frames before it for k = 7) into LDS, and convolves from LDS.
 #include <algorithm>
 
 #include "bitnet_device.hpp"
@@ -30,9 +31,14 @@ namespace bitnet {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunkFrames = 128;   // frames per partial maximum
-constexpr int kTileC = 64;          // channels per workgroup tile
-constexpr int kTileT = 64;          // output frames per workgroup tile
+constexpr int kMinChunkFrames = 128;   // frames per partial maximum, at least
+constexpr int kMaxChunks = 64;         // partial maxima per (sequence, channel), at most
+constexpr int kTileC = 64;             // channels per workgroup tile
+constexpr int kTileT = 64;             // output frames per workgroup tile
+// LDS row of the quantized tile: 64 channels plus 16 bytes of padding, so the
+// rows 4 apart that the 4 frame groups of a wave read together start 20 words
+// apart and fall in different banks.
+constexpr int kRowStride = kTileC + 16;
 
 struct DwParams {
   const float *x;          // [B][T][C]
@@ -42,33 +48,42 @@ struct DwParams {
   float *y;                // [B][T][C]
   int32_t *acc_out;        // [B][T][C] or null
   float *x_scale_out;      // [B][C] or null
-  const float *partial;    // [B][nchunk][C] chunk maxima; chunk 0 holds the scales
+  const float *partial;    // [B][nchunk][C] chunk maxima
   int B, T, C, k, nchunk, relu;
 };
 
+__host__ __device__ inline int chunk_frames(int64_t T) {
+  int cf = kMinChunkFrames;
+  while ((T + cf - 1) / cf > kMaxChunks) cf *= 2;
+  return cf;
+}
+
 // Workgroup (chunk, channel tile, b): thread (cq = tid % 16, fr = tid / 16)
 // takes channels 4cq..4cq+3 of the tile and frames fr, fr + 16, ... of the
-// chunk; the 16 frame lanes are then reduced through LDS.
+// chunk, 8 loads in flight at a time; the 16 frame lanes are then reduced
+// through LDS.
 __global__ void __launch_bounds__(kThreads) colmax_kernel(const float *x, int T, int C,
-                                                          int nchunk, float *partial) {
+                                                          int nchunk, int cf, float *partial) {
   __shared__ f32x4 red[kThreads];
   const int chunk = blockIdx.x, c0 = blockIdx.y * kTileC, b = blockIdx.z;
   const int tid = threadIdx.x, cq = tid & 15, fr = tid >> 4;
-  const int t0 = chunk * kChunkFrames;
+  const int t0 = chunk * cf, t1 = min(t0 + cf, T);
   const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x + (size_t)b * T * C + c0) + cq;
   f32x4 m = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  f32x4 v[kChunkFrames / 16];
+  for (int tb = t0; tb < t1; tb += 8 * 16) {
+    f32x4 v[8];
 #pragma unroll
-  for (int i = 0; i < kChunkFrames / 16; ++i) {
-    const int t = t0 + fr + 16 * i;
-    v[i] = t < T ? ld_global<f32x4>(x4 + (size_t)t * (C / 4)) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  }
+    for (int i = 0; i < 8; ++i) {
+      const int t = tb + fr + 16 * i;
+      v[i] = t < t1 ? ld_global<f32x4>(x4 + (size_t)t * (C / 4)) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 #pragma unroll
-  for (int i = 0; i < kChunkFrames / 16; ++i) {
-    m.x = fmaxf(m.x, fabsf(v[i].x));
-    m.y = fmaxf(m.y, fabsf(v[i].y));
-    m.z = fmaxf(m.z, fabsf(v[i].z));
-    m.w = fmaxf(m.w, fabsf(v[i].w));
+    for (int i = 0; i < 8; ++i) {
+      m.x = fmaxf(m.x, fabsf(v[i].x));
+      m.y = fmaxf(m.y, fabsf(v[i].y));
+      m.z = fmaxf(m.z, fabsf(v[i].z));
+      m.w = fmaxf(m.w, fabsf(v[i].w));
+    }
   }
   red[tid] = m;
   __syncthreads();
@@ -85,43 +100,29 @@ __global__ void __launch_bounds__(kThreads) colmax_kernel(const float *x, int T,
   }
 }
 
-// Scales of every (sequence, channel): the maximum of its chunk maxima, one
-// thread per (sequence, channel); written over chunk 0's maxima.
-__global__ void __launch_bounds__(kThreads) colscale_kernel(float *partial, int B, int C,
-                                                            int nchunk, float *x_scale_out) {
-  const int i = blockIdx.x * kThreads + threadIdx.x;
-  if (i >= B * C) return;
-  const int b = i / C, c = i - b * C;
-  float *col = partial + (size_t)b * nchunk * C + c;
-  float a = 0.0f;
-  for (int ch0 = 0; ch0 < nchunk; ch0 += 16) {   // 16 loads in flight at a time
-    float m[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u)
-      m[u] = ch0 + u < nchunk ? ld_global<float>(col + (size_t)(ch0 + u) * C) : 0.0f;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) a = fmaxf(a, m[u]);
-  }
-  const float s = (a == 0.0f) ? 1.0f : 127.0f / a;
-  st_global<float>(col, s);
-  if (x_scale_out) st_global<float>(x_scale_out + i, s);
+__device__ __forceinline__ f32x4 max4(f32x4 a, f32x4 b) {
+  return f32x4{fmaxf(a.x, b.x), fmaxf(a.y, b.y), fmaxf(a.z, b.z), fmaxf(a.w, b.w)};
 }
+
+// Byte e of w, sign-extended.
+__device__ __forceinline__ int sbyte(uint32_t w, int e) { return (int)(int8_t)(w >> (8 * e)); }
 
 template <bool RELU>
 __global__ void __launch_bounds__(kThreads) dwconv_kernel(DwParams p) {
+  __shared__ f32x4 red[kThreads];
   __shared__ float sx[kTileC], sw[kTileC], bs[kTileC];
-  __shared__ int8_t qk[kTileC][kMaxDwTaps];
+  __shared__ uint32_t taps[kMaxDwTaps][kTileC / 4];   // word cq of tap j: channels 4cq..4cq+3
   // quantized input frames t0 - (k-1) .. t0 + kTileT - 1, 64 channels each
-  __shared__ __attribute__((aligned(16))) int8_t xq[(kTileT + kMaxDwTaps - 1) * kTileC];
+  __shared__ __attribute__((aligned(16))) int8_t xq[(kTileT + kMaxDwTaps - 1) * kRowStride];
   const int tt = blockIdx.x, c0 = blockIdx.y * kTileC, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int t0 = tt * kTileT;
   const int halo = p.k - 1;
+  const int cq = tid & 15, fr = tid >> 4;
 
   // The tile's input frames t0 - halo .. t0 + kTileT - 1 (frames before 0 and
-  // past T are zeros), all loads of a thread at once; thread (cq, fr) takes
-  // channels 4cq..4cq+3 of frames fr, fr + 16, ...
-  const int cq = tid & 15, fr = tid >> 4;
+  // past T are zeros) and the chunk maxima of its channels (chunks fr, fr + 16,
+  // fr + 32, fr + 48), all loads of a thread at once.
   const int rows = kTileT + halo;
   const f32x4 *x4 = reinterpret_cast<const f32x4 *>(p.x + (size_t)b * p.T * p.C + c0) + cq;
   constexpr int kRowLoads = (kTileT + kMaxDwTaps - 1 + 15) / 16;
@@ -132,15 +133,38 @@ __global__ void __launch_bounds__(kThreads) dwconv_kernel(DwParams p) {
     v[i] = (r < rows && t >= 0 && t < p.T) ? ld_global<f32x4>(x4 + (size_t)t * (p.C / 4))
                                            : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  // Scales (from the column-scale launch), kernel taps, bias.
+  const f32x4 *pm =
+      reinterpret_cast<const f32x4 *>(p.partial + (size_t)b * p.nchunk * p.C + c0) + cq;
+  f32x4 cm[kMaxChunks / 16];
+#pragma unroll
+  for (int i = 0; i < kMaxChunks / 16; ++i) {
+    const int ch = fr + 16 * i;
+    cm[i] = ch < p.nchunk ? ld_global<f32x4>(pm + (size_t)ch * (p.C / 4))
+                          : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
   if (tid < kTileC) {
-    sx[tid] = ld_global<float>(p.partial + (size_t)b * p.nchunk * p.C + c0 + tid);
     sw[tid] = ld_global<float>(p.w_scale + c0 + tid);
     bs[tid] = p.bias ? ld_global<float>(p.bias + c0 + tid) : 0.0f;
   }
-  for (int i = tid; i < kTileC * p.k; i += kThreads) {
-    const int c = i / p.k, j = i - c * p.k;
-    qk[c][j] = p.q[(size_t)(c0 + c) * p.k + j];
+  for (int i = tid; i < p.k * (kTileC / 4); i += kThreads) {
+    const int j = i / (kTileC / 4), g = i - j * (kTileC / 4);
+    const int8_t *qc = p.q + (size_t)(c0 + 4 * g) * p.k + j;
+    taps[j][g] = pack4_i8(ld_global<int8_t>(qc), ld_global<int8_t>(qc + p.k),
+                          ld_global<int8_t>(qc + 2 * p.k), ld_global<int8_t>(qc + 3 * p.k));
+  }
+  red[tid] = max4(max4(cm[0], cm[1]), max4(cm[2], cm[3]));
+  __syncthreads();
+  if (tid < 16) {
+    f32x4 a = red[tid];
+    for (int r = 1; r < 16; ++r) a = max4(a, red[r * 16 + tid]);
+    const float *av = reinterpret_cast<const float *>(&a);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float s = (av[e] == 0.0f) ? 1.0f : 127.0f / av[e];
+      sx[4 * tid + e] = s;
+      if (p.x_scale_out && tt == 0)
+        st_global<float>(p.x_scale_out + (size_t)b * p.C + c0 + 4 * tid + e, s);
+    }
   }
   __syncthreads();
   const float s0 = sx[4 * cq], s1 = sx[4 * cq + 1], s2 = sx[4 * cq + 2], s3 = sx[4 * cq + 3];
@@ -148,36 +172,53 @@ __global__ void __launch_bounds__(kThreads) dwconv_kernel(DwParams p) {
   for (int i = 0; i < kRowLoads; ++i) {
     const int r = fr + 16 * i;
     if (r < rows)
-      *reinterpret_cast<uint32_t *>(&xq[r * kTileC + 4 * cq]) =
+      *reinterpret_cast<uint32_t *>(&xq[r * kRowStride + 4 * cq]) =
           pack4_i8(quant_one(v[i].x, s0), quant_one(v[i].y, s1), quant_one(v[i].z, s2),
                    quant_one(v[i].w, s3));
   }
   __syncthreads();
 
-  // Output frames t0 + fr + 16 i, channels 4cq..4cq+3.
-  for (int o = fr; o < kTileT; o += 16) {
-    const int t = t0 + o;
-    if (t >= p.T) break;
-    int acc[4] = {0, 0, 0, 0};
-    for (int j = 0; j < p.k; ++j) {
-      const uint32_t w = *reinterpret_cast<const uint32_t *>(&xq[(o + j) * kTileC + 4 * cq]);
+  // Output frames t0 + 4fr .. t0 + 4fr + 3, channels 4cq..4cq+3: a window of
+  // four input rows slides over the taps, one new row and one tap word per tap.
+  const int o0 = 4 * fr;
+  uint32_t w[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        acc[e] += (int)(int8_t)((w >> (8 * e)) & 0xff) * (int)qk[4 * cq + e][j];
-    }
+  for (int i = 0; i < 4; ++i)
+    w[i] = *reinterpret_cast<const uint32_t *>(&xq[(o0 + i) * kRowStride + 4 * cq]);
+  int acc[4][4] = {};
+  for (int j = 0; j < p.k; ++j) {
+    const uint32_t tw = taps[j][cq];
+    int tv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tv[e] = sbyte(tw, e);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][e] += sbyte(w[i], e) * tv[e];
+    w[0] = w[1];
+    w[1] = w[2];
+    w[2] = w[3];
+    if (j + 1 < p.k)
+      w[3] = *reinterpret_cast<const uint32_t *>(&xq[(o0 + 4 + j) * kRowStride + 4 * cq]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + o0 + i;
+    if (t >= p.T) break;
     const size_t off = ((size_t)b * p.T + t) * p.C + c0 + 4 * cq;
     f32x4 out;
     float *ov = reinterpret_cast<float *>(&out);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int c = 4 * cq + e;
-      double v = (double)acc[e] * (double)sw[c] / (double)sx[c];
-      if (p.bias) v += (double)bs[c];
-      if (RELU && v <= 0.0) v = 0.0;
-      ov[e] = (float)v;
+      double val = (double)acc[i][e] * (double)sw[c] / (double)sx[c];
+      if (p.bias) val += (double)bs[c];
+      if (RELU && val <= 0.0) val = 0.0;
+      ov[e] = (float)val;
     }
     st_global<f32x4>(p.y + off, out);
-    if (p.acc_out) st_global<v4i>(p.acc_out + off, v4i{acc[0], acc[1], acc[2], acc[3]});
+    if (p.acc_out)
+      st_global<v4i>(p.acc_out + off, v4i{acc[i][0], acc[i][1], acc[i][2], acc[i][3]});
   }
 }
 
@@ -202,7 +243,10 @@ __global__ void __launch_bounds__(kThreads) dw_quant_weights_kernel(const float 
 
 }  // namespace
 
-int dw_chunks(int64_t T) { return (int)((T + kChunkFrames - 1) / kChunkFrames); }
+int dw_chunks(int64_t T) {
+  const int cf = chunk_frames(T);
+  return (int)((T + cf - 1) / cf);
+}
 
 hipError_t launch_dw_quant_weights(const float *W, int64_t C, int64_t k, int8_t *q,
                                    float *w_scale, hipStream_t stream) {
@@ -216,10 +260,9 @@ hipError_t launch_dwconv(int B, int T, int C, int k, const float *x, const int8_
                          float *partial, int32_t *acc_out, float *x_scale_out,
                          hipStream_t stream) {
   const int nchunk = dw_chunks(T);
-  colmax_kernel<<<dim3(nchunk, C / kTileC, B), kThreads, 0, stream>>>(x, T, C, nchunk, partial);
-  colscale_kernel<<<(unsigned)((B * C + kThreads - 1) / kThreads), kThreads, 0, stream>>>(
-      partial, B, C, nchunk, x_scale_out);
-  DwParams p{x, q, w_scale, bias, y, acc_out, nullptr, partial, B, T, C, k, nchunk, relu};
+  colmax_kernel<<<dim3(nchunk, C / kTileC, B), kThreads, 0, stream>>>(x, T, C, nchunk,
+                                                                      chunk_frames(T), partial);
+  DwParams p{x, q, w_scale, bias, y, acc_out, x_scale_out, partial, B, T, C, k, nchunk, relu};
   const dim3 grid((T + kTileT - 1) / kTileT, C / kTileC, B);
   if (relu)
     dwconv_kernel<true><<<grid, kThreads, 0, stream>>>(p);
