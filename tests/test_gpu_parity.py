@@ -399,6 +399,34 @@ def test_grouped_many_ragged_parity(tb, M):
         assert_y_matches(ys[i].cpu().numpy(), ref["y"], M)
 
 
+@pytest.mark.parametrize("M", [1, 3, 5])
+def test_grouped_large_ragged_parity(tb, M):
+    """160 ragged projections in one grouped decode call, a launch big enough
+    to fill the chip (over 1000 tiles): at M = 1 and 3 every workgroup
+    quantizes its rows itself, at M = 5 (5 x 2176 > 8960) the rows are staged
+    from the quantization launch.  Two calls in a row; every output against
+    the oracle, bit for bit."""
+    import torch
+    say(f"[grouped] 160 ragged projections, M={M}")
+    rng = np.random.default_rng(960 + M)
+    shapes = [(int(rng.choice([72, 300, 1000, 1536, 2600, 4200])),
+               int(rng.choice([128, 384, 1536, 2176]))) for _ in range(160)]
+    Ws = [synth.normal_weights(N, K, seed=11000 + i) for i, (N, K) in enumerate(shapes)]
+    xs = [synth.activations(M, K, seed=12000 + i) for i, (N, K) in enumerate(shapes)]
+    packs = [oracle.ternarize_pack(W) for W in Ws]
+    dx = [dev_tensor(x) for x in xs]
+    dp = [dev_tensor(p) for p, _ in packs]
+    ds = [dev_tensor(np.array([s], np.float32)) for _, s in packs]
+    ys = [torch.full((M, N), float("nan"), device="cuda:0") for N, _ in shapes]
+    plan = tb.GroupedPlan(M, dx, dp, ds, ys, [N for N, _ in shapes], [K for _, K in shapes])
+    plan.run()
+    plan.run()
+    torch.cuda.synchronize()
+    for i, (N, K) in enumerate(shapes):
+        ref = oracle.ternary_matmul(xs[i], packs[i][0], packs[i][1], N)
+        assert_y_matches(ys[i].cpu().numpy(), ref["y"], M)
+
+
 @pytest.mark.parametrize("M,nchunks", [(40, 2), (300, 5), (1800, 7)])
 def test_grouped_overlap_matches_grouped(tb, M, nchunks):
     """The prefill grouped call with its quantization on a second stream gives
