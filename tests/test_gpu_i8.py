@@ -302,3 +302,90 @@ def test_i8_linear_rows_tall_tiles_sampled(tb):
     check_y_rows(y.cpu().numpy()[rows][:, cols].reshape(-1), y_ref, d, b[ns].astype(np.float64),
                  "tall tiles")
     assert not torch.isnan(y).any().item()
+
+
+# ---- larger ragged layers: every output against the oracle, and bit for bit
+# against the same call made on slices of the rows (rows are independent, so
+# any split of M must give the same bytes, whatever tiles each call uses).
+
+def _row_slices(tb, x, q, s, b, relu, rows_fn, K, N):
+    import torch
+    dev = "cuda:0"
+    M = x.shape[0]
+    cuts = [0, 1500, M] if M < 3000 else [0, 1500, 3000, M]
+    ys, accs = [], []
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        m = hi - lo
+        y = torch.full((m, N), float("nan"), device=dev)
+        acc = torch.empty((m, N), dtype=torch.int32, device=dev)
+        ws = torch.empty(tb.bitnet_i8_linear_workspace_bytes(m, K), dtype=torch.uint8, device=dev)
+        rows_fn(m, N, K, x[lo:hi], q, s, b, relu, y, ws, acc)
+        ys.append(y)
+        accs.append(acc)
+    return torch.cat(ys), torch.cat(accs)
+
+
+@pytest.mark.parametrize("M,N,K", [(2085, 300, 768), (2048, 1000, 256), (2085, 2048, 256),
+                                   (4100, 72, 2048)])
+@pytest.mark.parametrize("bias_on,relu", [(True, True), (False, False)])
+def test_i8_linear_large_ragged_parity(tb, M, N, K, bias_on, relu):
+    import torch
+    say(f"[i8] large layer M={M} N={N} K={K} bias={bias_on} relu={relu}")
+    dev = "cuda:0"
+    seed = M + 3 * N + 5 * K
+    x = synth.activations(M, K, seed)
+    x[M // 3] = 0
+    W = synth.normal_weights(N, K, seed + 1)
+    rng = np.random.default_rng(seed)
+    b = (rng.standard_normal(N, dtype=np.float32) * np.float32(0.1)) if bias_on else None
+    q, s = oracle.i8_quant_weights(W)
+    ref = oracle.i8_linear(x, q, s, b, relu)
+    qd = torch.from_numpy(q).to(dev)
+    sd = torch.tensor([s], dtype=torch.float32, device=dev)
+    bd = torch.from_numpy(b).to(dev) if b is not None else None
+    xd = torch.from_numpy(x).to(dev)
+    ybuf = torch.full((M * N + 64,), float("nan"), device=dev)
+    y = ybuf[:M * N].view(M, N)
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev)
+    ws = torch.empty(tb.bitnet_i8_linear_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    tb.bitnet_i8_linear_into(M, N, K, xd, qd, sd, bd, relu, y, ws, acc)
+    y2, acc2 = _row_slices(tb, xd, qd, sd, bd, relu, tb.bitnet_i8_linear_into, K, N)
+    torch.cuda.synchronize()
+    assert torch.isnan(ybuf[M * N:]).all().item(), "wrote past the end of y"
+    np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
+    d = ref["acc"].astype(np.float64) * np.float64(s) / ref["x_scale"].astype(np.float64)[:, None]
+    bias_vals = np.zeros(N) if b is None else np.broadcast_to(b.astype(np.float64), (M, N))
+    check_y(y.cpu().numpy(), ref["y"], d, bias_vals, f"M={M} N={N} K={K}")
+    assert torch.equal(acc, acc2)
+    assert torch.equal(y, y2), "the whole call and its row slices differ"
+
+
+@pytest.mark.parametrize("M,N,K", [(2085, 520, 1024), (2048, 2048, 512)])
+def test_i8_linear_rows_large_ragged_parity(tb, M, N, K):
+    """Per-channel scales on larger ragged layers, a zero weight channel
+    included; against the oracle and against row slices of the same call."""
+    import torch
+    say(f"[i8 rows] large layer M={M} N={N} K={K}")
+    dev = "cuda:0"
+    seed = 2 * M + N + K
+    x = synth.activations(M, K, seed)
+    W = synth.student_t_weights(N, K, seed + 1)
+    W[N // 3] = 0
+    b = np.random.default_rng(seed).standard_normal(N, dtype=np.float32) * np.float32(0.1)
+    q, s = oracle.rowq_quant_weights(W)
+    ref = oracle.i8_linear_rows(x, q, s, b, True)
+    qd, sd = torch.from_numpy(q).to(dev), torch.from_numpy(s).to(dev)
+    bd, xd = torch.from_numpy(b).to(dev), torch.from_numpy(x).to(dev)
+    y = torch.full((M, N), float("nan"), device=dev)
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev)
+    ws = torch.empty(tb.bitnet_i8_linear_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    tb.bitnet_i8_linear_rows_into(M, N, K, xd, qd, sd, bd, True, y, ws, acc)
+    y2, acc2 = _row_slices(tb, xd, qd, sd, bd, True, tb.bitnet_i8_linear_rows_into, K, N)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), ref["acc"])
+    d = (ref["acc"].astype(np.float64) * s.astype(np.float64)[None, :]
+         / ref["x_scale"].astype(np.float64)[:, None])
+    check_y_rows(y.cpu().numpy(), ref["y"], d, np.broadcast_to(b.astype(np.float64), (M, N)),
+                 f"M={M} N={N} K={K}")
+    assert torch.equal(acc, acc2)
+    assert torch.equal(y, y2), "the whole call and its row slices differ"
