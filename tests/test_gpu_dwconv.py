@@ -79,3 +79,11 @@ def test_dwconv_zero_column_and_channel(tb):
 def test_dwconv_encoder_size(tb):
     say("[dwconv] encoder stand-in B=1 T=8192 C=512 k=7")
     run_case(tb, 1, 8192, 512, 7, True, False, seed=70100)
+
+
+@pytest.mark.parametrize("B,T,C,k", [(2, 8392, 64, 3), (1, 20000, 64, 7)])
+def test_dwconv_long_sequence(tb, B, T, C, k):
+    """Sequences longer than 64 chunks of 128 frames: the column maxima use
+    chunks of 256 (8392 frames, 33 chunks) and 512 frames (20000, 40 chunks)."""
+    say(f"[dwconv] long sequence B={B} T={T} C={C} k={k}")
+    run_case(tb, B, T, C, k, True, True, seed=B * 7 + T)
