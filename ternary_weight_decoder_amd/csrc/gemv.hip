@@ -205,6 +205,47 @@ __device__ __forceinline__ void quant_rows_batched(const GemvProblem &p, GemvSha
   __syncthreads();
 }
 
+// A single row already held in registers (loaded by load_row_batch before the
+// workgroup's first weight loads): one absmax reduction, then the quantized
+// row, its scale and its row sum go to LDS.  Positions past the row hold zeros.
+__device__ __forceinline__ void quant_row_resident(const GemvProblem &p, GemvShared &sh,
+                                                   int8_t *xq_lds, bool write_out,
+                                                   const f32x4 (&v)[kQuantBatch]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n4 = p.K >> 2;
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kQuantBatch; ++j)
+    a = fmaxf(a, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+  a = wave_max(a);
+  if (lane == 0) sh.red[0][wave] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(sh.red[0][0], sh.red[0][1]), fmaxf(sh.red[0][2], sh.red[0][3]));
+  const float s = (a == 0.0f) ? 1.0f : 127.0f / a;
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < kQuantBatch; ++j) {
+    const int i = j * kThreads + tid;
+    if (i < n4) {
+      const int q0 = quant_one(v[j].x, s), q1 = quant_one(v[j].y, s);
+      const int q2 = quant_one(v[j].z, s), q3 = quant_one(v[j].w, s);
+      sum += q0 + q1 + q2 + q3;
+      const uint32_t w = pack4_i8(q0, q1, q2, q3);
+      *reinterpret_cast<uint32_t *>(xq_lds + perm_offset(4 * i)) = w;
+      if (write_out) st_global<uint32_t>(p.xq_out + 4 * i, w);
+    }
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) sh.ired[0][wave] = sum;
+  if (tid == 0) {
+    sh.scale[0] = s;
+    if (write_out) st_global<float>(p.x_scale_out, s);
+  }
+  __syncthreads();
+  if (tid == 0) sh.rowsum[0] = sh.ired[0][0] + sh.ired[0][1] + sh.ired[0][2] + sh.ired[0][3];
+  __syncthreads();
+}
+
 template <bool BATCHED>
 __device__ __forceinline__ void quant_rows_to_lds(const GemvProblem &p, GemvShared &sh,
                                                   int8_t *xq_lds, bool write_out) {
@@ -282,10 +323,24 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, bool s
     ++lu;
   };
   if (!FUSED) stage_chunk(0);
+  // A single fused row is loaded whole before the weights: the loads of one
+  // wave complete in issue order, so a row loaded after the weight ring could
+  // only be used once the ring's HBM reads had landed.
+  const bool resident = FUSED && p.M == 1 && (p.K >> 2) <= kQuantBatch * kThreads;
+  f32x4 xv[kQuantBatch];
+  if (resident)
+    load_row_batch(make_rsrc(p.x, (uint32_t)p.K * 4u), p.K >> 2, 0, xv);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < D; ++j) load_item(wr[j]);
 
-  if (FUSED) quant_rows_to_lds<SMALL>(p, sh, lds, p.xq_out != nullptr && blk == 0);
+  if (FUSED) {
+    const bool out = p.xq_out != nullptr && blk == 0;
+    if (resident)
+      quant_row_resident(p, sh, lds, out, xv);
+    else
+      quant_rows_to_lds<SMALL>(p, sh, lds, out);
+  }
 
   // Dequantization inputs of accumulator element r of this lane (row 4h + r).
   const float ws = ld_global<float>(p.w_scale);

@@ -154,6 +154,69 @@ __device__ __forceinline__ void lm_quant_rows(const LmParams &p, LmShared &sh, i
   __syncthreads();
 }
 
+// The same from rows already held in registers: the M rows as one flat run of
+// M*K/4 fp32 quads, thread t holding quads t, t + kThreads, ... (NQ of them,
+// zeros past the run), loaded by lm_load_rows before the workgroup's first
+// table loads.  The loads of a wave complete in issue order, so rows loaded
+// after the table ring could only be used once the ring's HBM reads had
+// landed, and every further pass over the rows would then run with the ring
+// full and the table stream stalled.  sh.amax must be zero before the call.
+template <int NQ>
+__device__ __forceinline__ void lm_load_rows(const LmParams &p, f32x4 (&v)[NQ]) {
+  const uint32_t total = (uint32_t)p.M * (uint32_t)(p.K >> 2);
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(p.x, total * 16u);
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) {
+    const uint32_t e = (uint32_t)(u * kThreads) + threadIdx.x;
+    v[u] = __builtin_bit_cast(
+        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (e < total ? e : total) * 16u, 0, 0));
+  }
+}
+
+template <int NQ>
+__device__ __forceinline__ void lm_quant_resident(const LmParams &p, LmShared &sh, int8_t *xq,
+                                                  bool write_out, const f32x4 (&v)[NQ]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n4 = p.K >> 2;
+  const int total = p.M * n4;
+  const int stride = p.K + kRowPad;
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) {
+    const int w0 = u * kThreads + 64 * wave;   // first quad of this wave
+    if (w0 >= total) break;
+    const int e = w0 + lane;
+    float a = fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w)));
+    const int m0 = w0 / n4, m1 = min(w0 + 63, total - 1) / n4;
+    if (m0 == m1) {
+      a = wave_max(a);
+      if (lane == 0) atomicMax(&sh.amax[m0], __builtin_bit_cast(uint32_t, a));
+    } else if (e < total) {
+      atomicMax(&sh.amax[e / n4], __builtin_bit_cast(uint32_t, a));
+    }
+  }
+  __syncthreads();
+  if (tid < p.M) {
+    const float a = __builtin_bit_cast(float, sh.amax[tid]);
+    const float s = (a == 0.0f) ? 1.0f : 127.0f / a;
+    sh.scale[tid] = s;
+    if (write_out) st_global<float>(p.x_scale_out + tid, s);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) {
+    const int e = u * kThreads + tid;
+    if (e < total) {
+      const int m = e / n4, i = e - m * n4;
+      const float s = sh.scale[m];
+      const uint32_t w = pack4_i8(quant_one(v[u].x, s), quant_one(v[u].y, s),
+                                  quant_one(v[u].z, s), quant_one(v[u].w, s));
+      *reinterpret_cast<uint32_t *>(xq + (size_t)m * stride + 4 * i) = w;
+      if (write_out) st_global<uint32_t>(p.xq_out + 4 * (size_t)e, w);
+    }
+  }
+  __syncthreads();
+}
+
 // Dynamic LDS of one workgroup: the quantized rows [M][K + kRowPad], then per
 // wave the column scales of its run [kMaxBpw * 16] and its int32 accumulators
 // [bpw][M][16].  The outputs are dequantized and stored after the loop, so
@@ -168,7 +231,9 @@ __host__ __device__ inline size_t lm_wave_bytes(int M, int bpw) {
   return (size_t)kMaxBpw * 16 * 4 + (size_t)bpw * 16 * 4 * M;
 }
 
-template <int D>
+// NQ > 0: the rows fit NQ quads per thread and are held in registers
+// (lm_load_rows / lm_quant_resident); NQ = 0: two batched passes over them.
+template <int D, int NQ>
 __global__ void __launch_bounds__(kThreads) lm_head_kernel(LmParams p) {
   __shared__ LmShared sh;
   extern __shared__ __attribute__((aligned(16))) int8_t lds[];
@@ -207,6 +272,12 @@ __global__ void __launch_bounds__(kThreads) lm_head_kernel(LmParams p) {
     }
     ++fetched;
   };
+  f32x4 xv[NQ > 0 ? NQ : 1];
+  if constexpr (NQ > 0) {
+    if (threadIdx.x < p.M) sh.amax[threadIdx.x] = 0u;
+    lm_load_rows<NQ>(p, xv);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   v4i wr[D][4];
 #pragma unroll
   for (int d = 0; d < D; ++d) load_item(wr[d]);
@@ -219,7 +290,12 @@ __global__ void __launch_bounds__(kThreads) lm_head_kernel(LmParams p) {
     sv[t] = (i < nb * 16 && n < p.V) ? ld_global<float>(p.w_scale + n) : 0.0f;
   }
 
-  lm_quant_rows(p, sh, xq_lds, p.xq_out != nullptr && blockIdx.x == 0);
+  if constexpr (NQ > 0) {
+    __syncthreads();   // sh.amax cleared
+    lm_quant_resident<NQ>(p, sh, xq_lds, p.xq_out != nullptr && blockIdx.x == 0, xv);
+  } else {
+    lm_quant_rows(p, sh, xq_lds, p.xq_out != nullptr && blockIdx.x == 0);
+  }
   // (Written unconditionally: a load whose value some path leaves unused
   // would make the compiler wait for all loads at the top of the loop.)
 #pragma unroll
@@ -406,7 +482,19 @@ hipError_t launch_lm_head(int M, int V, int K, const float *x, const int8_t *q,
   p.blocks_per_wave = lm_bpw(M, V, K);
   const int waves = (p.nblk + p.blocks_per_wave - 1) / p.blocks_per_wave;
   const int blocks = (waves + kWaves - 1) / kWaves;
-  lm_head_kernel<kDepth><<<blocks, kThreads, lm_head_lds_bytes(M, V, K), stream>>>(p);
+  // Quads of the rows per thread, held in registers when they fit.
+  const int64_t nq = ((int64_t)M * (K >> 2) + kThreads - 1) / kThreads;
+  const size_t lds = lm_head_lds_bytes(M, V, K);
+  if (nq <= 2)
+    lm_head_kernel<kDepth, 2><<<blocks, kThreads, lds, stream>>>(p);
+  else if (nq <= 6)
+    lm_head_kernel<kDepth, 6><<<blocks, kThreads, lds, stream>>>(p);
+  else if (nq <= 12)
+    lm_head_kernel<kDepth, 12><<<blocks, kThreads, lds, stream>>>(p);
+  else if (nq <= 24)
+    lm_head_kernel<kDepth, 24><<<blocks, kThreads, lds, stream>>>(p);
+  else
+    lm_head_kernel<kDepth, 0><<<blocks, kThreads, lds, stream>>>(p);
   return hipGetLastError();
 }
 
