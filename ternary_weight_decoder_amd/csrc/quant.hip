@@ -25,6 +25,23 @@ constexpr int kBlockVec = 10;                     // f32x4 per thread, workgroup
 constexpr int kWaveMaxK = 64 * 4 * kWaveVec;      // 2048
 constexpr int kBlockMaxK = kQuantThreads * 4 * kBlockVec;   // 10240
 
+// Row loads.  NT: non-temporal, for the grouped launches that feed the GEMM
+// (M > 16), whose fp32 rows are read once and would otherwise displace the
+// int8 rows that the contraction launch reads next.  The decode launches
+// (M <= 16) keep plain loads, which measured faster there.
+template <bool NT>
+__device__ __forceinline__ f32x4 ld_row(const f32x4 *p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load((const BITNET_GLOBAL f32x4 *)p);
+  else
+    return ld_global<f32x4>(p);
+}
+
+// Rows of a grouped launch from which its row loads are non-temporal.
+#ifndef BITNET_QUANT_NT_MINM
+#define BITNET_QUANT_NT_MINM 17
+#endif
+
 struct RowOut {
   int8_t *nat;        // natural order row, may be null
   int8_t *perm;       // permuted row, may be null
@@ -62,6 +79,7 @@ __device__ __forceinline__ void store_row_meta(const RowOut &o, float s, int sum
 
 // One wave, one row of K <= kWaveMaxK values (K % 4 == 0; the permuted row
 // needs K % 128 == 0).
+template <bool NT = false>
 __device__ __forceinline__ void quant_row_wave(const float *__restrict__ xr, int K,
                                                const RowOut &o) {
   const int lane = threadIdx.x & 63;
@@ -72,7 +90,7 @@ __device__ __forceinline__ void quant_row_wave(const float *__restrict__ xr, int
 #pragma unroll
   for (int j = 0; j < kWaveVec; ++j) {
     const int i = lane + 64 * j;
-    v[j] = i < n4 ? ld_global<f32x4>(x4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+    v[j] = i < n4 ? ld_row<NT>(x4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int j = 0; j < kWaveVec; ++j) a = fmaxf(a, absmax4(v[j]));
@@ -105,6 +123,7 @@ __device__ __forceinline__ void block_finish(int sum, float s, const RowOut &o, 
 
 // One workgroup, one row of any K (K % 4 == 0; the permuted row needs
 // K % 128 == 0).  Whole workgroup, uniform.
+template <bool NT = false>
 __device__ __forceinline__ void quant_row_block(const float *__restrict__ xr, int K,
                                                 const RowOut &o, QuantShared &sh) {
   const int tid = threadIdx.x;
@@ -117,7 +136,7 @@ __device__ __forceinline__ void quant_row_block(const float *__restrict__ xr, in
 #pragma unroll
     for (int j = 0; j < kBlockVec; ++j) {
       const int i = tid + kQuantThreads * j;
-      v[j] = i < n4 ? ld_global<f32x4>(x4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+      v[j] = i < n4 ? ld_row<NT>(x4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int j = 0; j < kBlockVec; ++j) a = fmaxf(a, absmax4(v[j]));
@@ -137,7 +156,7 @@ __device__ __forceinline__ void quant_row_block(const float *__restrict__ xr, in
 #pragma unroll
     for (int j = 0; j < kBlockVec; ++j) {
       const int i = c0 + tid + kQuantThreads * j;
-      v[j] = i < n4 ? ld_global<f32x4>(x4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+      v[j] = i < n4 ? ld_row<NT>(x4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int j = 0; j < kBlockVec; ++j) a = fmaxf(a, absmax4(v[j]));
@@ -148,7 +167,7 @@ __device__ __forceinline__ void quant_row_block(const float *__restrict__ xr, in
 #pragma unroll
     for (int j = 0; j < kBlockVec; ++j) {
       const int i = c0 + tid + kQuantThreads * j;
-      v[j] = i < n4 ? ld_global<f32x4>(x4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+      v[j] = i < n4 ? ld_row<NT>(x4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int j = 0; j < kBlockVec; ++j) {
@@ -213,6 +232,7 @@ __global__ void __launch_bounds__(kQuantThreads)
 // Grouped: workgroups [wg_end[s-1], wg_end[s]) quantize the M rows of problem
 // order[s] into its workspace, four rows per workgroup when K <= kWaveMaxK and
 // one row per workgroup otherwise.
+template <bool NT>
 __global__ void __launch_bounds__(kQuantThreads)
     quant_grouped_kernel(const bitnet_problem *__restrict__ problems, QuantTable tab,
                          uint8_t *__restrict__ workspace) {
@@ -236,11 +256,11 @@ __global__ void __launch_bounds__(kQuantThreads)
   if (K <= kWaveMaxK) {
     const int row = (int)local * kRowsPerBlock + (threadIdx.x >> 6);
     if (row >= M) return;
-    quant_row_wave(pr.x + (size_t)row * K, K, row_out(nullptr, xq, xs, nullptr, rs, row, K));
+    quant_row_wave<NT>(pr.x + (size_t)row * K, K, row_out(nullptr, xq, xs, nullptr, rs, row, K));
   } else {
     const int row = (int)local;
-    quant_row_block(pr.x + (size_t)row * K, K, row_out(nullptr, xq, xs, nullptr, rs, row, K),
-                    sh);
+    quant_row_block<NT>(pr.x + (size_t)row * K, K,
+                        row_out(nullptr, xq, xs, nullptr, rs, row, K), sh);
   }
 }
 
@@ -273,8 +293,11 @@ int64_t quant_grouped_blocks(int64_t M, int64_t K) {
 
 hipError_t launch_quant_grouped(const bitnet_problem *problems, const QuantTable &tab,
                                 uint8_t *workspace, hipStream_t stream) {
-  quant_grouped_kernel<<<tab.wg_end[tab.count - 1], kQuantThreads, 0, stream>>>(problems, tab,
-                                                                                 workspace);
+  const unsigned blocks = tab.wg_end[tab.count - 1];
+  if (tab.M >= BITNET_QUANT_NT_MINM)
+    quant_grouped_kernel<true><<<blocks, kQuantThreads, 0, stream>>>(problems, tab, workspace);
+  else
+    quant_grouped_kernel<false><<<blocks, kQuantThreads, 0, stream>>>(problems, tab, workspace);
   return hipGetLastError();
 }
 
