@@ -598,8 +598,8 @@ def prefill_config(torch, tb, synth, timer, problems, packed, w_scales, M, dev, 
     ys = [torch.empty((M, p.N), device=dev) for p in problems]
     plan = tb.GroupedPlan(M, xs, packed, w_scales, ys, [p.N for p in problems],
                           [p.K for p in problems])
-    steps = 5 if M > 1000 else 10
-    ms = timer.time(lambda i=0: plan.run(), steps, warmup=5)
+    steps = 30 if M > 1000 else 100
+    ms = timer.time(lambda i=0: plan.run(), steps, warmup=10 if M > 1000 else 20)
     ops = 2.0 * M * sum(p.N * p.K for p in problems)
     res = {"ms_per_step": round(ms, 4), "int8_TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
            "frac_of_int8_peak": round(ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
@@ -612,7 +612,7 @@ def prefill_config(torch, tb, synth, timer, problems, packed, w_scales, M, dev, 
     aux = torch.cuda.Stream()
     overlap = {}
     for nch in OVERLAP_CHUNKS:
-        ms_o = timer.time(lambda i=0: plan.run_overlap(aux, nch), steps, warmup=3)
+        ms_o = timer.time(lambda i=0: plan.run_overlap(aux, nch), steps, warmup=5)
         overlap[str(nch)] = round(ms_o, 4)
     best = min(overlap, key=overlap.get)
     ms_b = overlap[best]
@@ -627,8 +627,8 @@ def prefill_config(torch, tb, synth, timer, problems, packed, w_scales, M, dev, 
         zc = [torch.full_like(t, 0x55) for t in packed]
         zplan = tb.GroupedPlan(M, xs, zc, w_scales, ys, [p.N for p in problems],
                                [p.K for p in problems])
-        ms_z = timer.time(lambda i=0: zplan.run(), steps, warmup=3)
-        ms_r = timer.time(lambda i=0: plan.run(), steps, warmup=3)
+        ms_z = timer.time(lambda i=0: zplan.run(), steps, warmup=5)
+        ms_r = timer.time(lambda i=0: plan.run(), steps, warmup=5)
         res["code_independence"] = {"ms_per_step_all_zero_codes": round(ms_z, 4),
                                     "ms_per_step_these_codes": round(ms_r, 4)}
         del zc, zplan
@@ -673,7 +673,7 @@ def prefill_shapes_config(torch, tb, timer, problems, packed, w_scales, M, dev):
         ys = [torch.empty((M, N), device=dev) for _ in idx]
         plan = tb.GroupedPlan(M, xs, [packed[i] for i in idx], [w_scales[i] for i in idx], ys,
                               [N] * n, [K] * n)
-        ms_g = timer.time(lambda i=0: plan.run(), 10 if M > 1000 else 40, warmup=5)
+        ms_g = timer.time(lambda i=0: plan.run(), 30 if M > 1000 else 100, warmup=10)
         xq, xsc = tb.bitnet_quant_act(xs[0])
         ws = torch.empty(tb.bitnet_matmul_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
         ms_1 = timer.time(lambda i=0: tb.bitnet_ternary_matmul_q8_into(

@@ -25,10 +25,11 @@ constexpr int kBlockVec = 10;                     // f32x4 per thread, workgroup
 constexpr int kWaveMaxK = 64 * 4 * kWaveVec;      // 2048
 constexpr int kBlockMaxK = kQuantThreads * 4 * kBlockVec;   // 10240
 
-// Row loads.  NT: non-temporal, for the grouped launches that feed the GEMM
-// (M > 16), whose fp32 rows are read once and would otherwise displace the
-// int8 rows that the contraction launch reads next.  The decode launches
-// (M <= 16) keep plain loads, which measured faster there.
+// Row loads.  NT: non-temporal, for the prefill-sized grouped launches
+// (M > 64), whose fp32 rows are read once and would otherwise displace the
+// int8 rows that the contraction launch reads next.  Decode and batched-decode
+// launches (M <= 64), which stream their weights from HBM beside these rows,
+// keep plain loads: they measured faster there.
 template <bool NT>
 __device__ __forceinline__ f32x4 ld_row(const f32x4 *p) {
   if constexpr (NT)
@@ -39,7 +40,7 @@ __device__ __forceinline__ f32x4 ld_row(const f32x4 *p) {
 
 // Rows of a grouped launch from which its row loads are non-temporal.
 #ifndef BITNET_QUANT_NT_MINM
-#define BITNET_QUANT_NT_MINM 17
+#define BITNET_QUANT_NT_MINM 65
 #endif
 
 struct RowOut {
