@@ -40,6 +40,9 @@ __device__ __forceinline__ void st_global(void *p, T v) {
 constexpr int vmcnt_wait(int n) {
   return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8);
 }
+// The same for the LDS / scalar-memory counter alone (vmcnt left at its
+// maximum, 63, which never waits).
+constexpr int lgkmcnt_wait(int n) { return 0xf | (0x3 << 14) | (0x7 << 4) | ((n & 0xf) << 8); }
 
 // Raw buffer resource over `bytes` bytes at `base` (stride 0; the 32-bit data
 // format that untyped buffer loads need on gfx9-family parts).  A load whose

@@ -183,12 +183,21 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
 #pragma unroll
   for (int e = 0; e < 4; ++e) a_rd[e] = li * 128 + (((4 * lh + e) ^ swz(li)) * 16);
 
-  // Per-row dequantization factors and row sums of the tile.
+  // Per-row dequantization factors and row sums of the tile.  Their loads go
+  // out first and their values go to LDS after the ring's first loads are
+  // issued, so the tile start waits for one memory round trip, not two.  (A
+  // wave's loads complete in issue order: waiting for these does not wait for
+  // the ring.)  The publishing barrier waits for LDS only; the ring's first
+  // units stay in flight until the K loop's own waits.
+  float xs_row = 1.0f, ws_all = 0.0f;
+  int rs_row = 0;
   if (tid < BM) {
     const int row = min(m0 + tid, p.M - 1);
-    sh.factor[tid] = ld_global<float>(p.w_scale) / ld_global<float>(p.x_scale + row);
-    sh.rowsum[tid] = ld_global<int>(p.rowsum + row);
+    ws_all = ld_global<float>(p.w_scale);
+    xs_row = ld_global<float>(p.x_scale + row);
+    rs_row = ld_global<int>(p.rowsum + row);
   }
+  __builtin_amdgcn_sched_barrier(0);
 
   v4i bq[kStages][CB];
 #pragma unroll
@@ -196,7 +205,15 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
     load_b(u, bq[u]);
     issue_dma(u, u);
   }
-  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+  if (tid < BM) {
+    sh.factor[tid] = ws_all / xs_row;
+    sh.rowsum[tid] = rs_row;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(lgkmcnt_wait(0));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 
   // Accumulators start at -rowsum of their row, which removes the +1 offset of
   // the code fields: element r of a 32x32 block sits at row 8*(r/4) + 4*(lane/32)
