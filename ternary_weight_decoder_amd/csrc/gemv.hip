@@ -52,13 +52,25 @@ namespace {
 #define BITNET_GEMV_AUX 2
 #endif
 constexpr int kGemvC = BITNET_GEMV_C;           // 16-column blocks per wave tile
+// With the rows staged from the workspace (M > 1), a ring of 2 units and
+// chunks of 4 units measured faster than 3 and 8 (M = 4: 66.9 -> 65.9 us per
+// 196-projection sweep, M = 16: 85.7 -> 83.5 us); a ring of 1 unit, chunks of
+// 16 units, 4-unit rings and 32-column wave tiles were slower.
+#ifndef BITNET_GEMV_DEPTH_STAGED
+#define BITNET_GEMV_DEPTH_STAGED 2
+#endif
 constexpr int kGemvDepth = BITNET_GEMV_DEPTH;   // items in flight per wave
+constexpr int kGemvDepthStaged = BITNET_GEMV_DEPTH_STAGED;   // the same, rows staged
 constexpr int kWeightAux = BITNET_GEMV_AUX;     // cache-policy bits of weight loads
 constexpr int kWaveCols = 16 * kGemvC;          // columns of one wave tile
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kChunkUnits = 8;                   // units per staged activation chunk
+#ifndef BITNET_GEMV_CHUNK
+#define BITNET_GEMV_CHUNK 4
+#endif
+constexpr int kChunkUnits = BITNET_GEMV_CHUNK;   // units per staged activation chunk
 constexpr int kChunkBytes = kChunkUnits * kGemvMaxM * kUnit;   // 16 rows per unit
+static_assert(kChunkUnits % 4 == 0, "each of the four waves stages whole units");
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 // 16-byte chunk position of chunk c in staged row r: pairs of rows share a
@@ -265,7 +277,7 @@ template <bool FUSED, bool SMALL>
 __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, bool split,
                                            GemvShared &sh, int8_t *lds) {
   constexpr int C = kGemvC;
-  constexpr int D = kGemvDepth;
+  constexpr int D = FUSED ? kGemvDepth : kGemvDepthStaged;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
@@ -286,7 +298,8 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, bool s
   const int lane_col0 = (blk * G + cgrp) * kWaveCols + col;   // column of block 0
 
   // Staging: chunk k of the rows goes to LDS buffer k % 2; wave w copies units
-  // 2w and 2w + 1 of the chunk, 8 rows per 1 KB load: lane i takes row
+  // kChunkUnits / 4 * w .. + kChunkUnits / 4 - 1 of the chunk, 8 rows per
+  // 1 KB load: lane i takes row
   // 8q + i / 8 of load q and lands at chunk position i % 8, so it fetches
   // chunk stage_pos(i % 8, row) of that row.  Rows past M and units past K
   // are aimed beyond the buffer and land as zeros.
@@ -294,8 +307,8 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, bool s
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(FUSED ? nullptr : p.xqp, FUSED ? 0 : a_bytes);
   auto stage_chunk = [&](int k) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int j = 2 * wave + (q >> 1);             // unit within the chunk
+    for (int q = 0; q < kChunkUnits / 2; ++q) {
+      const int j = (kChunkUnits / 4) * wave + (q >> 1);   // unit within the chunk
       const int row = 8 * (q & 1) + (lane >> 3);
       const int u = k * kChunkUnits + j;
       const int chunk = stage_pos(lane & 7, row);
