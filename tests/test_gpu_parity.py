@@ -427,6 +427,40 @@ def test_grouped_large_ragged_parity(tb, M):
         assert_y_matches(ys[i].cpu().numpy(), ref["y"], M)
 
 
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_grouped_staged_decode_parity(tb, M):
+    """Decode calls of 2 to 4 rows whose longest projection puts M * K above
+    the in-workgroup quantization limit, so every projection's rows come from
+    the quantization launch and are staged through LDS: 96 ragged projections
+    with K from 128 (rows shorter than one staged chunk) to 8960, two of them
+    sharing an input; two calls in a row; every output against the oracle,
+    bit for bit."""
+    import torch
+    say(f"[grouped] staged decode, 96 ragged projections, M={M}")
+    rng = np.random.default_rng(970 + M)
+    shapes = [(int(rng.choice([72, 200, 1000, 1536, 2600])),
+               int(rng.choice([128, 384, 1536, 1664, 4608, 8960]))) for _ in range(96)]
+    shapes[0] = (1536, 8960)   # M * K above the in-workgroup limit at every M here
+    shapes[1] = (520, 1536)
+    shapes[2] = (200, 1536)    # shares problem 1's input
+    Ws = [synth.normal_weights(N, K, seed=13000 + i) for i, (N, K) in enumerate(shapes)]
+    xs = [synth.activations(M, K, seed=14000 + i) for i, (N, K) in enumerate(shapes)]
+    xs[2] = xs[1]
+    packs = [oracle.ternarize_pack(W) for W in Ws]
+    dx = [dev_tensor(x) for x in xs]
+    dx[2] = dx[1]
+    dp = [dev_tensor(p) for p, _ in packs]
+    ds = [dev_tensor(np.array([s], np.float32)) for _, s in packs]
+    ys = [torch.full((M, N), float("nan"), device="cuda:0") for N, _ in shapes]
+    plan = tb.GroupedPlan(M, dx, dp, ds, ys, [N for N, _ in shapes], [K for _, K in shapes])
+    plan.run()
+    plan.run()
+    torch.cuda.synchronize()
+    for i, (N, K) in enumerate(shapes):
+        ref = oracle.ternary_matmul(xs[i], packs[i][0], packs[i][1], N)
+        assert_y_matches(ys[i].cpu().numpy(), ref["y"], M)
+
+
 @pytest.mark.parametrize("M,nchunks", [(40, 2), (300, 5), (1800, 7)])
 def test_grouped_overlap_matches_grouped(tb, M, nchunks):
     """The prefill grouped call with its quantization on a second stream gives
