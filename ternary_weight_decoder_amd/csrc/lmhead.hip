@@ -33,8 +33,9 @@
 // of the quantized rows in LDS, so both operands of every MFMA agree on k;
 // padding inputs carry zero codes.  Loads past the wave's run are aimed beyond
 // the buffer and return zeros without a memory access.  The workgroup
-// quantizes the rows into LDS itself, after issuing the first D items, so the
-// first table loads overlap the quantization.
+// quantizes the rows into LDS itself: their loads are issued before the first
+// D items, so the table loads overlap the quantization, and waiting for the
+// rows does not wait for the table's HBM reads.
 #include <algorithm>
 
 #include "bitnet_device.hpp"
