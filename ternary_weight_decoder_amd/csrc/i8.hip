@@ -13,14 +13,17 @@
 // Weights are quantized once, offline, with one absmax scale per tensor.
 //
 // GEMM.  Workgroup tile 64 (or 128) x 128, 4 waves in a 2 x 2 arrangement,
-// each wave 32 (64) x 64 as blocks of 32 x 32.  K advances 64 inputs per step:
-// the activation tile (BM rows x 64 int8) and the weight tile (128 rows x 64
-// int8) go straight from memory into LDS (buffer_load ... lds), into a ring of
-// three stages issued two steps ahead; rows past M or N load as zeros.  Inside
-// a stage, 16-byte chunk c of tile row r sits at position c ^ ((r / 4) % 4), so
-// the operand reads of 16 consecutive rows hit 16 different bank groups.  Lane
-// (i = lane % 32, h = lane / 32) feeds k-step s of a stage with chunk 2s + h of
-// its A row and of its B row, so the k positions of both operands agree.
+// each wave 32 (64) x 64 as blocks of 32 x 32.  K advances KB = 128 inputs per
+// step on long rows (K >= 1024, K % 128 == 0), else 64: the activation tile (BM rows x KB int8) and
+// the weight tile (128 rows x KB int8) go straight from memory into LDS
+// (buffer_load ... lds), into a ring of two stages issued one step ahead (KB =
+// 128) or three stages issued two steps ahead (KB = 64), so 128 inputs are in
+// flight either way; rows past M or N load as zeros.  With 128-input steps
+// every row of a tile takes whole 128-byte lines.  Inside a stage, 16-byte chunk c of tile row r
+// sits at position c ^ swz(r), so the operand reads of 16 consecutive rows hit
+// 16 different bank groups.  Lane (i = lane % 32, h = lane / 32) feeds k-step s
+// of a stage with chunk 2s + h of its A row and of its B row, so the k
+// positions of both operands agree.
 // Tiles are dealt to the eight XCDs by row block (block b runs on XCD b % 8),
 // so the workgroups that read one block of activation rows share one L2.
 #include <algorithm>
@@ -32,26 +35,45 @@
 namespace bitnet {
 namespace {
 
+// LDS stages: 0 picks 2 for 128-input steps and 3 for 64-input steps.
 #ifndef BITNET_I8_RING
-#define BITNET_I8_RING 3
+#define BITNET_I8_RING 0
+#endif
+// Steps of 128 inputs for K % 128 == 0 and K >= BITNET_I8_WIDE_MINK (else 64).
+// Measured on the 8192-frame encoder layers: K = 2048 32.1 -> 30.3 us per
+// call with 128-input steps, K = 512 27.9 -> 28.3 us (kept at 64).
+#ifndef BITNET_I8_WIDE
+#define BITNET_I8_WIDE 1
+#endif
+#ifndef BITNET_I8_WIDE_MINK
+#define BITNET_I8_WIDE_MINK 1024
 #endif
 constexpr int kThreads = 256;
 constexpr int kBN = 128;
-constexpr int kKB = 64;                 // inputs per K step
-constexpr int kRing = BITNET_I8_RING;   // LDS stages
+template <int KB>
+constexpr int ring_stages() {
+  return BITNET_I8_RING > 0 ? BITNET_I8_RING : (KB == 128 ? 2 : 3);
+}
 constexpr int kStoreAux = 2;            // outputs are not read again here: non-temporal
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 // Tile height BM = 128 or 64: the 4 waves sit 2 x 2, each owning BM/2 rows
-// (BM/64 blocks of 32) and 64 columns (2 blocks of 32).
-template <int BM>
+// (BM/64 blocks of 32) and 64 columns (2 blocks of 32).  KB inputs per step.
+template <int BM, int KB, int kRing = ring_stages<KB>()>
 struct I8Shared {
-  __attribute__((aligned(16))) int8_t a[kRing][BM * kKB];
-  __attribute__((aligned(16))) int8_t b[kRing][kBN * kKB];
+  __attribute__((aligned(16))) int8_t a[kRing][BM * KB];
+  __attribute__((aligned(16))) int8_t b[kRing][kBN * KB];
   __attribute__((aligned(16))) float factor[BM];
 };
 
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+// Chunk position of tile row r.  A ds_read_b128 serves 16 lanes (16
+// consecutive rows, one chunk column) per cycle, and a 256-byte bank line holds
+// 256 / KB rows, so the rows that share a bank line, and the line groups,
+// need KB / 16 different positions.
+template <int KB>
+__device__ __forceinline__ int swz(int r) {
+  return (r / (256 / KB)) % (KB / 16);
+}
 
 // s_waitcnt immediate: at most n vector-memory operations outstanding and no
 // LDS operation (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
@@ -71,7 +93,7 @@ struct I8Params {
 
 // s_waitcnt for step u of the K loop: the loads of the `later` steps issued
 // after it (at most kRing - 2) may stay in flight, no LDS operation may.
-template <int kDmaPerWave>
+template <int kRing, int kDmaPerWave>
 __device__ __forceinline__ void wait_for_step(int later) {
   if (kRing >= 4 && later >= 2)
     __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_wait(2 * kDmaPerWave));
@@ -91,12 +113,16 @@ __device__ __forceinline__ float i8_out(float a, float c, float f, float b) {
   return v;
 }
 
-template <int BM, bool RELU, bool PERCOL>
+template <int BM, int KB, bool RELU, bool PERCOL>
 __global__ void __launch_bounds__(kThreads) i8_gemm_kernel(I8Params p) {
   constexpr int RB = BM / 64;            // 32-row blocks per wave
-  constexpr int kDmaA = BM / 64;         // 1 KB activation loads per wave and step
-  constexpr int kDmaPerWave = kDmaA + 2;
-  __shared__ I8Shared<BM> sh;
+  constexpr int kCh = KB / 16;           // 16-byte chunks per tile row
+  constexpr int kRowsPerDma = 64 / kCh;  // tile rows per 1 KB load
+  constexpr int kDmaA = BM / 4 / kRowsPerDma;   // activation loads per wave and step
+  constexpr int kDmaB = 32 / kRowsPerDma;       // weight loads per wave and step
+  constexpr int kDmaPerWave = kDmaA + kDmaB;
+  constexpr int kRing = ring_stages<KB>();
+  __shared__ I8Shared<BM, KB> sh;
   // Block b runs on XCD b % 8: XCD x takes row blocks x, x + 8, ... and every
   // column block of each.
   const int b = blockIdx.x, xcd = b & 7, j = b >> 3;
@@ -106,54 +132,55 @@ __global__ void __launch_bounds__(kThreads) i8_gemm_kernel(I8Params p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, lh = lane >> 5;
   const int wm = wave & 1, wn = wave >> 1;
-  const int steps = p.K / kKB;
+  const int steps = p.K / KB;
 
   // DMA: wave w fills activation rows [BM/4 w, BM/4 (w + 1)) and weight rows
-  // [32w, 32w + 32) with 1 KB loads; lane L of a load lands at position L % 4
-  // of tile row r = (first row of the load) + L / 4 and so fetches chunk
-  // (L % 4) ^ swz(r).
+  // [32w, 32w + 32) with 1 KB loads; lane L of a load lands at position
+  // L % kCh of tile row r = (first row of the load) + L / kCh and so fetches
+  // chunk (L % kCh) ^ swz(r).
   const uint32_t a_bytes = (uint32_t)((size_t)p.M * p.K);
   const uint32_t b_bytes = (uint32_t)((size_t)p.N * p.K);
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.xq, a_bytes);
   const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(p.q, b_bytes);
-  uint32_t a_off[kDmaA], b_off[2];
+  uint32_t a_off[kDmaA], b_off[kDmaB];
 #pragma unroll
   for (int q = 0; q < kDmaA; ++q) {
-    const int r = (BM / 4) * wave + 16 * q + (lane >> 2);
-    const int chunk = (lane & 3) ^ swz(r);
+    const int r = (BM / 4) * wave + kRowsPerDma * q + lane / kCh;
+    const int chunk = (lane % kCh) ^ swz<KB>(r);
     a_off[q] = m0 + r < p.M ? (uint32_t)(m0 + r) * p.K + 16 * chunk : a_bytes;
   }
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = 32 * wave + 16 * q + (lane >> 2);
-    const int chunk = (lane & 3) ^ swz(r);
+  for (int q = 0; q < kDmaB; ++q) {
+    const int r = 32 * wave + kRowsPerDma * q + lane / kCh;
+    const int chunk = (lane % kCh) ^ swz<KB>(r);
     b_off[q] = n0 + r < p.N ? (uint32_t)(n0 + r) * p.K + 16 * chunk : b_bytes;
   }
   // The step's K offset goes in the scalar offset; rows past M or N carry a
   // vector offset at the buffer's end, so they load zeros without a memory
   // access whatever the step.  Steps past K are never issued.
   auto issue = [&](int u, int slot) {
-    const uint32_t soff = (uint32_t)u * kKB;
+    const uint32_t soff = (uint32_t)u * KB;
 #pragma unroll
     for (int q = 0; q < kDmaA; ++q) {
       // (Through a local: a captured array element passed straight to the
       // builtin keeps this compiler's host pass from emitting the launch stub.)
       const uint32_t ao = a_off[q];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          a_rsrc, (lds_ptr_t)(&sh.a[slot][((BM / 4) * wave + 16 * q) * kKB]), 16, ao, soff, 0, 0);
+          a_rsrc, (lds_ptr_t)(&sh.a[slot][((BM / 4) * wave + kRowsPerDma * q) * KB]), 16, ao, soff,
+          0, 0);
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kDmaB; ++q) {
       const uint32_t bo = b_off[q];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          b_rsrc, (lds_ptr_t)(&sh.b[slot][(32 * wave + 16 * q) * kKB]), 16, bo, soff, 0, 0);
+          b_rsrc, (lds_ptr_t)(&sh.b[slot][(32 * wave + kRowsPerDma * q) * KB]), 16, bo, soff, 0, 0);
     }
   };
 
   // Operand reads: row (32 rb + li) of the wave's half, chunk 2s + lh.
-  uint32_t rd[2];
+  uint32_t rd[KB / 32];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) rd[s] = li * kKB + (((2 * s + lh) ^ swz(li)) * 16);
+  for (int s = 0; s < KB / 32; ++s) rd[s] = li * KB + (((2 * s + lh) ^ swz<KB>(li)) * 16);
 
   // Per-row dequantization factors of the tile (rows past M: any finite value).
   if (tid < BM) {
@@ -194,19 +221,19 @@ __global__ void __launch_bounds__(kThreads) i8_gemm_kernel(I8Params p) {
     // would see the new data.  Nothing is scheduled across this point, so
     // those reads and the MFMAs that use them stay on this side.
     __builtin_amdgcn_sched_barrier(0);
-    wait_for_step<kDmaPerWave>(min(kRing - 2, steps - 1 - u));
+    wait_for_step<kRing, kDmaPerWave>(min(kRing - 2, steps - 1 - u));
     __builtin_amdgcn_s_barrier();
     if (u + kRing - 1 < steps) issue(u + kRing - 1, (u + kRing - 1) % kRing);
     __builtin_amdgcn_sched_barrier(0);
-    const int8_t *as = sh.a[s] + (wm * (BM / 2)) * kKB;
-    const int8_t *bs = sh.b[s] + (wn * 64) * kKB;
+    const int8_t *as = sh.a[s] + (wm * (BM / 2)) * KB;
+    const int8_t *bs = sh.b[s] + (wn * 64) * KB;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < KB / 32; ++ks) {
       v4i av[RB], bv[2];
 #pragma unroll
-      for (int r = 0; r < RB; ++r) av[r] = *reinterpret_cast<const v4i *>(as + r * 32 * kKB + rd[ks]);
+      for (int r = 0; r < RB; ++r) av[r] = *reinterpret_cast<const v4i *>(as + r * 32 * KB + rd[ks]);
 #pragma unroll
-      for (int r = 0; r < 2; ++r) bv[r] = *reinterpret_cast<const v4i *>(bs + r * 32 * kKB + rd[ks]);
+      for (int r = 0; r < 2; ++r) bv[r] = *reinterpret_cast<const v4i *>(bs + r * 32 * KB + rd[ks]);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -354,17 +381,26 @@ hipError_t launch_i8_quant_weights(const float *W, int64_t N, int64_t K, int8_t 
   return hipGetLastError();
 }
 
+template <int KB, bool PERCOL>
+static void launch_i8_gemm_kb(const I8Params &p, bool tall, bool relu, unsigned grid,
+                              hipStream_t stream) {
+  if (tall && relu)
+    i8_gemm_kernel<128, KB, true, PERCOL><<<grid, kThreads, 0, stream>>>(p);
+  else if (tall)
+    i8_gemm_kernel<128, KB, false, PERCOL><<<grid, kThreads, 0, stream>>>(p);
+  else if (relu)
+    i8_gemm_kernel<64, KB, true, PERCOL><<<grid, kThreads, 0, stream>>>(p);
+  else
+    i8_gemm_kernel<64, KB, false, PERCOL><<<grid, kThreads, 0, stream>>>(p);
+}
+
 template <bool PERCOL>
 static hipError_t launch_i8_gemm_t(const I8Params &p, bool tall, bool relu, unsigned grid,
                                    hipStream_t stream) {
-  if (tall && relu)
-    i8_gemm_kernel<128, true, PERCOL><<<grid, kThreads, 0, stream>>>(p);
-  else if (tall)
-    i8_gemm_kernel<128, false, PERCOL><<<grid, kThreads, 0, stream>>>(p);
-  else if (relu)
-    i8_gemm_kernel<64, true, PERCOL><<<grid, kThreads, 0, stream>>>(p);
+  if (BITNET_I8_WIDE && p.K % 128 == 0 && p.K >= BITNET_I8_WIDE_MINK)
+    launch_i8_gemm_kb<128, PERCOL>(p, tall, relu, grid, stream);
   else
-    i8_gemm_kernel<64, false, PERCOL><<<grid, kThreads, 0, stream>>>(p);
+    launch_i8_gemm_kb<64, PERCOL>(p, tall, relu, grid, stream);
   return hipGetLastError();
 }
 

@@ -188,11 +188,13 @@ def test_i8_linear_short_tiles_many_workgroups(tb):
             "short tiles")
 
 
-def test_i8_linear_tall_tiles(tb):
-    """M = 16384, N = 4096, K = 64: 4096 tiles of 128 rows, the size from which
-    the call switches to 128-row tiles.  Sampled parity; no output left unwritten."""
+@pytest.mark.parametrize("K", [64, 1024])
+def test_i8_linear_tall_tiles(tb, K):
+    """M = 16384, N = 4096: 4096 tiles of 128 rows, the size from which the call
+    switches to 128-row tiles, with steps of 64 (K = 64) and of 128 inputs
+    (K = 1024).  Sampled parity; no output left unwritten."""
     import torch
-    M, N, K = 16384, 4096, 64
+    M, N = 16384, 4096
     say(f"[i8] linear M={M} N={N} K={K}, 128-row tiles")
     dev = "cuda:0"
     x = synth.activations(M, K, 5321)
@@ -277,10 +279,12 @@ def test_i8_linear_rows_zero_row_and_channel(tb):
     run_linear_rows(tb, 40, 130, 256, True, False, seed=91, zero_row=True, zero_channel=True)
 
 
-def test_i8_linear_rows_tall_tiles_sampled(tb):
-    """4096 tiles of 128 rows (the tall-tile path) with per-channel scales."""
+@pytest.mark.parametrize("K", [64, 1024])
+def test_i8_linear_rows_tall_tiles_sampled(tb, K):
+    """4096 tiles of 128 rows (the tall-tile path) with per-channel scales, with
+    steps of 64 and of 128 inputs."""
     import torch
-    M, N, K = 16384, 4096, 64
+    M, N = 16384, 4096
     say(f"[i8 rows] linear M={M} N={N} K={K}, 128-row tiles")
     dev = "cuda:0"
     x = synth.activations(M, K, 6321)
