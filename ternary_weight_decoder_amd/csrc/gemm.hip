@@ -18,7 +18,8 @@
 //     MFMAs and never touches LDS.
 // The unit loop is unrolled by three so ring slots are static; units past K
 // load zeros (no memory access) and add nothing, so every slot issues the same
-// loads and the wait counts are exact.
+// loads and the wait counts are exact.  With 128-row tiles a unit's loads go
+// out between its first MFMA chunks, not all at once after its barrier.
 // Lane (i = lane%32, h = lane/32) feeds MFMA e (0..3) of a unit with packed
 // dword d = 4h + e of its column and the 16 permuted activations at 16*d of its
 // row, so the k positions of both operands agree by construction.
@@ -89,6 +90,12 @@ struct GemmShared {
 #endif
 constexpr int kStoreAux = BITNET_GEMM_STORE_AUX;
 
+// Tile height from which a unit's loads are issued between its MFMA chunks
+// instead of right after the barrier (measured: faster with 128-row tiles,
+// slower with the 32- and 64-row tiles of batched decode).
+#ifndef BITNET_GEMM_SPREAD_MINBM
+#define BITNET_GEMM_SPREAD_MINBM 128
+#endif
 #ifndef BITNET_GEMM_FENCE
 #define BITNET_GEMM_FENCE 1
 #endif
@@ -132,6 +139,7 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
                                            int nunits, GemmShared<BM> &sh) {
   static_assert(RB >= 1 && RB <= TileCfg<BM>::RB, "row blocks per tile");
   constexpr int kDma = TileCfg<BM>::kDma;
+  constexpr bool kSpread = BM >= BITNET_GEMM_SPREAD_MINBM;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -249,10 +257,12 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
 #endif
       __builtin_amdgcn_s_waitcnt(vmcnt_wait((kStages - 2) * (kDma + CB)));
       __builtin_amdgcn_s_barrier();
-      load_b(u + kStages - 1, bq[(s + kStages - 1) % kStages]);
-      issue_dma(u + kStages - 1, (s + kStages - 1) % kStages);
+      if (!kSpread) {
+        load_b(u + kStages - 1, bq[(s + kStages - 1) % kStages]);
+        issue_dma(u + kStages - 1, (s + kStages - 1) % kStages);
+      }
 #if BITNET_GEMM_FENCE
-      __builtin_amdgcn_sched_barrier(0);   // the loads go out before the MFMAs
+      __builtin_amdgcn_sched_barrier(0);   // (shorter tiles) the loads go out before the MFMAs
 #endif
       // Operands of k-chunk e + 1 (LDS reads, code unpack) are fetched while
       // the MFMAs of chunk e run.
@@ -283,6 +293,19 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
           for (int cb = 0; cb < CB; ++cb)
             acc[rb][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_cu[rb], b_cu[cb], acc[rb][cb],
                                                                0, 0, 0);
+        // 128-row tiles: the next unit's loads go out behind this chunk's
+        // MFMAs (the activation copy after chunk 0, the codes after chunk 1)
+        // rather than all at once after the barrier, where the four waves'
+        // 24 loads held up the first MFMAs while the address queue took them.
+        if (kSpread && e == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_dma(u + kStages - 1, (s + kStages - 1) % kStages);
+          __builtin_amdgcn_sched_barrier(0);
+        } else if (kSpread && e == 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          load_b(u + kStages - 1, bq[(s + kStages - 1) % kStages]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
 #if BITNET_GEMM_SCHED
       // Interleave: every MFMA is followed by part of the next chunk's LDS
