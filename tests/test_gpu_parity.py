@@ -461,6 +461,34 @@ def test_grouped_staged_decode_parity(tb, M):
         assert_y_matches(ys[i].cpu().numpy(), ref["y"], M)
 
 
+@pytest.mark.parametrize("M", [32, 64, 200])
+def test_grouped_skewed_parity(tb, M):
+    """A grouped GEMM launch of two long-K projections (K = 8960, sharing one
+    input) among six short ones, as batched decode mixes down with gate and up:
+    32-, 64- and 128-row tiles (M = 200 leaves a ragged last row block), two
+    calls in a row, every output against the oracle."""
+    import torch
+    say(f"[grouped] skewed launch M={M}")
+    shapes = [(512, 8960), (520, 8960)] + [(1024, 1536), (1000, 1536), (256, 1536),
+                                           (2048, 1536), (768, 384), (200, 1536)]
+    Ws = [synth.normal_weights(N, K, seed=15000 + i) for i, (N, K) in enumerate(shapes)]
+    xs = [synth.activations(M, K, seed=16000 + i) for i, (N, K) in enumerate(shapes)]
+    xs[1] = xs[0]
+    packs = [oracle.ternarize_pack(W) for W in Ws]
+    dx = [dev_tensor(x) for x in xs]
+    dx[1] = dx[0]
+    dp = [dev_tensor(p) for p, _ in packs]
+    ds = [dev_tensor(np.array([s], np.float32)) for _, s in packs]
+    ys = [torch.full((M, N), float("nan"), device="cuda:0") for N, _ in shapes]
+    plan = tb.GroupedPlan(M, dx, dp, ds, ys, [N for N, _ in shapes], [K for _, K in shapes])
+    plan.run()
+    plan.run()
+    torch.cuda.synchronize()
+    for i, (N, K) in enumerate(shapes):
+        ref = oracle.ternary_matmul(xs[i], packs[i][0], packs[i][1], N)
+        assert_y_matches(ys[i].cpu().numpy(), ref["y"], M)
+
+
 @pytest.mark.parametrize("M,nchunks", [(40, 2), (300, 5), (1800, 7)])
 def test_grouped_overlap_matches_grouped(tb, M, nchunks):
     """The prefill grouped call with its quantization on a second stream gives
