@@ -379,7 +379,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &p, int blk, bool s
     for (int j = 0; j < D; ++j) {
       const int i = base + j;
       if (!FUSED && i < units && i % kChunkUnits == 0) {
-        // Chunk i / 8 begins.  This wave's copy of it was issued before the
+        // Chunk i / kChunkUnits begins.  This wave's copy of it was issued before the
         // code loads of the last kChunkUnits units (C each) or, for the first
         // chunk, before those of the first D units; after the barrier every
         // wave's part is in LDS and every wave is done with the other buffer,
