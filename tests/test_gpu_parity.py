@@ -371,14 +371,16 @@ def test_grouped_layer_parity(tb, M):
         assert_y_matches(ys[i].cpu().numpy(), ref["y"], M)
 
 
-@pytest.mark.parametrize("M", [1, 3, 16, 40, 200])
+@pytest.mark.parametrize("M", [1, 3, 16, 40, 64, 65, 200])
 def test_grouped_many_ragged_parity(tb, M):
     """64 independent projections of mixed ragged shapes in one grouped call,
     every output checked against the oracle.  With these sizes the host deals
     whole projections to the XCDs in every regime: M = 1 (fused quantization,
     K split across waves), M = 3 (fused, several rows), M = 16 (rows staged
-    through LDS), M = 40 (the prefill GEMM, 64-row tiles) and M = 200 (128-row
-    tiles, the last row block three 32-row blocks deep)."""
+    through LDS), M = 40 and 64 (the prefill GEMM, 64-row tiles, plain row
+    loads in the quantization launch), M = 65 (128-row tiles with the loads
+    spread over each unit, a last row block of one 32-row block, non-temporal
+    row loads) and M = 200 (the last row block three 32-row blocks deep)."""
     import torch
     say(f"[grouped] 64 ragged projections M={M}")
     rng = np.random.default_rng(900)
