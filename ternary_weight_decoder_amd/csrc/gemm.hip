@@ -140,6 +140,11 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
   static_assert(RB >= 1 && RB <= TileCfg<BM>::RB, "row blocks per tile");
   constexpr int kDma = TileCfg<BM>::kDma;
   constexpr bool kSpread = BM >= BITNET_GEMM_SPREAD_MINBM;
+  // Code loads of 32- and 64-row tiles (M <= 64: one row block, so every code
+  // is read once) are non-temporal and leave L2 to the activation rows that
+  // every column tile re-reads; 128-row tiles re-read codes across row bands
+  // and keep them cacheable.
+  constexpr int kCodeAux = BM <= 64 ? 2 : 0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -183,7 +188,7 @@ __device__ __forceinline__ void gemm_block(const GemmProblem &p, int m0, int n0,
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
       dst[cb] = __builtin_amdgcn_raw_buffer_load_b128(
-          w_rsrc, u < units ? w_off[cb] + (uint32_t)u * ustride : w_bytes, 0, 0);
+          w_rsrc, u < units ? w_off[cb] + (uint32_t)u * ustride : w_bytes, 0, kCodeAux);
   };
 
   // A operand reads: row 32rb + li, chunk 4lh + e at position (4lh + e) ^ swz(li).
