@@ -484,27 +484,42 @@ bitnet_status bitnet_ternary_matmul_grouped_overlap(int64_t M, const bitnet_prob
   }
   const int32_t chunks = c + 1;
   first[chunks] = count;
+  // Launch sizes over the whole call: every chunk's launches are smaller, so
+  // no chunk can fail its own size check once some chunks are queued.
+  uint64_t gemm_total = 0, quant_total = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    gemm_total += (uint64_t)gemm_blocks(M, problems_host[i].N);
+    if (owner[i] == i) quant_total += (uint64_t)quant_grouped_blocks(M, problems_host[i].K);
+  }
+  if (gemm_total >= ((uint64_t)1 << 31) || quant_total >= ((uint64_t)1 << 31))
+    return BITNET_ERR_SHAPE;
+  // Every event is created before the first launch, so a failure to create
+  // one leaves nothing queued.  Events are released after use; HIP frees them
+  // once their pending work completes.
+  hipEvent_t ev[BITNET_MAX_CHUNKS + 1];
+  int32_t made = 0;
+  for (; made <= chunks; ++made)
+    if (hipEventCreateWithFlags(&ev[made], hipEventDisableTiming) != hipSuccess) break;
+  if (made <= chunks) {
+    for (int32_t k = 0; k < made; ++k) hipEventDestroy(ev[k]);
+    return BITNET_ERR_HIP;
+  }
   hipStream_t gs = as_stream(stream), qs = as_stream(aux_stream);
   uint8_t *ws = reinterpret_cast<uint8_t *>(workspace);
   // The auxiliary stream starts after everything already queued on the main
   // stream (the inputs, and an earlier call's contractions over the same
-  // workspace).  Events are released after use; HIP frees them once their
-  // pending work completes.
-  hipEvent_t start = nullptr;
-  if (hipEventCreateWithFlags(&start, hipEventDisableTiming) != hipSuccess) return BITNET_ERR_HIP;
-  st = (hipEventRecord(start, gs) == hipSuccess && hipStreamWaitEvent(qs, start, 0) == hipSuccess)
+  // workspace).
+  st = (hipEventRecord(ev[chunks], gs) == hipSuccess &&
+        hipStreamWaitEvent(qs, ev[chunks], 0) == hipSuccess)
            ? BITNET_OK
            : BITNET_ERR_HIP;
-  hipEventDestroy(start);
   int32_t sub[kMaxGroup];
   for (int32_t k = 0; k < chunks && st == BITNET_OK; ++k) {
     const int32_t n = first[k + 1] - first[k];
     for (int32_t i = 0; i < n; ++i) sub[i] = first[k] + i;
-    hipEvent_t ev = nullptr;
-    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return BITNET_ERR_HIP;
-    st = prefill_chunk(M, problems_dev, problems_host, sub, n, ws_off, owner, ws, qs, gs, ev);
-    hipEventDestroy(ev);
+    st = prefill_chunk(M, problems_dev, problems_host, sub, n, ws_off, owner, ws, qs, gs, ev[k]);
   }
+  for (int32_t k = 0; k <= chunks; ++k) hipEventDestroy(ev[k]);
   return st;
 }
 
