@@ -79,6 +79,22 @@ A = 0x7f0000000000   # 256-byte aligned
 NULL = None
 
 
+def test_matmul_shape_limits(L):
+    """The largest shapes the size rules allow (each bound within a few hundred
+    elements of 2^31; the GPU tests run them) pass the shape check and stop at
+    the workspace check here, and one more row or column is a shape error."""
+    f = L.bitnet_ternary_matmul
+    at_limit = ((1398101, 256, 1536),    # M*K
+                (1800, 278460, 128),     # (M + 128)*N*4
+                (16, 239674, 8960))      # N*K
+    over = ((1398102, 256, 1536), (1800, 278461, 128), (16, 239675, 8960))
+    for M, N, K in at_limit:
+        assert M * K < 1 << 31 and N * K < 1 << 31 and (M + 128) * N * 4 < 1 << 31
+        assert f(M, N, K, A, A, A, A, A, 0, NULL, NULL, NULL, NULL) == ERR["WORKSPACE"]
+    for M, N, K in over:
+        assert f(M, N, K, A, A, A, A, A, 0, NULL, NULL, NULL, NULL) == ERR["SHAPE"]
+
+
 def test_matmul_validation(L):
     ws_ok = L.bitnet_matmul_workspace_bytes(1, 1536)
     f = L.bitnet_ternary_matmul

@@ -1,0 +1,184 @@
+"""GPU parity at the largest shapes the boundary accepts.
+
+The size rules keep every device offset in 32 bits: M*K, N*K and M*N below
+2^31, and (M + 128)*N*4 below 2^31 (the fp32 output addressed with a 128-row
+tile past M).  Each test takes one of those bounds to within a few hundred
+elements of 2^31 and checks the call against the oracle:
+  - M*K: the whole projection (quantization + prefill GEMM) over 1,398,101 rows
+    of K = 1536 (8.6 GB of fp32 activations);
+  - (M + 128)*N*4: the prefill GEMM at M = 1800 with N = 278,460 columns
+    (a 2 GB fp32 output);
+  - N*K: ternarize + pack of an 8960-input weight with 239,674 rows (8.6 GB of
+    fp32 masters), then the decode GEMV on it at M = 1 (quantization fused)
+    and M = 16 (rows staged from the quantization launch).
+Inputs are seeded: activations and the large masters come from torch's
+generator on the GPU, the small masters from the host generators; the oracle
+sees the same arrays.  Outputs are checked on sampled rows and columns (the
+first and last of each among them), int8 rows, scales and int32 accumulators
+bit for bit, fp32 outputs bit for bit on the decode path and within 1e-6
+relative on the prefill path; every output buffer is NaN-filled with a canary
+tail, and no NaN may remain.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from ternary_weight_decoder_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 1e-6
+CANARY = 4096
+LIMIT = 1 << 31
+
+
+@pytest.fixture(scope="module")
+def tb():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ternary_weight_decoder_amd import binding
+    binding.lib()
+    return binding
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def guarded(n, dtype):
+    """n elements followed by a canary tail, all NaN (or -1 for integers)."""
+    import torch
+    fill = float("nan") if dtype.is_floating_point else -1
+    buf = torch.full((n + CANARY,), fill, dtype=dtype, device="cuda:0")
+    return buf, buf[:n]
+
+
+def assert_canary(buf, n):
+    import torch
+    tail = buf[n:]
+    ok = torch.isnan(tail).all() if tail.dtype.is_floating_point else (tail == -1).all()
+    assert bool(ok), "canary overwritten"
+
+
+def gpu_normal(shape, seed, scale=1.0):
+    import torch
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(seed)
+    t = torch.randn(shape, generator=g, device="cuda:0")
+    if scale != 1.0:
+        t.mul_(scale)
+    return t
+
+
+def samples(size, count, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 1, size - 2, size - 1],
+                                     rng.integers(0, size, count)])).astype(np.int64)
+
+
+def pack_both(tb, W_host, W_dev):
+    """Ternarize + pack on the GPU and in the oracle; both must agree exactly."""
+    import torch
+    N, K = W_host.shape
+    packed = torch.empty(N * K // 4, dtype=torch.uint8, device="cuda:0")
+    w_scale = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(tb.bitnet_ternarize_workspace_bytes(N), dtype=torch.uint8, device="cuda:0")
+    tb.bitnet_ternarize_pack_into(W_dev, N, K, packed, w_scale, ws)
+    ref_packed, ref_scale = oracle.ternarize_pack(W_host)
+    torch.cuda.synchronize()
+    assert w_scale.cpu().numpy()[0] == ref_scale, "w_scale differs"
+    assert np.array_equal(packed.cpu().numpy(), ref_packed), "packed codes differ"
+    return packed, w_scale, ref_packed, ref_scale
+
+
+def run_and_check(tb, x, packed, w_scale, ref_packed, ref_scale, N, rows, cols, exact_y):
+    """One bitnet_ternary_matmul call with every optional output, checked on
+    rows x cols against the oracle."""
+    import torch
+    M, K = x.shape
+    y_buf, y = guarded(M * N, torch.float32)
+    a_buf, acc = guarded(M * N, torch.int32)
+    s_buf, xs = guarded(M, torch.float32)
+    xq = torch.full((M * K,), -128, dtype=torch.int8, device="cuda:0")
+    ws = torch.empty(tb.bitnet_matmul_workspace_bytes(M, K), dtype=torch.uint8, device="cuda:0")
+    tb.bitnet_ternary_matmul_into(M, N, K, x, packed, w_scale, y, ws, xq, xs, acc)
+    torch.cuda.synchronize()
+    for buf, n in ((y_buf, M * N), (a_buf, M * N), (s_buf, M)):
+        assert_canary(buf, n)
+    assert not bool(torch.isnan(y).any()), "unwritten output"
+    assert not bool((xq == -128).any()), "unwritten int8 row (or -128)"
+    del ws
+    r = torch.from_numpy(rows).to("cuda:0")
+    x_rows = x[r].cpu().numpy()
+    ref_xq, ref_xs = oracle.quant_act(x_rows)
+    np.testing.assert_array_equal(xq.view(M, K)[r].cpu().numpy(), ref_xq)
+    np.testing.assert_array_equal(xs[r].cpu().numpy(), ref_xs)
+    ms = np.repeat(np.arange(rows.size), cols.size).astype(np.int64)
+    ns = np.tile(cols, rows.size).astype(np.int64)
+    ref_acc, ref_y = oracle.matmul_sampled(ref_xq, ref_xs, ref_packed, ref_scale, N, ms, ns)
+    c = torch.from_numpy(cols).to("cuda:0")
+    got_acc = acc.view(M, N)[r][:, c].cpu().numpy().reshape(-1)
+    got_y = y.view(M, N)[r][:, c].cpu().numpy().reshape(-1)
+    np.testing.assert_array_equal(got_acc, ref_acc)
+    if exact_y:
+        np.testing.assert_array_equal(got_y.view(np.uint32), ref_y.view(np.uint32))
+    zero = ref_y == 0
+    assert (got_y[zero] == 0).all()
+    rel = np.abs(got_y.astype(np.float64) - ref_y) / np.maximum(np.abs(ref_y.astype(np.float64)),
+                                                                 1e-300)
+    worst = float(rel[~zero].max()) if (~zero).any() else 0.0
+    assert worst <= REL_TOL, f"max relative error {worst:.3e}"
+    return worst
+
+
+def test_max_rows_times_k(tb):
+    """M*K = 2^31 - 512: 1,398,101 rows of 1536 inputs through the whole
+    projection (quantization launch + prefill GEMM), N = 256."""
+    import torch
+    M, N, K = 1398101, 256, 1536
+    say(f"[limits] M*K: M={M} N={N} K={K}")
+    W = synth.normal_weights(N, K, seed=91)
+    packed, w_scale, ref_packed, ref_scale = pack_both(tb, W, torch.from_numpy(W).to("cuda:0"))
+    x = gpu_normal((M, K), seed=92)
+    worst = run_and_check(tb, x, packed, w_scale, ref_packed, ref_scale, N,
+                          samples(M, 60, 93), samples(N, 30, 94), exact_y=False)
+    say(f"[limits] M*K ok, max relative error {worst:.2e}")
+
+
+def test_max_output_bytes(tb):
+    """(M + 128)*N*4 = 2^31 - 128: the prefill GEMM at M = 1800 writing a
+    2 GB fp32 output (N = 278,460, a ragged last column tile)."""
+    import torch
+    M, N, K = 1800, 278460, 128
+    say(f"[limits] output bytes: M={M} N={N} K={K}")
+    W = synth.normal_weights(N, K, seed=95)
+    packed, w_scale, ref_packed, ref_scale = pack_both(tb, W, torch.from_numpy(W).to("cuda:0"))
+    x = gpu_normal((M, K), seed=96)
+    cols = np.unique(np.concatenate([samples(N, 40, 97), np.arange(N - 300, N)]))
+    worst = run_and_check(tb, x, packed, w_scale, ref_packed, ref_scale, N,
+                          samples(M, 40, 98), cols, exact_y=False)
+    say(f"[limits] output bytes ok, max relative error {worst:.2e}")
+
+
+def test_max_codes_decode(tb):
+    """N*K = 2^31 - 4608: an 8960-input weight with 239,674 rows ternarized
+    and packed (8.6 GB of masters, 537 MB of codes), then the decode GEMV at
+    M = 1 (quantization fused) and M = 16 (rows staged)."""
+    import torch
+    N, K = 239674, 8960
+    say(f"[limits] N*K: N={N} K={K}: masters on the GPU, a host copy for the oracle")
+    W_dev = gpu_normal((N, K), seed=99, scale=0.02)
+    W_host = W_dev.cpu().numpy()
+    packed, w_scale, ref_packed, ref_scale = pack_both(tb, W_host, W_dev)
+    del W_dev, W_host
+    torch.cuda.empty_cache()
+    for M in (1, 16):
+        x = gpu_normal((M, K), seed=100 + M)
+        rows = np.arange(M, dtype=np.int64)
+        run_and_check(tb, x, packed, w_scale, ref_packed, ref_scale, N, rows,
+                      samples(N, 60, 101 + M), exact_y=True)
+        say(f"[limits] N*K decode M={M} ok (bit-exact)")
