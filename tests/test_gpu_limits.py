@@ -182,3 +182,161 @@ def test_max_codes_decode(tb):
         run_and_check(tb, x, packed, w_scale, ref_packed, ref_scale, N, rows,
                       samples(N, 60, 101 + M), exact_y=True)
         say(f"[limits] N*K decode M={M} ok (bit-exact)")
+
+
+# ---- I8_S layers and the 8-bit table at their own limits ----------------------
+
+I8_TOL = 4.0 * 2.0 ** -24        # per-tensor epilogue: three fp32 roundings and the bias add
+I8_TOL_ROWS = 5.0 * 2.0 ** -24   # per-channel epilogue: one rounding more
+
+
+def check_i8(tb, x, q_dev, s_dev, q_ref, s_ref, b, per_channel, rows, cols):
+    """One I8_S linear call (bias, ReLU) checked on rows x cols: accumulators
+    bit-exact, outputs within the epilogue's bound, no NaN left, canary kept."""
+    import torch
+    M, K = x.shape
+    N = q_ref.shape[0]
+    y_buf, y = guarded(M * N, torch.float32)
+    a_buf, acc = guarded(M * N, torch.int32)
+    ws = torch.empty(tb.bitnet_i8_linear_workspace_bytes(M, K), dtype=torch.uint8,
+                     device="cuda:0")
+    call = tb.bitnet_i8_linear_rows_into if per_channel else tb.bitnet_i8_linear_into
+    call(M, N, K, x, q_dev, s_dev, torch.from_numpy(b).to("cuda:0"), True, y, ws, acc)
+    torch.cuda.synchronize()
+    for buf in (y_buf, a_buf):
+        assert_canary(buf, M * N)
+    assert not bool(torch.isnan(y).any()), "unwritten output"
+    del ws
+    r = torch.from_numpy(rows).to("cuda:0")
+    xq, xs = oracle.quant_act(x[r].cpu().numpy())
+    ms = np.repeat(np.arange(rows.size), cols.size).astype(np.int64)
+    ns = np.tile(cols, rows.size).astype(np.int64)
+    sampled = oracle.i8_linear_rows_sampled if per_channel else oracle.i8_linear_sampled
+    acc_ref, d, y_ref = sampled(xq, xs, q_ref, s_ref, b, True, ms, ns)
+    c = torch.from_numpy(cols).to("cuda:0")
+    np.testing.assert_array_equal(acc.view(M, N)[r][:, c].cpu().numpy().reshape(-1), acc_ref)
+    got = y.view(M, N)[r][:, c].cpu().numpy().reshape(-1)
+    tol = I8_TOL_ROWS if per_channel else I8_TOL
+    bound = tol * (np.abs(d) + np.abs(b[ns].astype(np.float64))) + 1e-37
+    worst = float((np.abs(got.astype(np.float64) - y_ref.astype(np.float64)) / bound).max())
+    assert worst <= 1.0, f"error {worst:.3f} x the bound"
+    assert (got >= 0).all()
+    return worst
+
+
+def test_i8_max_rows_times_k(tb):
+    """I8_S layer (one weight scale, bias, ReLU) at M*K = 2^31 - 512:
+    1,398,101 rows of 1536 inputs, N = 256."""
+    import torch
+    M, N, K = 1398101, 256, 1536
+    say(f"[limits] I8_S M*K: M={M} N={N} K={K}")
+    W = synth.normal_weights(N, K, seed=111)
+    b = np.random.default_rng(112).standard_normal(N, dtype=np.float32) * np.float32(0.1)
+    q_ref, s_ref = oracle.i8_quant_weights(W)
+    q_dev, s_dev = tb.bitnet_i8_quant_weights(torch.from_numpy(W).to("cuda:0"))
+    torch.cuda.synchronize()
+    assert s_dev.cpu().numpy()[0] == s_ref
+    np.testing.assert_array_equal(q_dev.cpu().numpy(), q_ref)
+    x = gpu_normal((M, K), seed=113)
+    worst = check_i8(tb, x, q_dev, s_dev, q_ref, s_ref, b, False, samples(M, 60, 114),
+                     samples(N, 30, 115))
+    say(f"[limits] I8_S M*K ok, worst {worst:.3f} of the bound")
+
+
+def test_i8_rows_max_output_bytes(tb):
+    """I8_S layer with one weight scale per output channel at
+    (M + 128)*N*4 = 2^31 - 128: M = 1800, N = 278,460, K = 128."""
+    import torch
+    M, N, K = 1800, 278460, 128
+    say(f"[limits] I8_S per-channel output bytes: M={M} N={N} K={K}")
+    W = synth.normal_weights(N, K, seed=116)
+    b = np.random.default_rng(117).standard_normal(N, dtype=np.float32) * np.float32(0.1)
+    q_ref, s_ref = oracle.rowq_quant_weights(W)
+    q_dev, s_dev = tb.bitnet_i8_quant_weights_rows(torch.from_numpy(W).to("cuda:0"))
+    torch.cuda.synchronize()
+    assert s_dev.cpu().numpy().tobytes() == s_ref.tobytes()
+    np.testing.assert_array_equal(q_dev.cpu().numpy(), q_ref)
+    x = gpu_normal((M, K), seed=118)
+    cols = np.unique(np.concatenate([samples(N, 40, 119), np.arange(N - 300, N)]))
+    worst = check_i8(tb, x, q_dev, s_dev, q_ref, s_ref, b, True, samples(M, 40, 120), cols)
+    say(f"[limits] I8_S per-channel output bytes ok, worst {worst:.3f} of the bound")
+
+
+def test_table_max_bytes(tb):
+    """The 8-bit table at its largest: V = 1,398,096 rows of 1536 inputs
+    (2^31 - 12,288 bytes of codes from 8.6 GB of masters), codes and scales
+    bit-exact, the lm_head at M = 1 and 16 on sampled columns and the
+    embedding of the first and last rows, bit-exact."""
+    import torch
+    V, K = 1398096, 1536
+    assert oracle.table_bytes(V, K) < LIMIT <= oracle.table_bytes(V + 1, K)
+    say(f"[limits] table V={V} K={K}: masters on the GPU, a host copy for the oracle")
+    W_dev = gpu_normal((V, K), seed=121, scale=0.02)
+    table = torch.empty(tb.bitnet_table_bytes(V, K), dtype=torch.int8, device="cuda:0")
+    s_dev = torch.full((V,), float("nan"), dtype=torch.float32, device="cuda:0")
+    tb.bitnet_table_quant_into(W_dev, V, K, table, s_dev)
+    W_host = W_dev.cpu().numpy()
+    del W_dev
+    q_ref, s_ref = oracle.rowq_quant_weights(W_host)
+    del W_host
+    torch.cuda.synchronize()
+    assert s_dev.cpu().numpy().tobytes() == s_ref.tobytes()
+    assert np.array_equal(table.cpu().numpy(), oracle.table_pack(q_ref))
+    torch.cuda.empty_cache()
+    for M in (1, 16):
+        x = gpu_normal((M, K), seed=122 + M)
+        y_buf, y = guarded(M * V, torch.float32)
+        a_buf, acc = guarded(M * V, torch.int32)
+        tb.bitnet_lm_head_into(M, V, K, x, table, s_dev, y, acc_out=acc)
+        torch.cuda.synchronize()
+        for buf in (y_buf, a_buf):
+            assert_canary(buf, M * V)
+        assert not bool(torch.isnan(y).any()), "unwritten output"
+        xq, xs = oracle.quant_act(x.cpu().numpy())
+        cols = np.unique(np.concatenate([samples(V, 200, 124 + M), np.arange(V - 40, V)]))
+        ms = np.repeat(np.arange(M), cols.size).astype(np.int64)
+        ns = np.tile(cols, M).astype(np.int64)
+        acc_s, y_s = oracle.rowq_linear_sampled(xq, xs, q_ref, s_ref, ms, ns)
+        c = torch.from_numpy(cols).to("cuda:0")
+        np.testing.assert_array_equal(acc.view(M, V)[:, c].cpu().numpy().reshape(-1), acc_s)
+        assert y.view(M, V)[:, c].cpu().numpy().reshape(-1).tobytes() == y_s.tobytes()
+        say(f"[limits] table lm_head M={M} ok (bit-exact)")
+    ids = np.array([0, 1, V - 2, V - 1, 700001], dtype=np.int32)
+    out = tb.bitnet_embed_lookup(torch.from_numpy(ids).to("cuda:0"), table, s_dev, K)
+    torch.cuda.synchronize()
+    assert out.cpu().numpy().tobytes() == oracle.rowq_embed(ids, q_ref, s_ref).tobytes()
+    say("[limits] table embedding ok (bit-exact)")
+
+
+def test_dwconv_max_elements(tb):
+    """The depthwise convolution at B*T*C = 2^29 - 1024 (the fp32 input and
+    output just under 2 GB each): 2 sequences of 524,287 frames x 512
+    channels, 7 taps, bias and ReLU; every output, accumulator and scale
+    bit-exact against the oracle."""
+    import torch
+    B, T, C, k = 2, 524287, 512, 7
+    assert B * T * C < LIMIT // 4 <= B * (T + 1) * C
+    say(f"[limits] depthwise conv B={B} T={T} C={C} k={k}")
+    x = gpu_normal((B, T, C), seed=131)
+    W = np.random.default_rng(132).standard_normal((C, k), dtype=np.float32) * np.float32(0.1)
+    b = np.random.default_rng(133).standard_normal(C, dtype=np.float32) * np.float32(0.1)
+    q, s = tb.bitnet_i8_dwconv_quant_weights(torch.from_numpy(W).to("cuda:0"))
+    y_buf, y = guarded(B * T * C, torch.float32)
+    a_buf, acc = guarded(B * T * C, torch.int32)
+    xs = torch.full((B, C), float("nan"), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(tb.bitnet_i8_dwconv_workspace_bytes(B, T, C), dtype=torch.uint8,
+                     device="cuda:0")
+    tb.bitnet_i8_dwconv_into(B, T, C, k, x, q, s, torch.from_numpy(b).to("cuda:0"), True, y, ws,
+                             acc, xs)
+    torch.cuda.synchronize()
+    for buf in (y_buf, a_buf):
+        assert_canary(buf, B * T * C)
+    del ws
+    q_ref, s_ref = oracle.rowq_quant_weights(W)
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+    assert s.cpu().numpy().tobytes() == s_ref.tobytes()
+    ref = oracle.i8_dwconv(x.cpu().numpy(), q_ref, s_ref, b, True)
+    assert xs.cpu().numpy().tobytes() == ref["x_scale"].tobytes()
+    assert np.array_equal(acc.cpu().numpy(), ref["acc"].reshape(-1))
+    assert y.cpu().numpy().tobytes() == ref["y"].tobytes()
+    say("[limits] depthwise conv ok (bit-exact)")
