@@ -243,7 +243,12 @@ bitnet_status bitnet_ternary_matmul_grouped(int64_t M, const bitnet_problem *pro
  * bitnet_ternary_matmul_grouped (the same kernels).  With M <= 16, nchunks <=
  * 1 or aux_stream == stream this is the plain grouped call on `stream`.
  * nchunks <= count and <= BITNET_MAX_CHUNKS; workspace as for the grouped
- * call.  Use distinct, default-priority streams. */
+ * call.  Use distinct, default-priority streams.  Shapes, sizes and the
+ * events are all checked or created before the first launch, so those errors
+ * leave nothing queued; a HIP error while the chunks are being queued
+ * (BITNET_ERR_HIP) can leave the earlier chunks queued.  The call is meant
+ * for prefill-sized steps: each chunk adds launches and an event hand-off
+ * between the streams. */
 #define BITNET_MAX_CHUNKS 32
 
 bitnet_status bitnet_ternary_matmul_grouped_overlap(int64_t M, const bitnet_problem *problems_dev,
