@@ -340,3 +340,55 @@ def test_dwconv_max_elements(tb):
     assert np.array_equal(acc.cpu().numpy(), ref["acc"].reshape(-1))
     assert y.cpu().numpy().tobytes() == ref["y"].tobytes()
     say("[limits] depthwise conv ok (bit-exact)")
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 200])
+def test_grouped_max_count(tb, M):
+    """The grouped call at its largest problem count (256 ragged projections,
+    a third of them sharing inputs), every output against the oracle; at
+    prefill sizes also the overlapped call at its largest chunk count (32),
+    bit for bit against the grouped call."""
+    import torch
+    count = tb.BITNET_MAX_GROUP
+    say(f"[limits] grouped call, {count} projections, M={M}")
+    rng = np.random.default_rng(140 + M)
+    shapes = [(int(rng.choice([16, 72, 200, 520, 1000])), int(rng.choice([128, 256, 640, 1536])))
+              for _ in range(count)]
+    Ws = [synth.normal_weights(N, K, seed=150000 + i) for i, (N, K) in enumerate(shapes)]
+    packs = [oracle.ternarize_pack(W) for W in Ws]
+    xs_host, dx, xd = [], [], {}
+    for i, (N, K) in enumerate(shapes):
+        key = (i // 3, K) if i % 2 == 0 else (i, K)   # some neighbours share an input buffer
+        if key not in xd:
+            x = synth.activations(M, K, seed=160000 + i)
+            xd[key] = (x, torch.from_numpy(x).to("cuda:0"))
+        xs_host.append(xd[key][0])
+        dx.append(xd[key][1])
+    dp = [torch.from_numpy(p).to("cuda:0") for p, _ in packs]
+    ds = [torch.tensor([s], dtype=torch.float32, device="cuda:0") for _, s in packs]
+    Ns, Ks = [N for N, _ in shapes], [K for _, K in shapes]
+    ys = [torch.full((M, N), float("nan"), device="cuda:0") for N in Ns]
+    plan = tb.GroupedPlan(M, dx, dp, ds, ys, Ns, Ks)
+    plan.run()
+    torch.cuda.synchronize()
+    for i, (N, K) in enumerate(shapes):
+        ref = oracle.ternary_matmul(xs_host[i], packs[i][0], packs[i][1], N)["y"]
+        y = ys[i].cpu().numpy()
+        assert not np.isnan(y).any(), f"problem {i}: unwritten output"
+        if M <= 16:
+            np.testing.assert_array_equal(y.view(np.uint32), ref.view(np.uint32))
+        else:
+            zero = ref == 0
+            assert (y[zero] == 0).all()
+            rel = np.abs(y.astype(np.float64) - ref) / np.maximum(np.abs(ref.astype(np.float64)),
+                                                                  1e-300)
+            assert float(rel[~zero].max(initial=0.0)) <= REL_TOL, f"problem {i}"
+    if M > 16:
+        ys2 = [torch.full((M, N), float("nan"), device="cuda:0") for N in Ns]
+        plan2 = tb.GroupedPlan(M, dx, dp, ds, ys2, Ns, Ks)
+        aux = torch.cuda.Stream()
+        plan2.run_overlap(aux, 32)
+        torch.cuda.synchronize()
+        for a, b in zip(ys2, ys):
+            assert torch.equal(a, b)
+    say(f"[limits] grouped call, {count} projections, M={M} ok")
