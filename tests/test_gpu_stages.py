@@ -160,3 +160,44 @@ def test_stages_general_shapes_bit_exact(tb, M):
     for n in shapes:
         got = ys[n].cpu().numpy()
         np.testing.assert_array_equal(got.view(np.uint32), ref[n].view(np.uint32), n)
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_stages_max_stages_bit_exact(tb, M):
+    """The staged call at its largest sizes: 256 stages of one problem each
+    (N = K = 128), every stage reading the previous stage's output.  Each
+    stage's master is a seeded N(0,1) matrix times a power of two picked on
+    the host so that the chain's outputs stay near 1 (the codes do not depend
+    on that factor); every output bit for bit against the oracle's own chain."""
+    import torch
+    n = tb.BITNET_MAX_GROUP
+    say(f"[stages] {n} single-problem stages, M={M}")
+    dev = "cuda:0"
+    x = synth.activations(M, 128, seed=910)
+    xd = torch.from_numpy(x).to(dev)
+    refs, stages, ys = [], [], []
+    prev, prev_d = x, xd
+    for s in range(n):
+        W0 = synth.normal_weights(128, 128, seed=920 + s, std=1.0)
+        pk, sc = oracle.ternarize_pack(W0)
+        a = float(np.abs(oracle.ternary_matmul(prev, pk, sc, 128)["y"]).max())
+        c = np.float32(2.0 ** -round(np.log2(a))) if a > 0 else np.float32(1.0)
+        pk, sc = oracle.ternarize_pack(W0 * c)
+        ref = oracle.ternary_matmul(prev, pk, sc, 128)["y"]
+        y = torch.full((M, 128), float("nan"), device=dev)
+        stages.append([(prev_d, torch.from_numpy(pk).to(dev),
+                        torch.tensor([sc], dtype=torch.float32, device=dev), y, 128, 128)])
+        refs.append(ref)
+        ys.append(y)
+        prev, prev_d = ref, y
+    assert 0.1 < float(np.abs(refs[-1]).max()) < 10.0
+    plan = tb.StagedPlan(M, stages)
+    for _ in range(2):
+        for y in ys:
+            y.fill_(float("nan"))
+        plan.run()
+        torch.cuda.synchronize()
+        assert not plan.timed_out() and plan.timeouts_total() == 0
+        for s in range(n):
+            np.testing.assert_array_equal(ys[s].cpu().numpy().view(np.uint32),
+                                          refs[s].view(np.uint32), f"stage {s}")
